@@ -1,0 +1,273 @@
+"""CPU oracle of the sparsely-gated MoE layer forward (numpy front end).
+
+TEST INFRASTRUCTURE ONLY: the tests, the package smoke check and the
+benchmark's CPU-baseline leg are the only code that may import this package.
+The product path (the HIP library and its Python binding) never imports it,
+and this package imports nothing from the product path.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, double accumulation,
+OpenMP over tokens); this module only marshals numpy arrays to it and composes
+the steps in the order the layer defines them:
+
+  gate logits -> [normalise] -> softmax -> top-k -> capacity / drop ->
+  permutation -> expert FFN -> weighted combine.
+
+Conventions (shared with the HIP path only through the documented layouts):
+  * floating tensors are numpy float32 (fp32) or uint16 holding bf16 bits;
+  * x [T,d], Wg [E,d], bg [E] fp32, W1 [E,n1,d] (n1 = F or 2F, SwiGLU gate
+    rows first), W2 [E,d,F], logits [T,E] fp32;
+  * topk_idx [T,k] int32, slot [T,k] int32 (-1 = dropped), counts [E],
+    offsets [E+1], src_token [P] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+RELU = 0
+SWIGLU = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c into liboracle.so (gcc, OpenMP, portable x86-64)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.orc_threads.restype = I
+    lib.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_to_double.restype = D
+    lib.orc_gate_logits.argtypes = [I, I, I, I, P, P, P, P, P]
+    lib.orc_normalize.argtypes = [I, P, D, P]
+    lib.orc_softmax.argtypes = [I, P, P]
+    lib.orc_gate_probs.argtypes = [I, P, I, D, P]
+    lib.orc_topk.argtypes = [I, I, P, P]
+    lib.orc_route.argtypes = [I, I, I, I, D, P, P, P, P]
+    lib.orc_capacity.argtypes = [I, I, I, D]
+    lib.orc_capacity.restype = ctypes.c_longlong
+    lib.orc_dispatch.argtypes = [I, I, I, ctypes.c_longlong, P, P, P, P, P]
+    lib.orc_dispatch.restype = I
+    lib.orc_expert_ffn.argtypes = [I, I, I, I, P, P, I, P, P, P]
+    lib.orc_forward_tokens.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, P, P]
+    lib.orc_ffn_rows.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, P]
+    lib.orc_combine.argtypes = [I, I, I, I, P, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle tensors are float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _c(a, dtype=None):
+    a = np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+    return a
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().orc_threads())
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (vectorised, same rule as the C side)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float64)
+
+
+def gate_logits(x, Wg, bg=None):
+    """z = x Wg^T + bg.  Returns (z_exact float64 [T,E], z32 float32 [T,E])."""
+    x = _c(x)
+    Wg = _c(Wg)
+    T, d = x.shape
+    E = Wg.shape[0]
+    assert Wg.shape == (E, d) and Wg.dtype == x.dtype
+    bgc = None if bg is None else _c(bg, np.float32)
+    ze = np.empty((T, E), np.float64)
+    z32 = np.empty((T, E), np.float32)
+    _load().orc_gate_logits(T, d, E, _dtype_code(x), _ptr(x), _ptr(Wg), _ptr(bgc), _ptr(ze), _ptr(z32))
+    return ze, z32
+
+
+def normalize(z_row, lam):
+    z_row = _c(z_row, np.float32)
+    E = z_row.shape[0]
+    out = np.empty(E, np.float64)
+    _load().orc_normalize(E, _ptr(z_row), float(lam), _ptr(out))
+    return out
+
+
+def softmax(s_row):
+    s_row = _c(s_row, np.float64)
+    E = s_row.shape[0]
+    out = np.empty(E, np.float64)
+    _load().orc_softmax(E, _ptr(s_row), _ptr(out))
+    return out
+
+
+def gate_probs(z_row, normalize_flag, lam):
+    z_row = _c(z_row, np.float32)
+    E = z_row.shape[0]
+    out = np.empty(E, np.float64)
+    _load().orc_gate_probs(E, _ptr(z_row), int(bool(normalize_flag)), float(lam), _ptr(out))
+    return out
+
+
+def topk(z_row, k):
+    z_row = _c(z_row, np.float32)
+    E = z_row.shape[0]
+    out = np.empty(k, np.int32)
+    _load().orc_topk(E, k, _ptr(z_row), _ptr(out))
+    return out
+
+
+def route(z32, k, normalize_flag=False, lam=1.0, want_p=False):
+    """Routing of all tokens on fp32 logits z32 [T,E].
+
+    Returns (topk_idx int32 [T,k], topk_w float64 [T,k]) and, with want_p,
+    also p float64 [T,E]."""
+    z32 = _c(z32, np.float32)
+    T, E = z32.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    p = np.empty((T, E), np.float64) if want_p else None
+    _load().orc_route(T, E, k, int(bool(normalize_flag)), float(lam), _ptr(z32), _ptr(idx), _ptr(w), _ptr(p))
+    return (idx, w, p) if want_p else (idx, w)
+
+
+def capacity(T, E, k, cf) -> int:
+    """Expert capacity, or -1 for no limit."""
+    return int(_load().orc_capacity(int(T), int(E), int(k), float(cf)))
+
+
+def dispatch(topk_idx, E, C):
+    """Counting + capacity + permutation.  Returns dict of counts, offsets,
+    slot, src_token (length P) and P."""
+    idx = _c(topk_idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    slot = np.empty((T, k), np.int32)
+    src = np.full(T * k, -1, np.int32)
+    P = _load().orc_dispatch(T, E, k, int(C), _ptr(idx), _ptr(counts), _ptr(offsets), _ptr(slot), _ptr(src))
+    return {"counts": counts, "offsets": offsets, "slot": slot, "src_token": src[:P].copy(), "P": int(P)}
+
+
+def expert_ffn(W1, W2, e, x_row, act, F, want_h=False):
+    """One input vector (float64 [d]) through expert e."""
+    W1 = _c(W1)
+    W2 = _c(W2)
+    d = W2.shape[1]
+    xr = _c(x_row, np.float64)
+    out = np.empty(d, np.float64)
+    h = np.empty(F, np.float64) if want_h else None
+    _load().orc_expert_ffn(d, F, int(act), _dtype_code(W1), _ptr(W1), _ptr(W2), int(e), _ptr(xr), _ptr(out), _ptr(h))
+    return (out, h) if want_h else out
+
+
+def forward_tokens(x, W1, W2, topk_idx, topk_w, slot, act, F, tokens=None):
+    """Layer output rows (float64 [n, d]) for the given tokens (default all)."""
+    x = _c(x)
+    W1 = _c(W1)
+    W2 = _c(W2)
+    T, d = x.shape
+    idx = _c(topk_idx, np.int32)
+    k = idx.shape[1]
+    w = _c(topk_w, np.float64)
+    sl = _c(slot, np.int32)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tok is None else tok.shape[0]
+    y = np.empty((n, d), np.float64)
+    _load().orc_forward_tokens(d, k, F, int(act), _dtype_code(x), _ptr(x), _ptr(W1), _ptr(W2), _ptr(idx), _ptr(w),
+                               _ptr(sl), n, _ptr(tok), _ptr(y))
+    return y
+
+
+def ffn_rows(x_perm, offsets, W1, W2, act, F, rows=None, want_h=False):
+    """Expert FFN of permuted rows (float64 [n, d]); the expert of a row is
+    found from offsets."""
+    xp = _c(x_perm)
+    W1 = _c(W1)
+    W2 = _c(W2)
+    off = _c(offsets, np.int32)
+    E = off.shape[0] - 1
+    d = W2.shape[1]
+    rr = None if rows is None else _c(rows, np.int32)
+    n = xp.shape[0] if rr is None else rr.shape[0]
+    out = np.empty((n, d), np.float64)
+    h = np.empty((n, F), np.float64) if want_h else None
+    _load().orc_ffn_rows(E, d, F, int(act), _dtype_code(xp), _ptr(off), _ptr(xp), _ptr(W1), _ptr(W2), n, _ptr(rr),
+                         _ptr(out), _ptr(h))
+    return (out, h) if want_h else out
+
+
+def combine(y_perm, slot, topk_w, T):
+    yp = _c(y_perm)
+    sl = _c(slot, np.int32)
+    w = _c(topk_w, np.float64)
+    k = sl.shape[1]
+    d = yp.shape[1]
+    y = np.empty((T, d), np.float64)
+    _load().orc_combine(T, d, k, _dtype_code(yp), _ptr(yp), _ptr(sl), _ptr(w), _ptr(y))
+    return y
+
+
+def moe_forward(x, Wg, bg, W1, W2, *, k, F, act, normalize_flag=False, lam=1.0, cf=0.0, logits=None,
+                tokens=None):
+    """Whole layer, composed step by step.  When logits (fp32 [T,E]) is given,
+    the gate is skipped and those logits are routed.  Returns a dict with the
+    routing, the permutation and y (float64) for the requested tokens."""
+    x = _c(x)
+    T = x.shape[0]
+    if logits is None:
+        z_exact, z32 = gate_logits(x, Wg, bg)
+    else:
+        z32 = _c(logits, np.float32)
+        z_exact = None
+    E = z32.shape[1]
+    idx, w = route(z32, k, normalize_flag, lam)
+    C = capacity(T, E, k, cf)
+    disp = dispatch(idx, E, C)
+    y = forward_tokens(x, W1, W2, idx, w, disp["slot"], act, F, tokens)
+    out = {"z_exact": z_exact, "z32": z32, "topk_idx": idx, "topk_w": w, "C": C, "y": y}
+    out.update(disp)
+    return out

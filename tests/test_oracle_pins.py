@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test ties one step of the oracle to a definition written out
+independently (numpy / scipy library routines, brute force on tiny inputs,
+closed forms, invariants the layer must satisfy).  A plausible slip in the
+oracle -- a dropped term, a wrong sign or index, a transposed operand, a
+swapped gate/up half, a sample instead of a population deviation, a wrong tie
+or drop rule -- fails at least one of them.
+
+Sources of the definitions: the MoE layer (gate picks k of n experts, weighted
+mix) from the FastMoE announcement page, "§1 MoE 设计" and Fig. 1, and the
+industry-overview page, "MoE的內涵"; Top-K routing from the Megatron-Core page,
+"关键特性"; capacity and dropping from its "MoE负载均衡的挑战与应对" section;
+the gating-logit normalisation from the Skywork-MoE news item, "技术创新 1", and
+the Skywork slides, slide 6; SwiGLU's gate/up halves from the Megatron-Core
+page, "权重转换要点"; ReLU experts from the FastMoE page, "特色三".
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import moe_inputs
+import oracle
+
+RNG = np.random.default_rng(12345)
+
+
+# ---------------------------------------------------------------- helpers
+def dense_ffn(xf, W1e, W2e, act, F):
+    """Textbook two-layer MLP in float64, written independently of the oracle."""
+    if act == oracle.RELU:
+        h = np.maximum(xf @ W1e.T, 0.0)
+    else:
+        g = xf @ W1e[:F].T
+        u = xf @ W1e[F:].T
+        h = g * scipy.special.expit(g) * u
+    return h @ W2e.T
+
+
+def brute_topk(z, k):
+    """Selection and order from counting: expert e takes position
+    #{e': z_e' > z_e} + #{e' < e: z_e' == z_e} when that is below k."""
+    E = z.shape[0]
+    pos = {}
+    for e in range(E):
+        r = sum(1 for f in range(E) if z[f] > z[e]) + sum(1 for f in range(e) if z[f] == z[e])
+        if r < k:
+            pos[r] = e
+    return np.array([pos[j] for j in range(k)], np.int32)
+
+
+def rand_bf16(shape, std=1.0):
+    return moe_inputs.f32_to_bf16_bits(RNG.standard_normal(shape).astype(np.float32) * np.float32(std))
+
+
+# ---------------------------------------------------------------- bf16 widening
+def test_bf16_widening_exact():
+    assert oracle.bf16_to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
+    assert oracle.bf16_to_f64(np.array([0xC000], np.uint16))[0] == -2.0
+    assert oracle.bf16_to_f64(np.array([0x3FC0], np.uint16))[0] == 1.5
+    assert oracle.bf16_to_f64(np.array([0x0001], np.uint16))[0] == 2.0 ** -133  # smallest subnormal
+    assert oracle._load().orc_bf16_to_double(0x4049) == 3.140625
+    # the generator's RNE rounding: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0)
+    assert moe_inputs.f32_to_bf16_bits(np.array([1.0 + 2.0 ** -8], np.float32))[0] == 0x3F80
+    assert moe_inputs.f32_to_bf16_bits(np.array([1.0 + 3 * 2.0 ** -8], np.float32))[0] == 0x3F82
+
+
+# ---------------------------------------------------------------- gate logits
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_logits_match_library_matmul(dtype):
+    T, d, E = 37, 96, 5
+    x = RNG.standard_normal((T, d)).astype(np.float32)
+    W = RNG.standard_normal((E, d)).astype(np.float32) * np.float32(0.1)
+    bg = RNG.standard_normal(E).astype(np.float32)
+    if dtype == "bf16":
+        x, W = moe_inputs.f32_to_bf16_bits(x), moe_inputs.f32_to_bf16_bits(W)
+    ze, z32 = oracle.gate_logits(x, W, bg)
+    ref = oracle.to_f64(x) @ oracle.to_f64(W).T + bg.astype(np.float64)[None, :]
+    assert np.max(np.abs(ze - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+    assert np.array_equal(z32, ref.astype(np.float32)) or np.max(np.abs(z32 - ref)) <= 2 ** -23 * np.max(np.abs(ref))
+    # without a bias the bias term must vanish
+    ze0, _ = oracle.gate_logits(x, W, None)
+    assert np.allclose(ze0 + bg[None, :], ze, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- top-k selection
+@pytest.mark.parametrize("E,k", [(1, 1), (2, 1), (3, 2), (4, 2), (5, 3), (6, 6), (6, 2)])
+def test_topk_brute_force_with_ties(E, k):
+    for trial in range(200):
+        # few distinct values -> many ties; include signed zeros
+        z = RNG.choice(np.array([-1.0, -0.0, 0.0, 0.5, 2.0], np.float32), size=E)
+        got = oracle.topk(z, k)
+        assert np.array_equal(got, brute_topk(z, k)), (z, got)
+        # library cross-check: stable sort by descending key, ties by index
+        lib = sorted(range(E), key=lambda e: (-float(z[e]), e))[:k]
+        assert got.tolist() == lib
+
+
+def test_topk_signed_zero_and_ties_go_to_lower_index():
+    z = np.array([-0.0, 0.0, -0.0, 0.0], np.float32)
+    assert oracle.topk(z, 2).tolist() == [0, 1]
+    z = np.array([0.0, -0.0, 1.0, -1.0], np.float32)
+    assert oracle.topk(z, 3).tolist() == [2, 0, 1]
+
+
+def test_route_selection_invariant_to_normalisation_and_exact_scaling():
+    T, E, k = 64, 16, 3
+    z = RNG.standard_normal((T, E)).astype(np.float32)
+    idx0, _ = oracle.route(z, k)
+    for norm, lam in [(True, 1.0), (True, 0.25), (True, 7.0)]:
+        idx1, _ = oracle.route(z, k, norm, lam)
+        assert np.array_equal(idx0, idx1)
+    idx2, _ = oracle.route(z * np.float32(4.0), k)  # exact in fp32
+    assert np.array_equal(idx0, idx2)
+
+
+# ---------------------------------------------------------------- normalisation
+def test_normalisation_zero_mean_unit_variance():
+    for E in (2, 8, 16, 512):
+        for lam in (1.0, 0.5, 3.0):
+            z = (RNG.standard_normal(E) * 3 + 1.7).astype(np.float32)
+            zt = oracle.normalize(z, lam)
+            s = zt / lam
+            assert abs(s.mean()) < 1e-12
+            assert abs((s * s).mean() - 1.0) < 1e-12
+            # library form: population standard deviation (numpy's default ddof=0)
+            zd = z.astype(np.float64)
+            ref = lam * (zd - zd.mean()) / zd.std()
+            assert np.max(np.abs(zt - ref)) < 1e-12
+
+
+def test_normalisation_constant_logits_give_uniform_probs():
+    z = np.full(8, 0.75, np.float32)
+    assert np.all(oracle.normalize(z, 1.0) == 0.0)
+    p = oracle.gate_probs(z, True, 1.0)
+    assert np.allclose(p, 1.0 / 8, rtol=0, atol=1e-15)
+
+
+def test_normalisation_sharpens_with_lambda():
+    # d log p_max / d lambda = zt_max/lambda - E_p[zt/lambda] >= 0: the top
+    # probability can only grow with lambda ("sharper" router probabilities).
+    for _ in range(50):
+        z = RNG.standard_normal(16).astype(np.float32)
+        prev = 0.0
+        for lam in (0.1, 0.3, 0.5, 1.0, 1.5, 2.0, 4.0, 8.0):
+            pm = oracle.gate_probs(z, True, lam).max()
+            assert pm >= prev - 1e-15
+            prev = pm
+
+
+# ---------------------------------------------------------------- softmax
+def test_softmax_library_and_closed_forms():
+    for E in (1, 2, 7, 64):
+        s = RNG.standard_normal(E) * 4
+        p = oracle.softmax(s)
+        assert abs(p.sum() - 1.0) < 1e-14
+        assert np.max(np.abs(p - scipy.special.softmax(s))) < 1e-15
+        assert np.max(np.abs(oracle.softmax(s + 123.0) - p)) < 1e-14  # shift invariance
+    assert oracle.softmax(np.array([5.0]))[0] == 1.0
+    p = oracle.softmax(np.array([1.0, 0.0]))
+    assert abs(p[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+
+
+def test_unnormalised_probs_are_softmax_of_fp32_logits():
+    z = RNG.standard_normal(10).astype(np.float32)
+    p = oracle.gate_probs(z, False, 1.0)
+    assert np.max(np.abs(p - scipy.special.softmax(z.astype(np.float64)))) < 1e-15
+
+
+# ---------------------------------------------------------------- weights
+def test_topk_weights_are_softmax_entries():
+    T, E, k = 50, 12, 4
+    z = RNG.standard_normal((T, E)).astype(np.float32)
+    for norm in (False, True):
+        idx, w, p = oracle.route(z, k, norm, 1.0, want_p=True)
+        assert np.array_equal(w, np.take_along_axis(p, idx.astype(np.int64), axis=1))
+        assert np.all(w.sum(axis=1) <= 1.0 + 1e-15)
+        # selection order = descending weight (softmax is increasing)
+        assert np.all(np.diff(w, axis=1) <= 1e-15)
+    idx, w = oracle.route(z, E)
+    assert np.max(np.abs(w.sum(axis=1) - 1.0)) < 1e-14
+
+
+# ---------------------------------------------------------------- capacity / dispatch
+def test_capacity_formula():
+    assert oracle.capacity(4096, 16, 2, 1.25) == 640
+    assert oracle.capacity(10, 3, 1, 1.0) == 4          # ceil(10/3)
+    assert oracle.capacity(10, 3, 1, 0.0) == -1
+    assert oracle.capacity(10, 3, 1, -2.0) == -1
+    assert oracle.capacity(8, 4, 2, 1e-30) == 1
+    assert oracle.capacity(4096, 8, 2, 0.25) == 256
+
+
+def brute_dispatch(idx, E, C):
+    T, k = idx.shape
+    slot = np.full((T, k), -1, np.int64)
+    counts = np.array([(idx == e).sum() for e in range(E)])
+    kept = counts if C < 0 else np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(kept)])
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            r = sum(1 for t2 in range(t) for j2 in range(k) if idx[t2, j2] == e)
+            if C < 0 or r < C:
+                slot[t, j] = offsets[e] + r
+    return counts, offsets, slot
+
+
+@pytest.mark.parametrize("T,E,k,cf", [(1, 1, 1, 0.0), (9, 3, 2, 0.0), (40, 5, 2, 0.5), (33, 4, 4, 1.0),
+                                      (60, 6, 1, 0.25), (20, 8, 3, 100.0)])
+def test_dispatch_brute_force(T, E, k, cf):
+    z = RNG.standard_normal((T, E)).astype(np.float32)
+    z[:, 0] += 1.0  # skew towards expert 0 so capacity bites
+    idx, _ = oracle.route(z, k)
+    C = oracle.capacity(T, E, k, cf)
+    got = oracle.dispatch(idx, E, C)
+    counts, offsets, slot = brute_dispatch(idx, E, C)
+    assert np.array_equal(got["counts"], counts)
+    assert np.array_equal(got["offsets"], offsets)
+    assert np.array_equal(got["slot"], slot)
+    assert got["counts"].sum() == T * k
+    dropped = T * k - got["offsets"][E]
+    assert dropped == int((got["slot"] < 0).sum())
+    if C < 0:
+        assert dropped == 0
+    P = got["P"]
+    st = got["src_token"]
+    for t in range(T):
+        for j in range(k):
+            if got["slot"][t, j] >= 0:
+                assert st[got["slot"][t, j]] == t
+
+
+def test_dispatch_matches_library_stable_sort():
+    T, E, k = 300, 7, 3
+    idx, _ = oracle.route(RNG.standard_normal((T, E)).astype(np.float32), k)
+    got = oracle.dispatch(idx, E, -1)
+    order = np.argsort(idx.ravel(), kind="stable")   # token-major list, stable by expert
+    assert np.array_equal(got["src_token"], (order // k).astype(np.int32))
+    # huge capacity is the same as dropless
+    big = oracle.dispatch(idx, E, 10 ** 9)
+    for key in ("counts", "offsets", "slot", "src_token"):
+        assert np.array_equal(big[key], got[key])
+
+
+def test_drops_keep_earliest_tokens():
+    T, E, k = 30, 3, 1
+    idx = np.zeros((T, k), np.int32)          # every token on expert 0
+    got = oracle.dispatch(idx, E, 4)
+    assert got["slot"][:4, 0].tolist() == [0, 1, 2, 3]
+    assert np.all(got["slot"][4:, 0] == -1)
+    assert got["offsets"].tolist() == [0, 4, 4, 4]
+
+
+# ---------------------------------------------------------------- expert FFN and layer
+@pytest.mark.parametrize("act", [oracle.RELU, oracle.SWIGLU])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_expert_is_dense_ffn(act, dtype):
+    # E = 1, k = 1: the only expert has probability 1 and the layer is a dense FFN.
+    T, d, F = 23, 64, 128
+    n1 = 2 * F if act == oracle.SWIGLU else F
+    x = RNG.standard_normal((T, d)).astype(np.float32)
+    Wg = RNG.standard_normal((1, d)).astype(np.float32)
+    W1 = (RNG.standard_normal((1, n1, d)) * 0.1).astype(np.float32)
+    W2 = (RNG.standard_normal((1, d, F)) * 0.1).astype(np.float32)
+    if dtype == "bf16":
+        x, Wg, W1, W2 = (moe_inputs.f32_to_bf16_bits(a) for a in (x, Wg, W1, W2))
+    out = oracle.moe_forward(x, Wg, None, W1, W2, k=1, F=F, act=act)
+    ref = dense_ffn(oracle.to_f64(x), oracle.to_f64(W1)[0], oracle.to_f64(W2)[0], act, F)
+    assert np.max(np.abs(out["y"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("act", [oracle.RELU, oracle.SWIGLU])
+def test_identical_experts_scale_by_weight_sum(act):
+    T, d, E, k, F = 31, 64, 6, 3, 64
+    n1 = 2 * F if act == oracle.SWIGLU else F
+    x = rand_bf16((T, d))
+    Wg = rand_bf16((E, d), 0.3)
+    W1_one = rand_bf16((1, n1, d), 0.1)
+    W2_one = rand_bf16((1, d, F), 0.1)
+    W1 = np.repeat(W1_one, E, axis=0)
+    W2 = np.repeat(W2_one, E, axis=0)
+    out = oracle.moe_forward(x, Wg, None, W1, W2, k=k, F=F, act=act)
+    ref = dense_ffn(oracle.to_f64(x), oracle.to_f64(W1_one)[0], oracle.to_f64(W2_one)[0], act, F)
+    ref = ref * out["topk_w"].sum(axis=1)[:, None]
+    assert np.max(np.abs(out["y"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("act", [oracle.RELU, oracle.SWIGLU])
+@pytest.mark.parametrize("norm,cf", [(False, 0.0), (True, 0.0), (False, 0.6), (True, 1.0)])
+def test_layer_equals_dense_mixture_formulation(act, norm, cf):
+    """Shazeer-style dense form: y_t = sum_e g_te FFN_e(x_t) with g_te = p_te when
+    expert e is a kept choice of token t, else 0 -- computed over every expert
+    by a second, vectorised code path."""
+    T, d, E, k, F = 16, 64, 6, 2, 64
+    n1 = 2 * F if act == oracle.SWIGLU else F
+    x = rand_bf16((T, d))
+    Wg = rand_bf16((E, d), 0.3)
+    bg = (RNG.standard_normal(E) * 0.5).astype(np.float32)
+    W1 = rand_bf16((E, n1, d), 0.1)
+    W2 = rand_bf16((E, d, F), 0.1)
+    lam = 1.0
+    out = oracle.moe_forward(x, Wg, bg, W1, W2, k=k, F=F, act=act, normalize_flag=norm, lam=lam, cf=cf)
+    xf = oracle.to_f64(x)
+    # independent gate: logits in float64, rounded to fp32 for the selection key
+    z = (xf @ oracle.to_f64(Wg).T + bg.astype(np.float64)).astype(np.float32)
+    zd = z.astype(np.float64)
+    s = lam * (zd - zd.mean(1, keepdims=True)) / zd.std(1, keepdims=True) if norm else zd
+    p = scipy.special.softmax(s, axis=1)
+    order = np.array([sorted(range(E), key=lambda e: (-float(z[t, e]), e))[:k] for t in range(T)])
+    C = math.ceil(cf * T * k / E) if cf > 0 else None
+    g = np.zeros((T, E))
+    seen = np.zeros(E, int)
+    for t in range(T):
+        for j in range(k):
+            e = order[t, j]
+            if C is None or seen[e] < C:
+                g[t, e] = p[t, e]
+            seen[e] += 1
+    ref = np.zeros((T, d))
+    for e in range(E):
+        ref += g[:, e:e + 1] * dense_ffn(xf, oracle.to_f64(W1)[e], oracle.to_f64(W2)[e], act, F)
+    assert np.array_equal(out["topk_idx"], order.astype(np.int32))
+    assert np.max(np.abs(out["y"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+    if cf > 0:
+        dropped = (out["slot"] < 0).sum()
+        assert out["counts"].sum() - out["offsets"][-1] == dropped
+
+
+def test_fully_dropped_token_outputs_zero():
+    T, d, E, k, F = 8, 64, 2, 1, 64
+    x = rand_bf16((T, d))
+    Wg = np.zeros((E, d), np.uint16)           # all logits 0 -> every token picks expert 0
+    W1 = rand_bf16((E, F, d), 0.1)
+    W2 = rand_bf16((E, d, F), 0.1)
+    out = oracle.moe_forward(x, Wg, None, W1, W2, k=k, F=F, act=oracle.RELU, cf=0.5)   # C = 2
+    assert out["C"] == 2
+    assert np.all(out["topk_idx"] == 0)
+    assert np.all(out["y"][2:] == 0.0)
+    assert np.any(out["y"][:2] != 0.0)
+
+
+def test_ffn_rows_and_combine_recompose_forward():
+    T, d, E, k, F = 40, 64, 5, 2, 128
+    x = rand_bf16((T, d))
+    Wg = rand_bf16((E, d), 0.3)
+    W1 = rand_bf16((E, 2 * F, d), 0.1)
+    W2 = rand_bf16((E, d, F), 0.1)
+    out = oracle.moe_forward(x, Wg, None, W1, W2, k=k, F=F, act=oracle.SWIGLU, cf=0.7)
+    xp = x[out["src_token"]]
+    yp = oracle.ffn_rows(xp, out["offsets"], W1, W2, oracle.SWIGLU, F)
+    # expert of each row from offsets: compare to a direct per-row call
+    for r in (0, out["P"] - 1) + tuple(out["offsets"][1:-1]):
+        if r >= out["P"]:
+            continue
+        e = int(np.searchsorted(out["offsets"], r, side="right") - 1)
+        ref = oracle.expert_ffn(W1, W2, e, oracle.to_f64(xp[r]), oracle.SWIGLU, F)
+        assert np.array_equal(yp[r], ref)
+    y = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            s = out["slot"][t, j]
+            if s >= 0:
+                y[t] += out["topk_w"][t, j] * yp[s]
+    assert np.max(np.abs(y - out["y"])) <= 1e-12 * np.max(np.abs(y))
+    # the oracle's combine on float64-exact expert outputs
+    yp32 = yp.astype(np.float32)
+    yc = oracle.combine(yp32, out["slot"], out["topk_w"], T)
+    yref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            s = out["slot"][t, j]
+            if s >= 0:
+                yref[t] += out["topk_w"][t, j] * yp32[s].astype(np.float64)
+    assert np.max(np.abs(yc - yref)) <= 1e-13 * np.max(np.abs(yref))
+
+
+def test_forward_token_subset_matches_full():
+    T, d, E, k, F = 24, 64, 4, 2, 64
+    x = rand_bf16((T, d))
+    Wg = rand_bf16((E, d), 0.3)
+    W1 = rand_bf16((E, F, d), 0.1)
+    W2 = rand_bf16((E, d, F), 0.1)
+    full = oracle.moe_forward(x, Wg, None, W1, W2, k=k, F=F, act=oracle.RELU)
+    toks = np.array([3, 17, 0, 23], np.int32)
+    sub = oracle.forward_tokens(x, W1, W2, full["topk_idx"], full["topk_w"], full["slot"], oracle.RELU, F, toks)
+    assert np.array_equal(sub, full["y"][toks])
+
+
+# ---------------------------------------------------------------- calibrated inputs
+@pytest.mark.parametrize("name", [n for n, c in moe_inputs.CASES.items() if c.bias == "zipf"])
+def test_zipf_bias_realises_target_shares(name):
+    case = moe_inputs.get(name)
+    inp = moe_inputs.make(case, weights=False)
+    _ze, z32 = oracle.gate_logits(inp["x"], inp["Wg"], inp["bg"])
+    idx, _ = oracle.route(z32, case.k)
+    f = np.bincount(idx.ravel(), minlength=case.E) / (case.T * case.k)
+    q = moe_inputs.zipf_shares(case.E, case.zipf_s)
+    assert np.max(np.abs(f - q)) < 0.005, (f, q)
