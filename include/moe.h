@@ -1,0 +1,185 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparsely-gated mixture-of-experts
+ * layer forward.
+ *
+ * The layer (FastMoE announcement page, "§1 MoE 设计", Fig. 1; industry
+ * overview page, "MoE的內涵"): a gate scores every token against E experts,
+ * each token goes to its k best experts, each expert is a two-layer MLP, and
+ * the token's output is the gate-weighted sum of its experts' outputs.  The
+ * entry points below are its steps:
+ *
+ *   moe_route        gate GEMM -> [gating-logit normalisation] -> softmax -> top-k
+ *   moe_permute      per-expert counts, capacity clip, stable counting-sort
+ *                    permutation of the token rows by expert
+ *   moe_expert_up    first expert linear layer + activation, per expert segment
+ *   moe_expert_down  second expert linear layer, per expert segment
+ *   moe_grouped_ffn  moe_expert_up then moe_expert_down
+ *   moe_combine      gate-weighted un-permute back to token order
+ *   moe_forward      all of the above
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory: every tensor argument is DEVICE memory owned by the caller (for
+ *   example a torch tensor's data_ptr()).  The library never allocates, frees,
+ *   copies to the host or synchronises; it only enqueues kernels on `stream`
+ *   (a hipStream_t; NULL is the null stream).  Results are valid once the
+ *   caller has synchronised with that stream.  Outputs must not alias inputs
+ *   or each other.  The library keeps no state between calls except a cached
+ *   per-device compute-unit count; calls are reentrant.
+ * Layout: every tensor is dense row-major.  "dtype" tensors hold fp32 or bf16
+ *   (bf16 as raw 16-bit patterns) according to problem->dtype.
+ *     x       [T][d]      dtype   token activations
+ *     Wg      [E][d]      dtype   gate weight (out x in, like nn.Linear.weight)
+ *     bg      [E]         fp32    gate bias (nullable)
+ *     logits  [T][E]      fp32
+ *     W1      [E][n1][d]  dtype   n1 = F (ReLU) or 2F (SwiGLU: rows 0..F-1 are
+ *                                 the gate projection, rows F..2F-1 the up
+ *                                 projection, the fused order of the
+ *                                 Megatron-Core page, "权重转换要点")
+ *     W2      [E][d][F]   dtype
+ *     topk_idx, slot [T][k] int32;  topk_w [T][k] fp32
+ *     counts [E], offsets [E+1] int32;  src_token [T*k] int32
+ *     x_perm, y_perm [T*k][d] dtype;  h [T*k][F] dtype
+ *   Only the first offsets[E] rows of x_perm / y_perm / h / src_token are
+ *   meaningful (P = offsets[E] = number of kept assignments).
+ * Alignment: dtype tensors and the workspace must be 16-byte aligned, int32
+ *   and fp32 tensors 4-byte aligned.
+ * Errors: arguments are checked on the host before anything is enqueued; on
+ *   any error nothing is enqueued, the call returns a non-zero moe_status and
+ *   moe_last_error() (per thread) says why.  A failed kernel launch returns
+ *   MOE_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *   synchronisation.  Non-finite logits or inputs violate a precondition and
+ *   give unspecified (but in-bounds) results.
+ * Limits: 1 <= k <= min(E, 8), E <= 1024, 0 <= T <= 2^24, d and F multiples
+ *   of 64 with 64 <= d, F <= 65536.  T == 0 is a valid empty call.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad option */
+    MOE_ERR_UNSUPPORTED = 2, /* outside the limits above */
+    MOE_ERR_WORKSPACE = 3,   /* workspace too small */
+    MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 };
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+typedef struct {
+    int32_t T;                /* tokens */
+    int32_t d;                /* model width */
+    int32_t E;                /* experts */
+    int32_t k;                /* experts per token */
+    int32_t F;                /* expert hidden width */
+    int32_t act;              /* MOE_ACT_RELU | MOE_ACT_SWIGLU */
+    int32_t dtype;            /* MOE_F32 | MOE_BF16 */
+    int32_t normalize;        /* 0: softmax(z); 1: softmax(lambda * standardise(z)) */
+    float lambda;             /* finite and > 0 when normalize == 1 */
+    float capacity_factor;    /* <= 0: dropless; > 0: capacity C = ceil(cf*T*k/E) */
+} moe_problem;
+
+/* Optional outputs of moe_forward; each field may be NULL (the library then
+ * keeps that tensor in the workspace). */
+typedef struct {
+    int32_t* topk_idx;  /* [T][k] */
+    float* topk_w;      /* [T][k] */
+    int32_t* counts;    /* [E] assignments per expert before the capacity clip */
+    int32_t* offsets;   /* [E+1] */
+    int32_t* slot;      /* [T][k] permuted row, -1 when dropped */
+    int32_t* src_token; /* [T*k] */
+} moe_route_info;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status s);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Expert capacity of a problem: C = ceil(cf * T * k / E) evaluated in double
+ * (cf > 0), or -1 when dropless (cf <= 0).  Tokens beyond C on one expert are
+ * dropped and contribute zero; the caller's residual connection carries them
+ * (Megatron-Core page, "MoE负载均衡的挑战与应对" and its Q&A).  Host only. */
+moe_status moe_capacity(const moe_problem* p, int32_t* C);
+
+/* Bytes of workspace that suffice for every entry point of this problem
+ * (moe_forward needs the most: routing, permutation, x_perm, h, y_perm).
+ * Host only. */
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* Gate and routing (FastMoE page, "特色二": one fully connected layer as
+ * gate; Skywork-MoE news item, "技术创新 1", and Skywork slides, slide 6:
+ * gating-logit normalisation; Megatron-Core page, "关键特性": Top-K router).
+ *   If x and Wg are both non-NULL: logits[t,e] = sum_i x[t,i] Wg[e,i] + bg[e]
+ *   (products and sums in fp64, rounded once to fp32) is WRITTEN.
+ *   If x and Wg are both NULL: logits is an INPUT.
+ *   Then per token: s = z, or lambda*(z - mean_e z)/std_e z (population std;
+ *   a token with std 0 gets s = 0); p = softmax(s) over all E experts;
+ *   topk_idx[t,0..k-1] = the k largest fp32 logits in descending order, equal
+ *   logits to the lower expert index, -0 == +0; topk_w[t,j] = p[topk_idx[t,j]]
+ *   (not renormalised). */
+moe_status moe_route(const moe_problem* p, const void* x, const void* Wg, const float* bg,
+                     float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Counting, capacity and permutation (Megatron-Core page, "关键特性": token
+ * permutation; "MoE负载均衡的挑战与应对": capacity / dropless).
+ *   counts[e] = number of (t,j) with topk_idx[t,j] == e;
+ *   kept_e = min(counts[e], C) (C from moe_capacity; no clip when dropless);
+ *   offsets = exclusive prefix sum of kept (E+1 entries);
+ *   the rank of (t,j) on its expert e is the number of earlier tokens t' < t
+ *   that chose e; it is kept iff rank < C, at row offsets[e] + rank:
+ *   slot[t,j] = that row (else -1), src_token[row] = t, x_perm[row] = x[t].
+ * topk_idx entries must lie in [0,E) and be distinct within a token (entries
+ * outside [0,E) are skipped; duplicates give unspecified rows, never writes
+ * out of bounds).  Needs ws_bytes >= moe_workspace_size. */
+moe_status moe_permute(const moe_problem* p, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* slot, int32_t* src_token, void* x_perm, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* First expert layer over the expert segments (FastMoE page, "特色三": ReLU
+ * two-layer MLP experts, many experts on one GPU; Megatron-Core page,
+ * "关键特性": GroupedGEMM): for every expert e and row r in
+ * [offsets[e], offsets[e+1]):  u = W1[e] x_perm[r];
+ *   ReLU:   h[r,f] = max(u_f, 0)
+ *   SwiGLU: h[r,f] = silu(u_f) * u_{F+f},  silu(g) = g / (1 + exp(-g))
+ * fp32 accumulation, h stored in dtype.  offsets is read on the device (no
+ * host synchronisation); offsets[E] <= T*k is required. */
+moe_status moe_expert_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1,
+                         void* h, void* stream);
+
+/* Second expert layer: y_perm[r] = W2[e] h[r] for r in expert e's segment. */
+moe_status moe_expert_down(const moe_problem* p, const void* h, const int32_t* offsets, const void* W2,
+                           void* y_perm, void* stream);
+
+/* moe_expert_up then moe_expert_down, with h in the workspace. */
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1,
+                           const void* W2, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine (industry overview page, "MoE的內涵": the gate weights the
+ * experts' mix): y[t] = sum over j = 0..k-1 with slot[t,j] >= 0, in that
+ * order, of topk_w[t,j] * y_perm[slot[t,j]] (fp32 accumulation, stored in
+ * dtype).  A token with every choice dropped gets y[t] = 0. */
+moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w,
+                       void* y, void* stream);
+
+/* The whole layer.  Wg == NULL means logits is a given INPUT (x is still the
+ * token activations); otherwise logits (nullable) receives the gate logits.
+ * info (nullable) receives the routing and permutation.  Needs
+ * ws_bytes >= moe_workspace_size. */
+moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                       const void* W2, void* y, float* logits, const moe_route_info* info, void* ws,
+                       size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,419 @@
+// Host side of the C ABI declared in include/moe.h: argument checks, workspace
+// layout and the launch sequence of the MoE-layer forward.  Nothing here
+// allocates device memory, copies to the host or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "moe.h"
+
+extern "C" {
+hipError_t moe_launch_gate(int dtype, const void* x, const void* Wg, const float* bg, float* logits, int T, int d,
+                           int E, hipStream_t stream);
+hipError_t moe_launch_router(const float* logits, int T, int E, int k, int normalize, float lambda,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream);
+hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, const void* x, int T, int d, int E, int k,
+                              long long C, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src_token,
+                              void* x_perm, int32_t* chunk_cnt, hipStream_t stream);
+hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const void* W, void* C,
+                                   const int32_t* offsets, int E, int K, int Nw, int Nout, int F, int max_rows,
+                                   int ncu, hipStream_t stream);
+hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w, int T, int d,
+                              int k, void* y, hipStream_t stream);
+}
+
+namespace {
+
+constexpr int kChunk = 256;      // tokens per permutation chunk (matches the permute kernels)
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 8;
+constexpr int kMaxT = 1 << 24;
+constexpr int kMaxDim = 65536;
+constexpr size_t kAlign = 256;
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+moe_status ok()
+{
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+size_t elem_bytes(const moe_problem* p) { return p->dtype == MOE_F32 ? 4 : 2; }
+int n1_of(const moe_problem* p) { return p->act == MOE_ACT_SWIGLU ? 2 * p->F : p->F; }
+
+long long capacity_of(const moe_problem* p)
+{
+    const double cf = p->capacity_factor;
+    if (!(cf > 0.0))
+        return -1;
+    return (long long)std::ceil(cf * p->T * p->k / p->E);
+}
+
+moe_status check_problem(const moe_problem* p)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
+    if (p->T < 0 || p->T > kMaxT)
+        return fail(p->T < 0 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED, "T=%d outside [0, %d]", p->T, kMaxT);
+    if (p->E < 1 || p->E > kMaxE)
+        return fail(p->E < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED, "E=%d outside [1, %d]", p->E, kMaxE);
+    if (p->k < 1 || p->k > p->E)
+        return fail(MOE_ERR_INVALID_ARG, "k=%d outside [1, E=%d]", p->k, p->E);
+    if (p->k > kMaxK)
+        return fail(MOE_ERR_UNSUPPORTED, "k=%d above %d", p->k, kMaxK);
+    if (p->d < 64 || p->d > kMaxDim || p->d % 64)
+        return fail(MOE_ERR_UNSUPPORTED, "d=%d must be a multiple of 64 in [64, %d]", p->d, kMaxDim);
+    if (p->F < 64 || p->F > kMaxDim || p->F % 64)
+        return fail(MOE_ERR_UNSUPPORTED, "F=%d must be a multiple of 64 in [64, %d]", p->F, kMaxDim);
+    if (p->act != MOE_ACT_RELU && p->act != MOE_ACT_SWIGLU)
+        return fail(MOE_ERR_INVALID_ARG, "act=%d is neither MOE_ACT_RELU nor MOE_ACT_SWIGLU", p->act);
+    if (p->dtype != MOE_F32 && p->dtype != MOE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "dtype=%d is neither MOE_F32 nor MOE_BF16", p->dtype);
+    if (p->normalize != 0 && p->normalize != 1)
+        return fail(MOE_ERR_INVALID_ARG, "normalize=%d is neither 0 nor 1", p->normalize);
+    if (p->normalize && !(std::isfinite(p->lambda) && p->lambda > 0.0f))
+        return fail(MOE_ERR_INVALID_ARG, "lambda=%g must be finite and > 0 with normalisation", (double)p->lambda);
+    if (std::isnan(p->capacity_factor) || std::isinf(p->capacity_factor))
+        return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+    const long long rows = (long long)p->T * p->k;
+    if (rows * (long long)std::max(n1_of(p), p->d) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "problem too large");
+    return MOE_OK;
+}
+
+moe_status check_ptr(const void* ptr, const char* name, size_t align)
+{
+    if (!ptr)
+        return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+    if (reinterpret_cast<uintptr_t>(ptr) % align)
+        return fail(MOE_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+    return MOE_OK;
+}
+
+#define CHECK(expr)                     \
+    do {                                \
+        moe_status _s = (expr);         \
+        if (_s != MOE_OK)               \
+            return _s;                  \
+    } while (0)
+
+// Workspace layout of a problem: every piece 256-byte aligned.
+struct Layout {
+    size_t topk_idx, topk_w, counts, offsets, slot, src_token, chunk_cnt, logits, x_perm, h, y_perm, total;
+};
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+Layout layout_of(const moe_problem* p)
+{
+    Layout L;
+    const size_t T = (size_t)p->T, k = (size_t)p->k, E = (size_t)p->E, d = (size_t)p->d, F = (size_t)p->F;
+    const size_t b = elem_bytes(p);
+    const size_t nchunks = (T + kChunk - 1) / kChunk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round_up(bytes);
+        return at;
+    };
+    L.topk_idx = take(T * k * 4);
+    L.topk_w = take(T * k * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.slot = take(T * k * 4);
+    L.src_token = take(T * k * 4);
+    L.chunk_cnt = take(std::max<size_t>(nchunks, 1) * E * 4);
+    L.logits = take(T * E * 4);
+    L.x_perm = take(T * k * d * b);
+    L.h = take(T * k * F * b);
+    L.y_perm = take(T * k * d * b);
+    L.total = off;
+    return L;
+}
+
+template <typename Tp>
+Tp* at(void* ws, size_t off)
+{
+    return reinterpret_cast<Tp*>(static_cast<char*>(ws) + off);
+}
+
+int cu_count()
+{
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+moe_status hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_problem* p, const void* ws, size_t ws_bytes)
+{
+    const size_t need = layout_of(p).total;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    return check_ptr(ws, "ws", 16);
+}
+
+// ---- the steps, on validated arguments
+moe_status do_route(const moe_problem* p, const void* x, const void* Wg, const float* bg, float* logits,
+                    int32_t* topk_idx, float* topk_w, hipStream_t s)
+{
+    if (Wg) {
+        CHECK(hip_status(moe_launch_gate(p->dtype, x, Wg, bg, logits, p->T, p->d, p->E, s), "gate launch"));
+    }
+    return hip_status(moe_launch_router(logits, p->T, p->E, p->k, p->normalize, p->lambda, topk_idx, topk_w, s),
+                      "router launch");
+}
+
+moe_status do_permute(const moe_problem* p, const int32_t* topk_idx, const void* x, int32_t* counts,
+                      int32_t* offsets, int32_t* slot, int32_t* src_token, void* x_perm, void* ws, hipStream_t s)
+{
+    const Layout L = layout_of(p);
+    return hip_status(moe_launch_permute(p->dtype, topk_idx, x, p->T, p->d, p->E, p->k, capacity_of(p), counts,
+                                         offsets, slot, src_token, x_perm, at<int32_t>(ws, L.chunk_cnt), s),
+                      "permute launch");
+}
+
+moe_status do_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1, void* h,
+                 hipStream_t s)
+{
+    const int epi = p->act == MOE_ACT_SWIGLU ? 2 : 1;
+    return hip_status(moe_launch_grouped_gemm(p->dtype, epi, x_perm, W1, h, offsets, p->E, p->d, n1_of(p), p->F, p->F,
+                                              p->T * p->k, cu_count(), s),
+                      "expert up launch");
+}
+
+moe_status do_down(const moe_problem* p, const void* h, const int32_t* offsets, const void* W2, void* y_perm,
+                   hipStream_t s)
+{
+    return hip_status(moe_launch_grouped_gemm(p->dtype, 0, h, W2, y_perm, offsets, p->E, p->F, p->d, p->d, p->F,
+                                              p->T * p->k, cu_count(), s),
+                      "expert down launch");
+}
+
+moe_status do_combine(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w, void* y,
+                      hipStream_t s)
+{
+    return hip_status(moe_launch_combine(p->dtype, y_perm, slot, topk_w, p->T, p->d, p->k, y, s), "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_capacity(const moe_problem* p, int32_t* C)
+{
+    CHECK(check_problem(p));
+    if (!C)
+        return fail(MOE_ERR_INVALID_ARG, "C is NULL");
+    const long long c = capacity_of(p);
+    *C = c > (long long)INT32_MAX ? INT32_MAX : (int32_t)c;
+    return ok();
+}
+
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes)
+{
+    CHECK(check_problem(p));
+    if (!bytes)
+        return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = layout_of(p).total;
+    return ok();
+}
+
+moe_status moe_route(const moe_problem* p, const void* x, const void* Wg, const float* bg, float* logits,
+                     int32_t* topk_idx, float* topk_w, void* stream)
+{
+    CHECK(check_problem(p));
+    if ((x == nullptr) != (Wg == nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "x and Wg must both be given (gate) or both be NULL (logits given)");
+    if (p->T == 0)
+        return ok();
+    if (Wg) {
+        CHECK(check_ptr(x, "x", 16));
+        CHECK(check_ptr(Wg, "Wg", 16));
+        if (bg)
+            CHECK(check_ptr(bg, "bg", 4));
+    }
+    CHECK(check_ptr(logits, "logits", 4));
+    CHECK(check_ptr(topk_idx, "topk_idx", 4));
+    CHECK(check_ptr(topk_w, "topk_w", 4));
+    CHECK(do_route(p, x, Wg, bg, logits, topk_idx, topk_w, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_permute(const moe_problem* p, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* slot, int32_t* src_token, void* x_perm, void* ws, size_t ws_bytes,
+                       void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(topk_idx, "topk_idx", 4));
+    CHECK(check_ptr(x, "x", 16));
+    CHECK(check_ptr(counts, "counts", 4));
+    CHECK(check_ptr(offsets, "offsets", 4));
+    CHECK(check_ptr(slot, "slot", 4));
+    CHECK(check_ptr(src_token, "src_token", 4));
+    CHECK(check_ptr(x_perm, "x_perm", 16));
+    CHECK(check_ws(p, ws, ws_bytes));
+    CHECK(do_permute(p, topk_idx, x, counts, offsets, slot, src_token, x_perm, ws, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_expert_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1, void* h,
+                         void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(x_perm, "x_perm", 16));
+    CHECK(check_ptr(offsets, "offsets", 4));
+    CHECK(check_ptr(W1, "W1", 16));
+    CHECK(check_ptr(h, "h", 16));
+    CHECK(do_up(p, x_perm, offsets, W1, h, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_expert_down(const moe_problem* p, const void* h, const int32_t* offsets, const void* W2,
+                           void* y_perm, void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(h, "h", 16));
+    CHECK(check_ptr(offsets, "offsets", 4));
+    CHECK(check_ptr(W2, "W2", 16));
+    CHECK(check_ptr(y_perm, "y_perm", 16));
+    CHECK(do_down(p, h, offsets, W2, y_perm, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1,
+                           const void* W2, void* y_perm, void* ws, size_t ws_bytes, void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(x_perm, "x_perm", 16));
+    CHECK(check_ptr(offsets, "offsets", 4));
+    CHECK(check_ptr(W1, "W1", 16));
+    CHECK(check_ptr(W2, "W2", 16));
+    CHECK(check_ptr(y_perm, "y_perm", 16));
+    CHECK(check_ws(p, ws, ws_bytes));
+    const Layout L = layout_of(p);
+    void* h = at<char>(ws, L.h);
+    CHECK(do_up(p, x_perm, offsets, W1, h, (hipStream_t)stream));
+    CHECK(do_down(p, h, offsets, W2, y_perm, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w, void* y,
+                       void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(y_perm, "y_perm", 16));
+    CHECK(check_ptr(slot, "slot", 4));
+    CHECK(check_ptr(topk_w, "topk_w", 4));
+    CHECK(check_ptr(y, "y", 16));
+    CHECK(do_combine(p, y_perm, slot, topk_w, y, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                       const void* W2, void* y, float* logits, const moe_route_info* info, void* ws, size_t ws_bytes,
+                       void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(x, "x", 16));
+    CHECK(check_ptr(W1, "W1", 16));
+    CHECK(check_ptr(W2, "W2", 16));
+    CHECK(check_ptr(y, "y", 16));
+    if (Wg) {
+        CHECK(check_ptr(Wg, "Wg", 16));
+        if (bg)
+            CHECK(check_ptr(bg, "bg", 4));
+        if (logits)
+            CHECK(check_ptr(logits, "logits", 4));
+    } else {
+        if (!logits)
+            return fail(MOE_ERR_INVALID_ARG, "logits must be given when Wg is NULL");
+        CHECK(check_ptr(logits, "logits", 4));
+    }
+    CHECK(check_ws(p, ws, ws_bytes));
+    const Layout L = layout_of(p);
+    moe_route_info r = {};
+    if (info)
+        r = *info;
+#define PICK(field, type) (r.field ? r.field : at<type>(ws, L.field))
+    int32_t* topk_idx = PICK(topk_idx, int32_t);
+    float* topk_w = PICK(topk_w, float);
+    int32_t* counts = PICK(counts, int32_t);
+    int32_t* offsets = PICK(offsets, int32_t);
+    int32_t* slot = PICK(slot, int32_t);
+    int32_t* src_token = PICK(src_token, int32_t);
+#undef PICK
+    const void* ptrs[] = {topk_idx, topk_w, counts, offsets, slot, src_token};
+    for (const void* q : ptrs)
+        CHECK(check_ptr(q, "route info field", 4));
+    float* z = logits ? logits : at<float>(ws, L.logits);
+    void* x_perm = at<char>(ws, L.x_perm);
+    void* h = at<char>(ws, L.h);
+    void* y_perm = at<char>(ws, L.y_perm);
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(do_route(p, Wg ? x : nullptr, Wg, bg, z, topk_idx, topk_w, s));
+    CHECK(do_permute(p, topk_idx, x, counts, offsets, slot, src_token, x_perm, ws, s));
+    CHECK(do_up(p, x_perm, offsets, W1, h, s));
+    CHECK(do_down(p, h, offsets, W2, y_perm, s));
+    CHECK(do_combine(p, y_perm, slot, topk_w, y, s));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Gate-weighted combine back to token order (gfx950).
+//
+// The gate weights the chosen experts' outputs (industry overview page,
+// "MoE的內涵"); a dropped choice contributes nothing and the residual outside
+// the layer carries the token (Megatron-Core page, "MoE负载均衡的挑战与应对").
+//
+// One wavefront per token: for j = 0..k-1 in order, if slot[t,j] >= 0 it
+// reads the row y_perm[slot] with 16-byte loads and accumulates
+// topk_w[t,j] * row in fp32 (fma, fixed order, so results are reproducible),
+// then writes y[t] once.  Each lane owns up to 8 16-byte vectors per pass.
+#include "common.h"
+
+namespace moe {
+
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::storage* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ slot,
+                                                          const float* __restrict__ topk_w, int T, int d, int k,
+                                                          typename ET::storage* __restrict__ y)
+{
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T)
+        return;
+    constexpr int kPer = 16 / ET::kBytes;
+    const int nvec = d / kPer;
+    int rows[8];
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
+        w[j] = (j < k) ? topk_w[(size_t)t * k + j] : 0.0f;
+    }
+    for (int v0 = 0; v0 < nvec; v0 += kWave * 8) {
+        float acc[8][kPer];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int q = 0; q < kPer; ++q)
+                acc[u][q] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] < 0)
+                continue;
+            const uint4* src = reinterpret_cast<const uint4*>(y_perm + (size_t)rows[j] * d);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int v = v0 + u * kWave + lane;
+                if (v < nvec) {
+                    const uint4 raw = src[v];
+                    float f[kPer];
+                    if constexpr (ET::kBytes == 2) {
+                        unpack8(raw, f, bf16_t{});
+                    } else {
+                        f[0] = __uint_as_float(raw.x);
+                        f[1] = __uint_as_float(raw.y);
+                        f[2] = __uint_as_float(raw.z);
+                        f[3] = __uint_as_float(raw.w);
+                    }
+#pragma unroll
+                    for (int q = 0; q < kPer; ++q)
+                        acc[u][q] = fmaf(w[j], f[q], acc[u][q]);
+                }
+            }
+        }
+        uint4* dst = reinterpret_cast<uint4*>(y + (size_t)t * d);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < nvec) {
+                uint4 o;
+                if constexpr (ET::kBytes == 2) {
+                    o.x = f32_to_bf16_bits(acc[u][0]) | (f32_to_bf16_bits(acc[u][1]) << 16);
+                    o.y = f32_to_bf16_bits(acc[u][2]) | (f32_to_bf16_bits(acc[u][3]) << 16);
+                    o.z = f32_to_bf16_bits(acc[u][4]) | (f32_to_bf16_bits(acc[u][5]) << 16);
+                    o.w = f32_to_bf16_bits(acc[u][6]) | (f32_to_bf16_bits(acc[u][7]) << 16);
+                } else {
+                    o.x = __float_as_uint(acc[u][0]);
+                    o.y = __float_as_uint(acc[u][1]);
+                    o.z = __float_as_uint(acc[u][2]);
+                    o.w = __float_as_uint(acc[u][3]);
+                }
+                dst[v] = o;
+            }
+        }
+    }
+}
+
+}  // namespace moe
+
+extern "C" hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w,
+                                         int T, int d, int k, void* y, hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid((T + 3) / 4), block(256);
+    if (dtype == 0)
+        moe_combine_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)y_perm, slot, topk_w, T, d, k, (float*)y);
+    else
+        moe_combine_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)y_perm, slot, topk_w, T, d, k,
+                                                               (uint16_t*)y);
+    return hipGetLastError();
+}

@@ -1,0 +1,231 @@
+// Counting-sort permutation of token rows by expert (gfx950).
+//
+// Megatron-Core page, "关键特性": token permutation kernel; "MoE负载均衡的挑战与应对":
+// capacity with dropping, or dropless variable-size expert inputs.
+//
+// The T*k assignments are ordered by (expert, token).  The rank of assignment
+// (t,j) on its expert e is the number of earlier tokens that chose e; ranks
+// below the capacity C are kept at row offsets[e] + rank.  No atomic decides
+// a rank, so the permutation is the same on every run:
+//
+//   count   chunks of 256 tokens build per-chunk expert histograms
+//           (LDS atomics only count; counts do not depend on their order)
+//   scan    one block: per-expert prefix over chunks (-> each chunk's base
+//           rank), counts, capacity clip, exclusive scan over experts
+//   scatter chunk by chunk again: rank = chunk base + earlier wavefronts'
+//           counts + rank inside the wavefront, the last from ballots that
+//           find the lanes holding the same expert; writes slot, src_token
+//   gather  one wavefront per token reads x[t] once (16-byte loads) and
+//           writes it to each of the token's kept rows of x_perm
+#include "common.h"
+
+namespace moe {
+
+constexpr int kChunk = 256;  // tokens per chunk (one thread per token)
+constexpr int kMaxE = 1024;
+
+__global__ __launch_bounds__(kChunk) void moe_count_kernel(const int32_t* __restrict__ topk_idx, int T, int E,
+                                                           int k, int32_t* __restrict__ chunk_cnt)
+{
+    __shared__ int32_t hist[kMaxE];
+    for (int e = threadIdx.x; e < E; e += kChunk)
+        hist[e] = 0;
+    __syncthreads();
+    const int t = blockIdx.x * kChunk + threadIdx.x;
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_idx[(size_t)t * k + j];
+            if (e >= 0 && e < E)
+                atomicAdd(&hist[e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kChunk)
+        chunk_cnt[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One block of 1024 threads; thread e owns expert e.  chunk_cnt is turned
+// into each chunk's base rank in place.
+__global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ chunk_cnt, int nchunks, int E,
+                                                        long long C, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets)
+{
+    __shared__ int32_t wsum[1024 / kWave];
+    const int e = threadIdx.x;
+    int running = 0;
+    if (e < E) {
+        int c = 0;
+        for (; c + 4 <= nchunks; c += 4) {
+            const int v0 = chunk_cnt[(size_t)(c + 0) * E + e];
+            const int v1 = chunk_cnt[(size_t)(c + 1) * E + e];
+            const int v2 = chunk_cnt[(size_t)(c + 2) * E + e];
+            const int v3 = chunk_cnt[(size_t)(c + 3) * E + e];
+            chunk_cnt[(size_t)(c + 0) * E + e] = running;
+            chunk_cnt[(size_t)(c + 1) * E + e] = running + v0;
+            chunk_cnt[(size_t)(c + 2) * E + e] = running + v0 + v1;
+            chunk_cnt[(size_t)(c + 3) * E + e] = running + v0 + v1 + v2;
+            running += v0 + v1 + v2 + v3;
+        }
+        for (; c < nchunks; ++c) {
+            const int v = chunk_cnt[(size_t)c * E + e];
+            chunk_cnt[(size_t)c * E + e] = running;
+            running += v;
+        }
+        counts[e] = running;
+    }
+    int kept = (e < E) ? running : 0;
+    if (C >= 0 && kept > C)
+        kept = (int)C;
+    // exclusive scan of kept over the 1024 threads
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    int incl = kept;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(incl, o);
+        if (lane >= o)
+            incl += n;
+    }
+    if (lane == kWave - 1)
+        wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w)
+        base += wsum[w];
+    if (e < E)
+        offsets[e] = base + incl - kept;
+    if (e == E - 1)
+        offsets[E] = base + incl;
+}
+
+__global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __restrict__ topk_idx, int T, int E,
+                                                             int k, long long C,
+                                                             const int32_t* __restrict__ chunk_base,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ slot,
+                                                             int32_t* __restrict__ src_token)
+{
+    constexpr int kWaves = kChunk / kWave;
+    __shared__ int32_t wave_cnt[kWaves][kMaxE];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    for (int i = threadIdx.x; i < kWaves * E; i += kChunk)
+        wave_cnt[i / E][i % E] = 0;
+    __syncthreads();
+    const int t = blockIdx.x * kChunk + threadIdx.x;
+    const bool live = t < T;
+    int my[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        my[j] = -1;
+        if (j < k && live) {
+            const int e = topk_idx[(size_t)t * k + j];
+            my[j] = (e >= 0 && e < E) ? e : -1;
+        }
+        if (my[j] >= 0)
+            atomicAdd(&wave_cnt[wave][my[j]], 1);
+    }
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < E)
+        ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j >= k)
+            break;
+        const int e = my[j];
+        // lanes below this one whose choice in some column equals e
+        int r = 0;
+#pragma unroll
+        for (int j2 = 0; j2 < 8; ++j2) {
+            if (j2 >= k)
+                break;
+            const int col = my[j2];
+            uint64_t peers = __ballot(col >= 0);
+            for (int b = 0; b < nbits; ++b) {
+                const uint64_t ones = __ballot(col >= 0 && ((col >> b) & 1));
+                peers &= (((e >> b) & 1) ? ones : ~ones);
+            }
+            r += __popcll(peers & below);
+        }
+        if (e < 0)
+            continue;
+        for (int w = 0; w < wave; ++w)
+            r += wave_cnt[w][e];
+        const long long rank = (long long)chunk_base[(size_t)blockIdx.x * E + e] + r;
+        if (C < 0 || rank < C) {
+            const int row = offsets[e] + (int)rank;
+            slot[(size_t)t * k + j] = row;
+            src_token[row] = t;
+        } else {
+            slot[(size_t)t * k + j] = -1;
+        }
+    }
+    if (live) {
+        for (int j = 0; j < k; ++j)
+            if (my[j] < 0)
+                slot[(size_t)t * k + j] = -1;
+    }
+}
+
+// One wavefront per token; the row is read once and written to each kept slot.
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_gather_kernel(const typename ET::storage* __restrict__ x,
+                                                         const int32_t* __restrict__ slot, int T, int d, int k,
+                                                         typename ET::storage* __restrict__ x_perm)
+{
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T)
+        return;
+    constexpr int kPer = 16 / ET::kBytes;           // elements per 16-byte vector
+    const int nvec = d / kPer;                       // 16-byte vectors per row
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * d);
+    for (int v0 = 0; v0 < nvec; v0 += kWave * 8) {
+        uint4 buf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < nvec)
+                buf[u] = src[v];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] < 0)
+                continue;
+            uint4* dst = reinterpret_cast<uint4*>(x_perm + (size_t)rows[j] * d);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int v = v0 + u * kWave + lane;
+                if (v < nvec)
+                    dst[v] = buf[u];
+            }
+        }
+    }
+}
+
+}  // namespace moe
+
+extern "C" hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, const void* x, int T, int d, int E,
+                                         int k, long long C, int32_t* counts, int32_t* offsets, int32_t* slot,
+                                         int32_t* src_token, void* x_perm, int32_t* chunk_cnt,
+                                         hipStream_t stream)
+{
+    using namespace moe;
+    const int nchunks = (T + kChunk - 1) / kChunk;
+    moe_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, chunk_cnt);
+    moe_scan_kernel<<<1, 1024, 0, stream>>>(chunk_cnt, nchunks, E, C, counts, offsets);
+    moe_scatter_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, C, chunk_cnt, offsets, slot, src_token);
+    const dim3 grid((T + 3) / 4);
+    if (dtype == 0)
+        moe_gather_kernel<f32_t><<<grid, 256, 0, stream>>>((const float*)x, slot, T, d, k, (float*)x_perm);
+    else
+        moe_gather_kernel<bf16_t><<<grid, 256, 0, stream>>>((const uint16_t*)x, slot, T, d, k,
+                                                            (uint16_t*)x_perm);
+    return hipGetLastError();
+}

@@ -1,0 +1,265 @@
+// Gate GEMM and wavefront-per-token router (gfx950).
+//
+// Gate: one fully connected layer scores every token against every expert
+// (FastMoE announcement page, "特色二").  Router: optional Skywork gating-logit
+// normalisation (Skywork-MoE news item, "技术创新 1"; Skywork slides, slide 6),
+// softmax over all experts, top-k on the fp32 logit (Megatron-Core page,
+// "关键特性"; FastMoE page, Fig. 4: the top-2 gate takes the two best scores).
+#include "common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- gate GEMM
+// logits[t,e] = (float)( sum_i x[t,i] * Wg[e,i] + bg[e] ) with every product
+// and sum in fp64.  bf16 x bf16 and fp32 x fp32 products are exact in fp64,
+// so the only roundings are the fp64 additions; the result is the correctly
+// rounded fp32 value of a sum accurate to ~1e-16 relative, independent of the
+// tiling.  Routing decisions therefore do not depend on how this kernel (or
+// any other correct gate) orders its sums.
+//
+// Work split: a block of 4 wavefronts takes 16 tokens, each wavefront 4 of
+// them; the 64 lanes split the model dimension in 8-element chunks (lane l
+// takes chunks l, l+64, ...), so the x rows and Wg rows are read with 16-byte
+// coalesced loads.  Experts go in groups of 8.  The 4 x 8 partial sums of a
+// lane are reduced across the wavefront by recursive halving: each exchange
+// halves the values a lane holds, so 32 values need 16+8+4+2+1+1 shuffles.
+constexpr int kGateTokPerWave = 4;
+constexpr int kGateExpGroup = 8;
+constexpr int kGateTokPerBlock = 4 * kGateTokPerWave;
+
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET::storage* __restrict__ x,
+                                                              const typename ET::storage* __restrict__ Wg,
+                                                              const float* __restrict__ bg,
+                                                              float* __restrict__ logits, int T, int d, int E)
+{
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int t0 = blockIdx.x * kGateTokPerBlock + wave * kGateTokPerWave;
+    if (t0 >= T)
+        return;
+    const int nchunk = d / 8;
+    for (int e0 = 0; e0 < E; e0 += kGateExpGroup) {
+        double acc[kGateTokPerWave * kGateExpGroup];
+#pragma unroll
+        for (int v = 0; v < kGateTokPerWave * kGateExpGroup; ++v)
+            acc[v] = 0.0;
+        for (int c = lane; c < nchunk; c += kWave) {
+            double xd[kGateTokPerWave][8];
+#pragma unroll
+            for (int tt = 0; tt < kGateTokPerWave; ++tt) {
+                float xf[8];
+                const int t = min(t0 + tt, T - 1);  // rows past T are computed but not stored
+                load8(x + (size_t)t * d + (size_t)c * 8, xf);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    xd[tt][i] = (double)xf[i];
+            }
+#pragma unroll
+            for (int ee = 0; ee < kGateExpGroup; ++ee) {
+                const int e = min(e0 + ee, E - 1);
+                float wf[8];
+                load8(Wg + (size_t)e * d + (size_t)c * 8, wf);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const double wd = (double)wf[i];
+#pragma unroll
+                    for (int tt = 0; tt < kGateTokPerWave; ++tt)
+                        acc[tt * kGateExpGroup + ee] = fma(xd[tt][i], wd, acc[tt * kGateExpGroup + ee]);
+                }
+            }
+        }
+        // Recursive halving over lane bits 5..1: after the exchange across
+        // bit b a lane keeps the half of its values selected by its own bit b.
+        double* v = acc;
+        int n = kGateTokPerWave * kGateExpGroup;  // 32
+#pragma unroll
+        for (int bit = 5; bit >= 1; --bit) {
+            const int half = n / 2;
+            const bool upper = (lane >> bit) & 1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i < half) {
+                    const double keep = upper ? v[half + i] : v[i];
+                    const double send = upper ? v[i] : v[half + i];
+                    v[i] = keep + __shfl_xor(send, 1 << bit);
+                }
+            }
+            n = half;
+        }
+        double s = v[0] + __shfl_xor(v[0], 1);
+        // lane l now holds value index (l >> 1): token (l >> 4), expert ((l >> 1) & 7)
+        const int t = t0 + (lane >> 4);
+        const int e = e0 + ((lane >> 1) & 7);
+        if ((lane & 1) == 0 && t < T && e < E) {
+            if (bg)
+                s += (double)bg[e];
+            logits[(size_t)t * E + e] = (float)s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- router
+// One wavefront per token.  Expert e lives in lane e % 64, register e / 64.
+//
+// Selection key: the raw fp32 logit mapped to an order-preserving 32-bit
+// integer (-0 folded onto +0), in the high half of a 64-bit key whose low
+// half is (0xffffffff - e); the wavefront-wide maximum is then the largest
+// logit with ties going to the lowest expert index.  k rounds of max-reduce
+// give the k experts in descending order.  The standardise-and-scale
+// normalisation and the softmax are strictly increasing maps for lambda > 0
+// and sigma > 0 (and constant otherwise), so selecting on the logit is the
+// same as selecting on the probability, without depending on how either side
+// rounds exp or the reductions.
+//
+// Probabilities are formed in fp64 (mean, population variance, softmax) and
+// only the k selected ones are stored, rounded to fp32.
+__device__ __forceinline__ uint32_t ordered_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) == 0)
+        u = 0;  // -0 == +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ double wave_max(double v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmax(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t w = __shfl_xor(v, o);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int normalize, float lambda,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w)
+{
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T)
+        return;
+    const float* zt = logits + (size_t)t * E;
+    float z[VPL];
+    uint64_t key[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        z[i] = e < E ? zt[e] : 0.0f;
+        key[i] = e < E ? ((uint64_t)ordered_key(z[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
+    }
+    // scores s (fp64): the logit, or lambda * (z - mu) / sigma
+    double s[VPL];
+    if (normalize) {
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            part += (lane + kWave * i < E) ? (double)z[i] : 0.0;
+        const double mu = wave_sum(part) / E;
+        part = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const double c = (double)z[i] - mu;
+            part += (lane + kWave * i < E) ? c * c : 0.0;
+        }
+        const double sigma = sqrt(wave_sum(part) / E);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            s[i] = sigma == 0.0 ? 0.0 : (double)lambda * ((double)z[i] - mu) / sigma;
+    } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            s[i] = (double)z[i];
+    }
+    double m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (lane + kWave * i < E)
+            m = fmax(m, s[i]);
+    m = wave_max(m);
+    double ex[VPL];
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        ex[i] = (lane + kWave * i < E) ? exp(s[i] - m) : 0.0;
+        part += ex[i];
+    }
+    const double denom = wave_sum(part);
+
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+        const int owner = e % kWave;
+        const int reg = e / kWave;
+        double mine = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            if (i == reg && lane == owner) {
+                mine = ex[i];
+                key[i] = 0;  // taken
+            }
+        }
+        const double pe = __shfl(mine, owner) / denom;
+        if (lane == 0) {
+            topk_idx[(size_t)t * k + j] = e;
+            topk_w[(size_t)t * k + j] = (float)pe;
+        }
+    }
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------- launchers
+extern "C" hipError_t moe_launch_gate(int dtype, const void* x, const void* Wg, const float* bg, float* logits,
+                                      int T, int d, int E, hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid((T + kGateTokPerBlock - 1) / kGateTokPerBlock), block(256);
+    if (dtype == 0)
+        moe_gate_logits_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)x, (const float*)Wg, bg, logits,
+                                                                  T, d, E);
+    else
+        moe_gate_logits_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)x, (const uint16_t*)Wg, bg,
+                                                                   logits, T, d, E);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_router(const float* logits, int T, int E, int k, int normalize, float lambda,
+                                        int32_t* topk_idx, float* topk_w, hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid((T + 3) / 4), block(256);
+    const int vpl = (E + kWave - 1) / kWave;
+    if (vpl <= 1)
+        moe_router_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    else if (vpl <= 2)
+        moe_router_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    else if (vpl <= 4)
+        moe_router_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    else if (vpl <= 8)
+        moe_router_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    else
+        moe_router_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    return hipGetLastError();
+}

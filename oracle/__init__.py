@@ -76,6 +76,7 @@ def _load():
     lib.orc_forward_tokens.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, P, P]
     lib.orc_ffn_rows.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, P]
     lib.orc_combine.argtypes = [I, I, I, I, P, P, P, P]
+    lib.orc_down_rows.argtypes = [I, I, I, I, P, P, P, I, P, P]
     _lib = lib
     return lib
 
@@ -238,6 +239,20 @@ def ffn_rows(x_perm, offsets, W1, W2, act, F, rows=None, want_h=False):
     _load().orc_ffn_rows(E, d, F, int(act), _dtype_code(xp), _ptr(off), _ptr(xp), _ptr(W1), _ptr(W2), n, _ptr(rr),
                          _ptr(out), _ptr(h))
     return (out, h) if want_h else out
+
+
+def down_rows(h, offsets, W2, rows=None):
+    """Second expert layer on given hidden rows h [*, F] (float64 [n, d])."""
+    h = _c(h)
+    W2 = _c(W2)
+    off = _c(offsets, np.int32)
+    E = off.shape[0] - 1
+    d, F = W2.shape[1], W2.shape[2]
+    rr = None if rows is None else _c(rows, np.int32)
+    n = h.shape[0] if rr is None else rr.shape[0]
+    out = np.empty((n, d), np.float64)
+    _load().orc_down_rows(E, d, F, _dtype_code(h), _ptr(off), _ptr(h), _ptr(W2), n, _ptr(rr), _ptr(out))
+    return out
 
 
 def combine(y_perm, slot, topk_w, T):

@@ -345,3 +345,25 @@ void orc_combine(int T, int d, int k, int dtype, const void* yp, const int32_t* 
         }
     }
 }
+
+/* Second expert layer alone on given hidden rows: out[n] = W2[e] h[r] for
+ * r = rows[n] (rows == NULL means 0..nrows-1), e the expert whose segment
+ * [offsets[e], offsets[e+1]) holds r.  h [*, F] dtype, out [nrows, d]. */
+void orc_down_rows(int E, int d, int F, int dtype, const int32_t* offsets, const void* h, const void* W2,
+                   int nrows, const int32_t* rows, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int n = 0; n < nrows; ++n) {
+        int r = rows ? rows[n] : n;
+        int e = 0;
+        while (e < E && !(offsets[e] <= r && r < offsets[e + 1]))
+            ++e;
+        for (int o = 0; o < d; ++o) {
+            double s = 0.0;
+            if (e < E)
+                for (int f = 0; f < F; ++f)
+                    s += elem(dtype, W2, (size_t)e * d * F + (size_t)o * F + f) * elem(dtype, h, (size_t)r * F + f);
+            out[(size_t)n * d + o] = s;
+        }
+    }
+}

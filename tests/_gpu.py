@@ -1,0 +1,88 @@
+"""Helpers of the GPU parity tests: host <-> device marshalling and the
+tolerance metric.  Inputs come from moe_inputs, expected values from the
+oracle; nothing here computes any step of the layer."""
+import numpy as np
+import torch
+
+import mixture_experts_layer_logit_amd as moe
+
+# max-abs-rel error bound on floating outputs: max|gpu - oracle| / max|oracle|
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# absolute bound on the stored gate weights topk_w (fp32 outputs of an fp64 softmax)
+TOPK_W_ATOL = 1e-5
+
+
+def dev(a):
+    """numpy array -> CUDA tensor (uint16 is taken as bf16 bits)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    """CUDA tensor -> numpy (bf16 as uint16 bits)."""
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def to_f64(a):
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def maxrel(got, ref):
+    got = to_f64(np.asarray(got)) if np.asarray(got).dtype in (np.uint16, np.float32) else np.asarray(got)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    scale = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (scale if scale > 0 else 1.0))
+
+
+def torch_dtype(case):
+    return torch.float32 if case.dtype == "f32" else torch.bfloat16
+
+
+def problem_of(case, **over):
+    kw = dict(T=case.T, d=case.d, E=case.E, k=case.k, F=case.F, act=case.act, dtype=case.dtype,
+              normalize=case.normalize, lam=case.lam, cf=case.cf)
+    kw.update(over)
+    return moe.problem(kw["T"], kw["d"], kw["E"], kw["k"], kw["F"], act=kw["act"], dtype=kw["dtype"],
+                       normalize=kw["normalize"], lam=kw["lam"], cf=kw["cf"])
+
+
+def run_forward(case, inp, ws_fill=None):
+    """moe_forward through the C ABI; returns host copies of every output."""
+    p = problem_of(case)
+    T, E, k, d = case.T, case.E, case.k, case.d
+    x = dev(inp["x"])
+    W1 = dev(inp["W1"])
+    W2 = dev(inp["W2"])
+    Wg = dev(inp["Wg"]) if inp.get("Wg") is not None else None
+    bg = dev(inp["bg"]) if inp.get("bg") is not None else None
+    if inp.get("logits") is not None and Wg is None:
+        logits = dev(inp["logits"])
+    else:
+        logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    y = torch.empty(T, d, dtype=torch_dtype(case), device="cuda")
+    info = {
+        "topk_idx": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+        "topk_w": torch.empty(T, k, dtype=torch.float32, device="cuda"),
+        "counts": torch.empty(E, dtype=torch.int32, device="cuda"),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+        "slot": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+        "src_token": torch.full((T * k,), -7, dtype=torch.int32, device="cuda"),
+    }
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
+    moe.moe_forward(p, x, Wg, bg, W1, W2, y, logits=logits, info=info, ws=ws)
+    torch.cuda.synchronize()
+    out = {key: host(v) for key, v in info.items()}
+    out["y"] = host(y)
+    out["logits"] = host(logits)
+    return out

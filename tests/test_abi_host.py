@@ -1,0 +1,119 @@
+"""C-ABI host checks: the library loads, exports every declared entry point,
+sizes workspaces and capacities, and rejects bad arguments before anything is
+enqueued.  No kernel is launched (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_logit_amd as moe
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_entry_points():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load()
+    names = declared_entry_points()
+    assert set(names) >= {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_status_strings():
+    lib = moe.load()
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("T,E,k,cf", [(4096, 16, 2, 1.25), (10, 3, 1, 1.0), (8, 4, 2, 1e-30), (4096, 8, 2, 0.0),
+                                      (4096, 8, 2, -1.0), (16384, 512, 2, 0.25), (1, 1, 1, 3.0)])
+def test_capacity_matches_oracle(T, E, k, cf):
+    p = moe.problem(T, 64, E, k, 64, cf=cf)
+    assert moe.moe_capacity(p) == oracle.capacity(T, E, k, cf)
+
+
+def workspace_formula(T, d, E, k, F, b):
+    r = lambda n: (n + 255) // 256 * 256
+    nch = max((T + 255) // 256, 1)
+    return (r(T * k * 4) * 4 + r(E * 4) + r((E + 1) * 4) + r(nch * E * 4) + r(T * E * 4)
+            + r(T * k * d * b) * 2 + r(T * k * F * b))
+
+
+@pytest.mark.parametrize("T,d,E,k,F,dt", [(256, 64, 4, 2, 128, "f32"), (4096, 4096, 8, 2, 14336, "bf16"),
+                                          (1, 64, 1, 1, 64, "bf16"), (16384, 1024, 512, 2, 512, "bf16")])
+def test_workspace_size(T, d, E, k, F, dt):
+    p = moe.problem(T, d, E, k, F, dtype=dt)
+    assert moe.moe_workspace_size(p) == workspace_formula(T, d, E, k, F, 4 if dt == "f32" else 2)
+
+
+BAD = [
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=1025), moe.MOE_ERR_UNSUPPORTED),
+    (dict(k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=9, E=16), moe.MOE_ERR_UNSUPPORTED),
+    (dict(k=5, E=4), moe.MOE_ERR_INVALID_ARG),
+    (dict(d=96), moe.MOE_ERR_UNSUPPORTED),
+    (dict(F=32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(dtype=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(normalize=True, lam=0.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(normalize=True, lam=float("inf")), moe.MOE_ERR_INVALID_ARG),
+    (dict(cf=float("nan")), moe.MOE_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_bad_problem_rejected(kw, status):
+    args = dict(T=64, d=64, E=8, k=2, F=64)
+    args.update(kw)
+    p = moe.problem(args.pop("T"), args.pop("d"), args.pop("E"), args.pop("k"), args.pop("F"), **args)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(p)
+    assert ei.value.status == status
+    assert moe.load().moe_last_error()
+
+
+FAKE = 1 << 20  # a 16-byte aligned, never dereferenced address
+
+
+def test_bad_pointers_rejected_before_launch():
+    p = moe.problem(64, 64, 8, 2, 64)
+    ws = moe.moe_workspace_size(p)
+    lib = moe.load()
+    pp = ctypes.byref(p)
+    # x given without Wg
+    assert lib.moe_route(pp, FAKE, None, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # missing logits
+    assert lib.moe_route(pp, None, None, None, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # misaligned x
+    assert lib.moe_route(pp, FAKE + 2, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"aligned" in lib.moe_last_error()
+    # workspace too small
+    assert lib.moe_permute(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_grouped_ffn(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == moe.MOE_ERR_WORKSPACE
+    # forward without Wg and without logits
+    assert lib.moe_forward(pp, FAKE, None, None, FAKE, FAKE, FAKE, None, None, FAKE, ws, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # null outputs
+    assert lib.moe_combine(pp, FAKE, FAKE, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_up(pp, FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(pp, FAKE, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op():
+    p = moe.problem(0, 64, 8, 2, 64)
+    lib = moe.load()
+    pp = ctypes.byref(p)
+    # T == 0: nothing to do, no pointer is touched
+    assert lib.moe_forward(pp, None, None, None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
+    assert lib.moe_route(pp, None, None, None, None, None, None, None) == moe.MOE_OK

@@ -399,3 +399,28 @@ def test_zipf_bias_realises_target_shares(name):
     f = np.bincount(idx.ravel(), minlength=case.E) / (case.T * case.k)
     q = moe_inputs.zipf_shares(case.E, case.zipf_s)
     assert np.max(np.abs(f - q)) < 0.005, (f, q)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_down_rows_is_second_linear_layer(dtype):
+    E, d, F = 4, 64, 128
+    offsets = np.array([0, 5, 5, 12, 20], np.int32)   # expert 1 empty
+    h = RNG.standard_normal((20, F)).astype(np.float32)
+    W2 = (RNG.standard_normal((E, d, F)) * 0.1).astype(np.float32)
+    if dtype == "bf16":
+        h, W2 = moe_inputs.f32_to_bf16_bits(h), moe_inputs.f32_to_bf16_bits(W2)
+    out = oracle.down_rows(h, offsets, W2)
+    h64, W64 = oracle.to_f64(h), oracle.to_f64(W2)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        ref = h64[a:b] @ W64[e].T
+        assert np.max(np.abs(out[a:b] - ref), initial=0.0) <= 1e-12 * max(1.0, np.max(np.abs(ref), initial=0.0))
+    # consistent with the whole FFN: down(h of ffn_rows) == ffn_rows
+    xp = moe_inputs.f32_to_bf16_bits(RNG.standard_normal((20, d)).astype(np.float32))
+    W1 = moe_inputs.f32_to_bf16_bits((RNG.standard_normal((E, F, d)) * 0.1).astype(np.float32))
+    W2b = moe_inputs.f32_to_bf16_bits(W2) if dtype == "f32" else W2
+    full, hh = oracle.ffn_rows(xp, offsets, W1, W2b, oracle.RELU, F, want_h=True)
+    assert hh.shape == (20, F)
+    ref = np.stack([hh[r] @ oracle.to_f64(W2b)[int(np.searchsorted(offsets, r, side="right") - 1)].T
+                    for r in range(20)])
+    assert np.max(np.abs(full - ref)) <= 1e-12 * np.max(np.abs(ref))
