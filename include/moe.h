@@ -151,7 +151,9 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_idx, const void
  *   ReLU:   h[r,f] = max(u_f, 0)
  *   SwiGLU: h[r,f] = silu(u_f) * u_{F+f},  silu(g) = g / (1 + exp(-g))
  * fp32 accumulation, h stored in dtype.  offsets is read on the device (no
- * host synchronisation); offsets[E] <= T*k is required. */
+ * host synchronisation) and must be non-decreasing with offsets[E] <= T*k;
+ * x_perm and h hold T*k rows.  Offsets outside [0, T*k] or decreasing are
+ * clamped into range (unspecified results, never an out-of-bounds access). */
 moe_status moe_expert_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1,
                          void* h, void* stream);
 
@@ -166,7 +168,8 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const int32
 /* Weighted combine (industry overview page, "MoE的內涵": the gate weights the
  * experts' mix): y[t] = sum over j = 0..k-1 with slot[t,j] >= 0, in that
  * order, of topk_w[t,j] * y_perm[slot[t,j]] (fp32 accumulation, stored in
- * dtype).  A token with every choice dropped gets y[t] = 0. */
+ * dtype).  A token with every choice dropped gets y[t] = 0.  y_perm holds
+ * T*k rows; a slot >= T*k counts as dropped. */
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w,
                        void* y, void* stream);
 

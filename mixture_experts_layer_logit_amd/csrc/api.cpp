@@ -22,9 +22,9 @@ hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, const void* x,
                               void* x_perm, int32_t* chunk_cnt, hipStream_t stream);
 hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const void* W, void* C,
                                    const int32_t* offsets, int E, int K, int Nw, int Nout, int F, int max_rows,
-                                   int ncu, hipStream_t stream);
+                                   int mean_rows, int ncu, hipStream_t stream);
 hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w, int T, int d,
-                              int k, void* y, hipStream_t stream);
+                              int k, int max_rows, void* y, hipStream_t stream);
 }
 
 namespace {
@@ -93,6 +93,10 @@ moe_status check_problem(const moe_problem* p)
     const long long rows = (long long)p->T * p->k;
     if (rows * (long long)std::max(n1_of(p), p->d) >= (1LL << 40))
         return fail(MOE_ERR_UNSUPPORTED, "problem too large");
+    // one expert's weight matrix is addressed with 32-bit byte offsets
+    if ((long long)n1_of(p) * p->d * (long long)elem_bytes(p) >= (1LL << 31) ||
+        (long long)p->d * p->F * (long long)elem_bytes(p) >= (1LL << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "one expert's weights must stay below 2 GiB");
     return MOE_OK;
 }
 
@@ -204,12 +208,22 @@ moe_status do_permute(const moe_problem* p, const int32_t* topk_idx, const void*
                       "permute launch");
 }
 
+// Expected rows per expert: T*k/E, or the capacity when that is smaller.
+int mean_rows_of(const moe_problem* p)
+{
+    long long m = (long long)p->T * p->k / p->E;
+    const long long C = capacity_of(p);
+    if (C >= 0 && C < m)
+        m = C;
+    return (int)std::min<long long>(m, INT32_MAX);
+}
+
 moe_status do_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1, void* h,
                  hipStream_t s)
 {
     const int epi = p->act == MOE_ACT_SWIGLU ? 2 : 1;
     return hip_status(moe_launch_grouped_gemm(p->dtype, epi, x_perm, W1, h, offsets, p->E, p->d, n1_of(p), p->F, p->F,
-                                              p->T * p->k, cu_count(), s),
+                                              p->T * p->k, mean_rows_of(p), cu_count(), s),
                       "expert up launch");
 }
 
@@ -217,14 +231,14 @@ moe_status do_down(const moe_problem* p, const void* h, const int32_t* offsets, 
                    hipStream_t s)
 {
     return hip_status(moe_launch_grouped_gemm(p->dtype, 0, h, W2, y_perm, offsets, p->E, p->F, p->d, p->d, p->F,
-                                              p->T * p->k, cu_count(), s),
+                                              p->T * p->k, mean_rows_of(p), cu_count(), s),
                       "expert down launch");
 }
 
 moe_status do_combine(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w, void* y,
                       hipStream_t s)
 {
-    return hip_status(moe_launch_combine(p->dtype, y_perm, slot, topk_w, p->T, p->d, p->k, y, s), "combine launch");
+    return hip_status(moe_launch_combine(p->dtype, y_perm, slot, topk_w, p->T, p->d, p->k, p->T * p->k, y, s), "combine launch");
 }
 
 }  // namespace

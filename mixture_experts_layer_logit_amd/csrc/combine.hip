@@ -8,6 +8,7 @@
 // reads the row y_perm[slot] with 16-byte loads and accumulates
 // topk_w[t,j] * row in fp32 (fma, fixed order, so results are reproducible),
 // then writes y[t] once.  Each lane owns up to 8 16-byte vectors per pass.
+// Slots at or past the row count (T*k) are treated as dropped.
 #include "common.h"
 
 namespace moe {
@@ -16,7 +17,7 @@ template <typename ET>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::storage* __restrict__ y_perm,
                                                           const int32_t* __restrict__ slot,
                                                           const float* __restrict__ topk_w, int T, int d, int k,
-                                                          typename ET::storage* __restrict__ y)
+                                                          int max_rows, typename ET::storage* __restrict__ y)
 {
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -29,6 +30,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::sto
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
+        if (rows[j] >= max_rows)
+            rows[j] = -1;  // out-of-range slots count as dropped
         w[j] = (j < k) ? topk_w[(size_t)t * k + j] : 0.0f;
     }
     for (int v0 = 0; v0 < nvec; v0 += kWave * 8) {
@@ -89,14 +92,15 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::sto
 }  // namespace moe
 
 extern "C" hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w,
-                                         int T, int d, int k, void* y, hipStream_t stream)
+                                         int T, int d, int k, int max_rows, void* y, hipStream_t stream)
 {
     using namespace moe;
     const dim3 grid((T + 3) / 4), block(256);
     if (dtype == 0)
-        moe_combine_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)y_perm, slot, topk_w, T, d, k, (float*)y);
+        moe_combine_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)y_perm, slot, topk_w, T, d, k, max_rows,
+                                                              (float*)y);
     else
         moe_combine_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)y_perm, slot, topk_w, T, d, k,
-                                                               (uint16_t*)y);
+                                                               max_rows, (uint16_t*)y);
     return hipGetLastError();
 }
