@@ -169,7 +169,6 @@ def main():
         offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
         slot = torch.empty(T, k, dtype=torch.int32, device="cuda")
         src = torch.empty(T * k, dtype=torch.int32, device="cuda")
-        x_perm = torch.empty(T * k, d, dtype=dt, device="cuda")
         h = torch.empty(T * k, F, dtype=dt, device="cuda")
         y_perm = torch.empty(T * k, d, dtype=dt, device="cuda")
         y = torch.empty(T, d, dtype=dt, device="cuda")
@@ -183,13 +182,14 @@ def main():
         moe.moe_route(p, x if Wg is not None else None, Wg, bg, logits, idx, w, stream=s)
         if ev is not None:
             ev[1].record(stream)
-        moe.moe_permute(p, idx, x, counts, offsets, slot, src, x_perm, ws, stream=s)
+        # no x_perm copy: the up projection gathers the rows of x through src
+        moe.moe_permute(p, idx, None, counts, offsets, slot, src, None, ws, stream=s)
         if ev is not None:
             ev[2].record(stream)
-        moe.moe_expert_up(p, x_perm, offsets, W1, h, stream=s)
+        moe.moe_expert_up(p, x, src, offsets, W1, h, ws=ws, stream=s)
         if ev is not None:
             ev[3].record(stream)
-        moe.moe_expert_down(p, h, offsets, W2, y_perm, stream=s)
+        moe.moe_expert_down(p, h, offsets, W2, y_perm, ws=ws, stream=s)
         if ev is not None:
             ev[4].record(stream)
         moe.moe_combine(p, y_perm, slot, w, y, stream=s)
@@ -221,7 +221,6 @@ def main():
     up_tflops = up_flops / (stage_ms["expert_up"] * 1e-3) / 1e12
     ffn_tflops = (up_flops + down_flops) / ((stage_ms["expert_up"] + stage_ms["expert_down"]) * 1e-3) / 1e12
     row_bytes = d * (4 if case.dtype == "f32" else 2)
-    permute_gbps = (T + P) * row_bytes / (stage_ms["permute"] * 1e-3) / 1e9
     combine_gbps = (T + P) * row_bytes / (stage_ms["combine"] * 1e-3) / 1e9
 
     result = {
@@ -248,7 +247,6 @@ def main():
         "tflops": (up_flops + down_flops + gate_flops) / (ms_per_step * 1e-3) / 1e12,
         "grouped_gemm_pct_of_bf16_peak": 100.0 * ffn_tflops / peak,
         "stage_ms": stage_ms,
-        "permute_hbm_frac": permute_gbps / HBM_GBPS,
         "combine_hbm_frac": combine_gbps / HBM_GBPS,
         "kept_rows": P,
         "dropped_assignments": dropped,

@@ -111,8 +111,8 @@ const char* moe_last_error(void);
 moe_status moe_capacity(const moe_problem* p, int32_t* C);
 
 /* Bytes of workspace that suffice for every entry point of this problem
- * (moe_forward needs the most: routing, permutation, x_perm, h, y_perm).
- * Host only. */
+ * (moe_forward needs the most: routing, permutation, h, y_perm and the
+ * partial tiles of the grouped GEMM's K-split last round).  Host only. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
 /* Gate and routing (FastMoE page, "特色二": one fully connected layer as
@@ -139,7 +139,9 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* Wg, const 
  *   slot[t,j] = that row (else -1), src_token[row] = t, x_perm[row] = x[t].
  * topk_idx entries must lie in [0,E) and be distinct within a token (entries
  * outside [0,E) are skipped; duplicates give unspecified rows, never writes
- * out of bounds).  Needs ws_bytes >= moe_workspace_size. */
+ * out of bounds).  x_perm == NULL (then x may be NULL too) skips the row
+ * copy, for callers that read x through src_token (moe_expert_up does).
+ * Needs ws_bytes >= moe_workspace_size. */
 moe_status moe_permute(const moe_problem* p, const int32_t* topk_idx, const void* x, int32_t* counts,
                        int32_t* offsets, int32_t* slot, int32_t* src_token, void* x_perm, void* ws,
                        size_t ws_bytes, void* stream);
@@ -147,19 +149,27 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_idx, const void
 /* First expert layer over the expert segments (FastMoE page, "特色三": ReLU
  * two-layer MLP experts, many experts on one GPU; Megatron-Core page,
  * "关键特性": GroupedGEMM): for every expert e and row r in
- * [offsets[e], offsets[e+1]):  u = W1[e] x_perm[r];
+ * [offsets[e], offsets[e+1]):  u = W1[e] a_r, where a_r = a[r] when
+ * src_token is NULL (a = x_perm, T*k rows) and a_r = a[src_token[r]] when it
+ * is given (a = x, T rows: the permuted rows are gathered on the fly; x
+ * must then be below 0xF0000000 bytes, else MOE_ERR_UNSUPPORTED);
  *   ReLU:   h[r,f] = max(u_f, 0)
  *   SwiGLU: h[r,f] = silu(u_f) * u_{F+f},  silu(g) = g / (1 + exp(-g))
  * fp32 accumulation, h stored in dtype.  offsets is read on the device (no
  * host synchronisation) and must be non-decreasing with offsets[E] <= T*k;
- * x_perm and h hold T*k rows.  Offsets outside [0, T*k] or decreasing are
- * clamped into range (unspecified results, never an out-of-bounds access). */
-moe_status moe_expert_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1,
-                         void* h, void* stream);
+ * h holds T*k rows.  Offsets outside [0, T*k] or decreasing are
+ * clamped into range (unspecified results, never an out-of-bounds access).
+ * ws (nullable; if given, ws_bytes >= moe_workspace_size) lets the last,
+ * partly filled round of output tiles be split along K, with the parts
+ * summed in a fixed order: results stay deterministic, but may differ from
+ * the unsplit ones in the last bits (another fp32 summation order). */
+moe_status moe_expert_up(const moe_problem* p, const void* a, const int32_t* src_token, const int32_t* offsets,
+                         const void* W1, void* h, void* ws, size_t ws_bytes, void* stream);
 
-/* Second expert layer: y_perm[r] = W2[e] h[r] for r in expert e's segment. */
+/* Second expert layer: y_perm[r] = W2[e] h[r] for r in expert e's segment
+ * (same offsets and workspace rules as moe_expert_up). */
 moe_status moe_expert_down(const moe_problem* p, const void* h, const int32_t* offsets, const void* W2,
-                           void* y_perm, void* stream);
+                           void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_expert_up then moe_expert_down, with h in the workspace. */
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1,

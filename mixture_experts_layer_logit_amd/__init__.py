@@ -64,8 +64,8 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_route.argtypes = [PP, P, P, P, P, P, P, P]
     lib.moe_permute.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-    lib.moe_expert_up.argtypes = [PP, P, P, P, P, P]
-    lib.moe_expert_down.argtypes = [PP, P, P, P, P, P]
+    lib.moe_expert_up.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_expert_down.argtypes = [PP, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_grouped_ffn.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_combine.argtypes = [PP, P, P, P, P, P]
     lib.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), P, ctypes.c_size_t, P]
@@ -144,13 +144,15 @@ def moe_permute(p, topk_idx, x, counts, offsets, slot, src_token, x_perm, ws, st
                               _ptr(src_token), _ptr(x_perm), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_expert_up(p, x_perm, offsets, W1, h, stream=None):
-    _check(load().moe_expert_up(ctypes.byref(p), _ptr(x_perm), _ptr(offsets), _ptr(W1), _ptr(h), _stream(stream)))
+def moe_expert_up(p, a, src_token, offsets, W1, h, ws=None, stream=None):
+    """a is x_perm (src_token None) or x (rows gathered through src_token)."""
+    _check(load().moe_expert_up(ctypes.byref(p), _ptr(a), _ptr(src_token), _ptr(offsets), _ptr(W1), _ptr(h),
+                                _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_expert_down(p, h, offsets, W2, y_perm, stream=None):
-    _check(load().moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(offsets), _ptr(W2), _ptr(y_perm),
-                                  _stream(stream)))
+def moe_expert_down(p, h, offsets, W2, y_perm, ws=None, stream=None):
+    _check(load().moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(offsets), _ptr(W2), _ptr(y_perm), _ptr(ws),
+                                  _nbytes(ws), _stream(stream)))
 
 
 def moe_grouped_ffn(p, x_perm, offsets, W1, W2, y_perm, ws, stream=None):

@@ -20,9 +20,10 @@ hipError_t moe_launch_router(const float* logits, int T, int E, int k, int norma
 hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, const void* x, int T, int d, int E, int k,
                               long long C, int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src_token,
                               void* x_perm, int32_t* chunk_cnt, hipStream_t stream);
-hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const void* W, void* C,
-                                   const int32_t* offsets, int E, int K, int Nw, int Nout, int F, int max_rows,
-                                   int mean_rows, int ncu, hipStream_t stream);
+hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const int32_t* gather, int gather_rows,
+                                   const void* W, void* C, const int32_t* offsets, int E, int K, int Nw, int Nout,
+                                   int F, int max_rows, int mean_rows, int ncu, float* partial, hipStream_t stream);
+size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows);
 hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w, int T, int d,
                               int k, int max_rows, void* y, hipStream_t stream);
 }
@@ -35,6 +36,9 @@ constexpr int kMaxK = 8;
 constexpr int kMaxT = 1 << 24;
 constexpr int kMaxDim = 65536;
 constexpr size_t kAlign = 256;
+// The fused row gather of the up projection addresses x with 32-bit byte
+// offsets, and offsets from 0xF0000000 up are its out-of-range marker.
+constexpr unsigned long long kGatherBytes = 0xF0000000ull;
 
 thread_local char g_err[512] = "";
 
@@ -116,10 +120,19 @@ moe_status check_ptr(const void* ptr, const char* name, size_t align)
             return _s;                  \
     } while (0)
 
-// Workspace layout of a problem: every piece 256-byte aligned.
+// Whether x is small enough to be read through src_token by the up projection.
+bool gather_ok(const moe_problem* p)
+{
+    return (unsigned long long)p->T * p->d * elem_bytes(p) < kGatherBytes;
+}
+
+// Workspace layout of a problem: every piece 256-byte aligned.  x_perm is
+// only there (non-zero size) when x is too large to gather from directly.
 struct Layout {
-    size_t topk_idx, topk_w, counts, offsets, slot, src_token, chunk_cnt, logits, x_perm, h, y_perm, total;
+    size_t topk_idx, topk_w, counts, offsets, slot, src_token, chunk_cnt, logits, partial, h, y_perm, x_perm, total;
 };
+
+int mean_rows_of(const moe_problem* p);
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -143,9 +156,10 @@ Layout layout_of(const moe_problem* p)
     L.src_token = take(T * k * 4);
     L.chunk_cnt = take(std::max<size_t>(nchunks, 1) * E * 4);
     L.logits = take(T * E * 4);
-    L.x_perm = take(T * k * d * b);
+    L.partial = take(moe_grouped_gemm_partial_bytes(p->dtype, mean_rows_of(p)));
     L.h = take(T * k * F * b);
     L.y_perm = take(T * k * d * b);
+    L.x_perm = take(gather_ok(p) ? 0 : T * k * d * b);
     L.total = off;
     return L;
 }
@@ -200,7 +214,8 @@ moe_status do_route(const moe_problem* p, const void* x, const void* Wg, const f
 }
 
 moe_status do_permute(const moe_problem* p, const int32_t* topk_idx, const void* x, int32_t* counts,
-                      int32_t* offsets, int32_t* slot, int32_t* src_token, void* x_perm, void* ws, hipStream_t s)
+                      int32_t* offsets, int32_t* slot, int32_t* src_token, void* x_perm /* nullable */, void* ws,
+                      hipStream_t s)
 {
     const Layout L = layout_of(p);
     return hip_status(moe_launch_permute(p->dtype, topk_idx, x, p->T, p->d, p->E, p->k, capacity_of(p), counts,
@@ -218,20 +233,22 @@ int mean_rows_of(const moe_problem* p)
     return (int)std::min<long long>(m, INT32_MAX);
 }
 
-moe_status do_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1, void* h,
-                 hipStream_t s)
+// partial: the tail-split workspace (nullable: no split).  gather
+// (nullable): A is x itself and permuted row r reads row gather[r] of x.
+moe_status do_up(const moe_problem* p, const void* A, const int32_t* gather, const int32_t* offsets, const void* W1,
+                 void* h, float* partial, hipStream_t s)
 {
     const int epi = p->act == MOE_ACT_SWIGLU ? 2 : 1;
-    return hip_status(moe_launch_grouped_gemm(p->dtype, epi, x_perm, W1, h, offsets, p->E, p->d, n1_of(p), p->F, p->F,
-                                              p->T * p->k, mean_rows_of(p), cu_count(), s),
+    return hip_status(moe_launch_grouped_gemm(p->dtype, epi, A, gather, p->T, W1, h, offsets, p->E, p->d, n1_of(p),
+                                              p->F, p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, s),
                       "expert up launch");
 }
 
 moe_status do_down(const moe_problem* p, const void* h, const int32_t* offsets, const void* W2, void* y_perm,
-                   hipStream_t s)
+                   float* partial, hipStream_t s)
 {
-    return hip_status(moe_launch_grouped_gemm(p->dtype, 0, h, W2, y_perm, offsets, p->E, p->F, p->d, p->d, p->F,
-                                              p->T * p->k, mean_rows_of(p), cu_count(), s),
+    return hip_status(moe_launch_grouped_gemm(p->dtype, 0, h, nullptr, 0, W2, y_perm, offsets, p->E, p->F, p->d,
+                                              p->d, p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, s),
                       "expert down launch");
 }
 
@@ -307,33 +324,44 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_idx, const void
     if (p->T == 0)
         return ok();
     CHECK(check_ptr(topk_idx, "topk_idx", 4));
-    CHECK(check_ptr(x, "x", 16));
+    if (x_perm) {
+        CHECK(check_ptr(x, "x", 16));
+        CHECK(check_ptr(x_perm, "x_perm", 16));
+    }
     CHECK(check_ptr(counts, "counts", 4));
     CHECK(check_ptr(offsets, "offsets", 4));
     CHECK(check_ptr(slot, "slot", 4));
     CHECK(check_ptr(src_token, "src_token", 4));
-    CHECK(check_ptr(x_perm, "x_perm", 16));
     CHECK(check_ws(p, ws, ws_bytes));
     CHECK(do_permute(p, topk_idx, x, counts, offsets, slot, src_token, x_perm, ws, (hipStream_t)stream));
     return ok();
 }
 
-moe_status moe_expert_up(const moe_problem* p, const void* x_perm, const int32_t* offsets, const void* W1, void* h,
-                         void* stream)
+moe_status moe_expert_up(const moe_problem* p, const void* a, const int32_t* src_token, const int32_t* offsets,
+                         const void* W1, void* h, void* ws, size_t ws_bytes, void* stream)
 {
     CHECK(check_problem(p));
     if (p->T == 0)
         return ok();
-    CHECK(check_ptr(x_perm, "x_perm", 16));
+    CHECK(check_ptr(a, src_token ? "x" : "x_perm", 16));
+    if (src_token) {
+        CHECK(check_ptr(src_token, "src_token", 4));
+        if (!gather_ok(p))
+            return fail(MOE_ERR_UNSUPPORTED, "x of %llu bytes is too large to gather; pass x_perm",
+                        (unsigned long long)p->T * p->d * elem_bytes(p));
+    }
     CHECK(check_ptr(offsets, "offsets", 4));
     CHECK(check_ptr(W1, "W1", 16));
     CHECK(check_ptr(h, "h", 16));
-    CHECK(do_up(p, x_perm, offsets, W1, h, (hipStream_t)stream));
+    if (ws)
+        CHECK(check_ws(p, ws, ws_bytes));
+    float* partial = ws ? at<float>(ws, layout_of(p).partial) : nullptr;
+    CHECK(do_up(p, a, src_token, offsets, W1, h, partial, (hipStream_t)stream));
     return ok();
 }
 
 moe_status moe_expert_down(const moe_problem* p, const void* h, const int32_t* offsets, const void* W2,
-                           void* y_perm, void* stream)
+                           void* y_perm, void* ws, size_t ws_bytes, void* stream)
 {
     CHECK(check_problem(p));
     if (p->T == 0)
@@ -342,7 +370,10 @@ moe_status moe_expert_down(const moe_problem* p, const void* h, const int32_t* o
     CHECK(check_ptr(offsets, "offsets", 4));
     CHECK(check_ptr(W2, "W2", 16));
     CHECK(check_ptr(y_perm, "y_perm", 16));
-    CHECK(do_down(p, h, offsets, W2, y_perm, (hipStream_t)stream));
+    if (ws)
+        CHECK(check_ws(p, ws, ws_bytes));
+    float* partial = ws ? at<float>(ws, layout_of(p).partial) : nullptr;
+    CHECK(do_down(p, h, offsets, W2, y_perm, partial, (hipStream_t)stream));
     return ok();
 }
 
@@ -360,8 +391,9 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const int32
     CHECK(check_ws(p, ws, ws_bytes));
     const Layout L = layout_of(p);
     void* h = at<char>(ws, L.h);
-    CHECK(do_up(p, x_perm, offsets, W1, h, (hipStream_t)stream));
-    CHECK(do_down(p, h, offsets, W2, y_perm, (hipStream_t)stream));
+    float* partial = at<float>(ws, L.partial);
+    CHECK(do_up(p, x_perm, nullptr, offsets, W1, h, partial, (hipStream_t)stream));
+    CHECK(do_down(p, h, offsets, W2, y_perm, partial, (hipStream_t)stream));
     return ok();
 }
 
@@ -418,14 +450,22 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, cons
     for (const void* q : ptrs)
         CHECK(check_ptr(q, "route info field", 4));
     float* z = logits ? logits : at<float>(ws, L.logits);
-    void* x_perm = at<char>(ws, L.x_perm);
+    float* partial = at<float>(ws, L.partial);
     void* h = at<char>(ws, L.h);
     void* y_perm = at<char>(ws, L.y_perm);
     hipStream_t s = (hipStream_t)stream;
     CHECK(do_route(p, Wg ? x : nullptr, Wg, bg, z, topk_idx, topk_w, s));
-    CHECK(do_permute(p, topk_idx, x, counts, offsets, slot, src_token, x_perm, ws, s));
-    CHECK(do_up(p, x_perm, offsets, W1, h, s));
-    CHECK(do_down(p, h, offsets, W2, y_perm, s));
+    // the up projection reads the token rows of x through src_token, so the
+    // permutation writes no x_perm copy (unless x is beyond 32-bit offsets)
+    if (gather_ok(p)) {
+        CHECK(do_permute(p, topk_idx, x, counts, offsets, slot, src_token, nullptr, ws, s));
+        CHECK(do_up(p, x, src_token, offsets, W1, h, partial, s));
+    } else {
+        void* x_perm = at<char>(ws, L.x_perm);
+        CHECK(do_permute(p, topk_idx, x, counts, offsets, slot, src_token, x_perm, ws, s));
+        CHECK(do_up(p, x_perm, nullptr, offsets, W1, h, partial, s));
+    }
+    CHECK(do_down(p, h, offsets, W2, y_perm, partial, s));
     CHECK(do_combine(p, y_perm, slot, topk_w, y, s));
     return ok();
 }

@@ -12,22 +12,28 @@
 // for every expert e and row r in [offsets[e], offsets[e+1]).  Both operands
 // have K contiguous ("X W^T"), fp32 accumulation, output stored in the input
 // type.  SwiGLU: C[r, f] = silu(u_f) * u_{F+f}, silu(g) = g / (1 + exp(-g)).
+// With a gather index, A row r is read from row gather[r] of A (the up
+// projection reads the token rows of x directly, so the permuted copy x_perm
+// need not be written and read back).
 //
 // Design (gfx950):
-//  * Persistent grid, one block per CU slot.  Each block walks a flattened
-//    list of tiles; the per-expert tile counts come from the device offsets
-//    (no host round trip), scanned in LDS at kernel start.  Tile order is
-//    (expert, n-tile, m-tile) with m fastest, so the tiles sharing a weight
-//    panel are consecutive; each round of the persistent loop hands every XCD
-//    a contiguous range of that order (blocks are dealt to the 8 XCDs
-//    round-robin), so panel re-reads hit that XCD's L2.
+//  * Persistent grid, one block per resident slot.  The per-expert tile
+//    counts come from the device offsets (no host round trip), scanned in
+//    LDS at kernel start.  Tile order is (expert, group of GM m-tiles,
+//    n-tile, m-tile); each round of the persistent loop hands every XCD a
+//    contiguous run of that order (blocks are dealt to the 8 XCDs
+//    round-robin), so the XCD's concurrent tiles share GM activation tiles
+//    and a run of weight panels in its L2.
+//  * Tail split: the tiles left after the last full round of the grid are
+//    split along K into up to 4 parts that fill that round; their fp32
+//    partial tiles go to a workspace and a second kernel adds the parts in a
+//    fixed order and applies the epilogue (deterministic, no atomics).
 //  * Block tile BM x BN, K in 128-byte slices (64 bf16 / 32 fp32), loaded
 //    straight from memory into LDS (buffer_load ... lds: no staging
-//    registers), double-buffered with one barrier per slice.  Each wave load
+//    registers), double-buffered, one barrier per slice.  Each wave load
 //    fills a contiguous 1 KB LDS block (8 rows); the 16-byte chunks of an LDS
-//    row are XOR-swizzled by (row & 7) -- applied on the source side, by
-//    choosing which chunk each lane fetches -- so the MFMA operand reads
-//    (32 rows, same chunk) hit distinct banks.
+//    row are XOR-swizzled (see swz) by choosing which chunk each lane fetches,
+//    so the MFMA operand reads hit every LDS bank once.
 //  * Buffer resources give 32-bit offsets from scalar bases: one over the
 //    tile's activation rows, whose end is the segment end (rows past it read
 //    zero), one over the expert's weight matrix.
@@ -45,25 +51,24 @@ namespace moe {
 enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
 
 constexpr int kGemmMaxE = 1024;
-#ifndef MOE_XCD_REMAP
-#define MOE_XCD_REMAP 1
-#endif
+constexpr int kMaxSplit = 4;         // K parts of a tail tile
+constexpr int kSplitSlots = 256;     // partial tiles the workspace holds
+constexpr int kMinSplitSlices = 8;   // split only tiles with at least this many K slices
 
 // Tile geometry.  BM x BN output tile per block, WM x WN waves; each K slice
-// is RB bytes of every tile row (64 or 128), staged through S LDS buffers;
-// OCC = blocks per CU the kernel is built for; GM = m-tiles grouped together
-// in the tile order.
+// is RB bytes of every tile row, staged through S LDS buffers; OCC = blocks
+// per CU the kernel is built for; GM = m-tiles grouped together in the tile
+// order.
 template <typename ET, int BM_, int BN_, int WM_, int WN_, int RB_, int S_, int OCC_, int GM_>
 struct GemmShape {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RB = RB_, S = S_, OCC = OCC_, GM = GM_;
     static constexpr int kThreads = WM * WN * kWave;
     static constexpr int kWaves = WM * WN;
-    static constexpr int kBK = RB / ET::kBytes;          // K elements per slice
-    static constexpr int kPer = 16 / ET::kBytes;         // elements per 16-byte chunk
-    static constexpr int kNch = RB / 16;                 // 16-byte chunks per row
-    static constexpr int kRowsPerBlk = 1024 / RB;        // rows per 1 KB DMA block
-    static constexpr int kSwzShift = (RB == 128) ? 1 : 2; // log2(256 / RB): rows per 256-byte bank cycle
-    static constexpr int kKSteps = RB / 32;              // MFMA k-steps per slice
+    static constexpr int kBK = RB / ET::kBytes;           // K elements per slice
+    static constexpr int kNch = RB / 16;                  // 16-byte chunks per row
+    static constexpr int kRowsPerBlk = 1024 / RB;         // rows per 1 KB DMA block
+    static constexpr int kSwzShift = (RB == 128) ? 1 : 2;  // log2(256 / RB)
+    static constexpr int kKSteps = RB / 32;               // MFMA k-steps per slice
     static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
     static constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
     static constexpr int kLdsA = BM * RB, kLdsB = BN * RB;
@@ -71,12 +76,14 @@ struct GemmShape {
     static constexpr int kBlkA = BM / kRowsPerBlk / kWaves;  // DMA blocks per wave per slice
     static constexpr int kBlkB = BN / kRowsPerBlk / kWaves;
     static constexpr int kLoads = kBlkA + kBlkB;
+    static constexpr int kTileFloats = BM * BN;          // one partial tile
     static_assert(RB == 64 || RB == 128, "slice rows are 64 or 128 bytes");
     static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(BM % (kRowsPerBlk * kWaves) == 0 && BN % (kRowsPerBlk * kWaves) == 0,
                   "DMA blocks must split evenly across waves");
     static_assert(S >= 2 && S <= 4, "2 to 4 stages");
     static_assert((S - 2) * kLoads <= 63, "vmcnt range");
+    static_assert(kWaves % 2 == 0, "block parity must be fixed per wave");
 };
 
 // LDS byte offset of 16-byte chunk `c` of tile row `row` for RB-byte rows.
@@ -150,6 +157,53 @@ __device__ void tile_prefix(const int32_t* __restrict__ offsets, int E, int max_
     __syncthreads();
 }
 
+// One output tile: expert, first row and row count, first output column.
+struct TileDec {
+    int e, row0, rows, n0;
+};
+
+template <typename S>
+__device__ __forceinline__ TileDec decode_tile(int tile, const int32_t* s_pref, const int32_t* __restrict__ offsets,
+                                               int E, int max_rows, int ntn, int tile_cols)
+{
+    int lo = 0, hi = E;  // largest e with s_pref[e] <= tile
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= tile)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    TileDec t;
+    t.e = lo;
+    int seg0, seg_rows;
+    seg_bounds(offsets, t.e, max_rows, seg0, seg_rows);
+    const int mt_e = (seg_rows + S::BM - 1) / S::BM;
+    // (m-group, n-tile, m-tile within group) order inside the expert
+    const int local = tile - s_pref[t.e];
+    const int g = local / (S::GM * ntn);
+    const int within = local - g * S::GM * ntn;
+    const int gs = min(S::GM, mt_e - g * S::GM);
+    const int nt = within / gs;
+    const int mt = g * S::GM + within % gs;
+    t.row0 = seg0 + mt * S::BM;
+    t.rows = min(S::BM, seg_rows - mt * S::BM);
+    t.n0 = nt * tile_cols;
+    return t;
+}
+
+// K parts of each tail tile: the tiles after the last full round of G blocks
+// are split so that the last round is filled (at most kSplitSlots partials,
+// each part at least kMinSplitSlices / 2 slices long).
+__device__ __forceinline__ int split_parts(int total, int G, int nk, bool enabled)
+{
+    const int tail = total % G;
+    if (!enabled || tail == 0 || nk < kMinSplitSlices)
+        return 1;
+    const int slots = min(G, kSplitSlots);
+    return max(1, min(min(kMaxSplit, slots / tail), nk / (kMinSplitSlices / 2)));
+}
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -169,7 +223,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes)
 // lds + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base).
 // Issued from asm so that the compiler does not track the LDS writes: they
 // are ordered by the kernel's own vmcnt waits and barriers (the compiler
-// would otherwise make every LDS read wait for all loads in flight).  The
+// would otherwise make LDS reads wait for all loads in flight).  The
 // instruction has no destination register; its address operands are read at
 // issue.
 __device__ __forceinline__ void dma16(const i32x4& rsrc, const uint8_t* lds, uint32_t voff, uint32_t soff)
@@ -206,14 +260,79 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// Accumulators of one wave: kFM x kFN 32x32 blocks.
+template <typename S>
+struct Acc {
+    f32x16 v[S::kFM][S::kFN];
+};
+
+// Epilogue: activation and store of a tile from the wave's accumulators.
+// Lane holds row m = .. + (lane & 31), 4 consecutive columns per group.
+template <typename ET, typename S, int EPI>
+__device__ __forceinline__ void store_tile(const Acc<S>& acc, typename ET::storage* __restrict__ C, const TileDec& t,
+                                           int Nout, int ncols)
+{
+    typedef typename ET::storage T;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / S::WN, wn = wave % S::WN;
+#pragma unroll
+    for (int i = 0; i < S::kFM; ++i) {
+        const int m = wm * S::kWaveM + i * 32 + (lane & 31);
+        if (m >= t.rows)
+            continue;
+        T* crow = C + (size_t)(t.row0 + m) * Nout;
+        constexpr int kJ = (EPI == EPI_SWIGLU) ? S::kFN / 2 : S::kFN;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int nl = j * 32 + 8 * g4 + 4 * (lane >> 5);
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float u = acc.v[i][j][4 * g4 + q];
+                    if (EPI == EPI_RELU)
+                        u = fmaxf(u, 0.0f);
+                    if (EPI == EPI_SWIGLU) {
+                        const float up = acc.v[i][j + S::kFN / 2][4 * g4 + q];
+                        u = u / (1.0f + __expf(-u)) * up;
+                    }
+                    v[q] = u;
+                }
+                const int n = t.n0 + ((EPI == EPI_SWIGLU) ? wn * (S::kWaveN / 2) : wn * S::kWaveN) + nl;
+                if (n < ncols) {
+                    if constexpr (ET::kBytes == 2) {
+                        uint2 o;
+                        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(crow + n) = o;
+                    } else {
+                        *reinterpret_cast<float4*>(crow + n) = make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Partial tiles hold the accumulators in thread order: float4 number
+// ((wave*kFM + i)*kFN + j)*4 + g of every lane, lane-minor, so both kernels
+// read and write them with coalesced 16-byte accesses.
+template <typename S>
+__device__ __forceinline__ size_t partial_index(int wave, int i, int j, int g, int lane)
+{
+    return ((((size_t)(wave * S::kFM + i) * S::kFN + j) * 4 + g) * kWave + lane) * 4;
+}
+
 template <typename ET, typename S, int EPI>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
-void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const typename ET::storage* __restrict__ W,
+void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const int32_t* __restrict__ gather,
+                             int gather_rows, const typename ET::storage* __restrict__ W,
                              typename ET::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E,
-                             int K, int Nw, int Nout, int F, int max_rows)
+                             int K, int Nw, int Nout, int F, int max_rows, float* __restrict__ partial)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only types; the host pass needs the stub only
-    typedef typename ET::storage T;
     constexpr int kWaves = S::kWaves;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[S::kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[S::kStage];
@@ -232,11 +351,10 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const t
     // chunk of swz().  The swizzle term depends on the block only through the
     // parity of its index for 128-byte rows; a wave's blocks are
     // wave + kWaves*i, whose parity is the wave's (kWaves is even).
-    static_assert(kWaves % 2 == 0, "block parity must be fixed per wave");
     const int lrow = lane / S::kNch, lphys = lane % S::kNch;
-    const int blk_row0 = (S::RB == 128) ? 8 * (wave & 1) : 0;  // R0 mod (2 * 256 / RB) that matters
+    const int blk_row0 = (S::RB == 128) ? 8 * (wave & 1) : 0;
     const int lchunk = lphys ^ (((blk_row0 + lrow) >> S::kSwzShift) & (S::kNch - 1));
-    const uint32_t lane_off = (uint32_t)lrow * rowK + (uint32_t)(lchunk << 4);
+    const uint32_t lane_chunk = (uint32_t)(lchunk << 4);
 
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
     const int ncols = (EPI == EPI_SWIGLU) ? F : Nout;
@@ -245,46 +363,48 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const t
     const int total = s_pref[E];
     const int G = gridDim.x;
     const int nk = K / S::kBK;
+    const int parts = split_parts(total, G, nk, partial != nullptr);
+    const int full = total - total % G;
+    const int tail = total - full;
+    const int items = full + tail * parts;
 
-    for (int base = 0; base < total; base += G) {
+    for (int base = 0; base < items; base += G) {
         // XCD-aware order: blocks b, b+8, b+16, ... share an XCD.
         const int b = blockIdx.x;
-        const int tile = (MOE_XCD_REMAP && G % 8 == 0) ? base + (b % 8) * (G / 8) + b / 8 : base + b;
-        if (tile >= total)
+        const int item = (G % 8 == 0) ? base + (b % 8) * (G / 8) + b / 8 : base + b;
+        if (item >= items)
             continue;
-        int lo = 0, hi = E;  // largest e with s_pref[e] <= tile
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_pref[mid] <= tile)
-                lo = mid;
-            else
-                hi = mid;
+        int tile = item, k0 = 0, k1 = nk, slot = -1;
+        if (item >= full && parts > 1) {
+            const int j = item - full, part = j / tail;
+            tile = full + j % tail;
+            k0 = part * nk / parts;
+            k1 = (part + 1) * nk / parts;
+            slot = (j % tail) * parts + part;
         }
-        const int e = lo;
-        int seg0, seg_rows;
-        seg_bounds(offsets, e, max_rows, seg0, seg_rows);
-        const int mt_e = (seg_rows + S::BM - 1) / S::BM;
-        // (m-group, n-tile, m-tile within group) order: groups of GM m-tiles
-        // sweep all n-tiles together, so GM activation tiles and a run of
-        // weight panels are live on an XCD at once
-        const int local = tile - s_pref[e];
-        const int g = local / (S::GM * ntn);
-        const int within = local - g * S::GM * ntn;
-        const int gs = min(S::GM, mt_e - g * S::GM);
-        const int nt = within / gs;
-        const int mt = g * S::GM + within % gs;
-        const int row0 = seg0 + mt * S::BM;
-        const int rows = min(S::BM, seg_rows - mt * S::BM);
-        const int n0 = nt * tile_cols;
+        const TileDec t = decode_tile<S>(tile, s_pref, offsets, E, max_rows, ntn, tile_cols);
 
-        // activation rows [row0, row0 + rows): rows past the segment read 0
-        const i32x4 rsA = make_rsrc(A + (size_t)row0 * K, (uint32_t)rows * rowK);
-        // this expert's weight matrix: rows past Nw read 0
-        const i32x4 rsW = make_rsrc(W + (size_t)e * Nw * K, (uint32_t)Nw * rowK);
-        uint32_t voffA[S::kBlkA], voffB[S::kBlkB];
+        // activation rows: the tile's rows of A (rows past the segment read
+        // 0), or rows gather[row] of A
+        i32x4 rsA;
+        uint32_t voffA[S::kBlkA];
+        if (gather) {
+            rsA = make_rsrc(A, (uint32_t)gather_rows * rowK);
 #pragma unroll
-        for (int i = 0; i < S::kBlkA; ++i)
-            voffA[i] = (uint32_t)(S::kRowsPerBlk * (wave + kWaves * i)) * rowK + lane_off;
+            for (int i = 0; i < S::kBlkA; ++i) {
+                const int r = S::kRowsPerBlk * (wave + kWaves * i) + lrow;
+                const int src = (r < t.rows) ? gather[t.row0 + r] : -1;
+                voffA[i] = (src >= 0 && src < gather_rows) ? (uint32_t)src * rowK + lane_chunk : 0xf0000000u;
+            }
+        } else {
+            rsA = make_rsrc(A + (size_t)t.row0 * K, (uint32_t)t.rows * rowK);
+#pragma unroll
+            for (int i = 0; i < S::kBlkA; ++i)
+                voffA[i] = (uint32_t)(S::kRowsPerBlk * (wave + kWaves * i) + lrow) * rowK + lane_chunk;
+        }
+        // this expert's weight matrix: rows past Nw read 0
+        const i32x4 rsW = make_rsrc(W + (size_t)t.e * Nw * K, (uint32_t)Nw * rowK);
+        uint32_t voffB[S::kBlkB];
 #pragma unroll
         for (int i = 0; i < S::kBlkB; ++i) {
             const int r = S::kRowsPerBlk * (wave + kWaves * i);  // first LDS row of the block
@@ -292,12 +412,12 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const t
             if (EPI == EPI_SWIGLU) {
                 const int wblk = r / S::kWaveN, rr = r % S::kWaveN;
                 const int half = rr / (S::kWaveN / 2);
-                const int hc = n0 + wblk * (S::kWaveN / 2) + rr % (S::kWaveN / 2);
+                const int hc = t.n0 + wblk * (S::kWaveN / 2) + rr % (S::kWaveN / 2);
                 wrow = half ? F + hc : (hc < F ? hc : Nw);  // gate rows past F read 0
             } else {
-                wrow = n0 + r;
+                wrow = t.n0 + r;
             }
-            voffB[i] = (uint32_t)wrow * rowK + lane_off;
+            voffB[i] = (uint32_t)(wrow + lrow) * rowK + lane_chunk;
         }
 
         auto issue = [&](int kt, uint8_t* dst) {
@@ -310,14 +430,14 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const t
                 dma16(rsW, dst + S::kLdsA + (wave + kWaves * i) * 1024, voffB[i], soff);
         };
 
-        f32x16 acc[S::kFM][S::kFN];
+        Acc<S> acc;
 #pragma unroll
         for (int i = 0; i < S::kFM; ++i)
 #pragma unroll
             for (int j = 0; j < S::kFN; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    acc[i][j][v] = 0.0f;
+                    acc.v[i][j][v] = 0.0f;
 
         // Wait until at most n slices of this wave's loads are in flight.
         auto wait_slices = [&](int n) {
@@ -332,12 +452,11 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const t
         // One K slice kt held in `cur`: wait for it (later slices may stay in
         // flight), meet the other waves (they have finished slice kt-1, so its
         // buffer `nxt` is free), start loading slice kt+S-1 into `nxt`, then
-        // multiply.  Buffers are distinct LDS arrays known at compile time, so
-        // reads of `cur` never wait for the loads into `nxt`.
+        // multiply.  Buffers are distinct LDS arrays known at compile time.
         auto slice = [&](int kt, const uint8_t* cur, uint8_t* nxt) {
-            wait_slices(min(S::S - 2, nk - 1 - kt));
+            wait_slices(min(S::S - 2, k1 - 1 - kt));
             lds_barrier();
-            if (kt + S::S - 1 < nk)
+            if (kt + S::S - 1 < k1)
                 issue(kt + S::S - 1, nxt);
             const uint8_t* bufA = cur;
             const uint8_t* bufB = cur + S::kLdsA;
@@ -358,15 +477,16 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const t
 #pragma unroll
                     for (int j = 0; j < S::kFN; ++j) {
                         if constexpr (ET::kBytes == 2) {
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8, fa[j]), __builtin_bit_cast(bf16x8, fb[i]), acc[i][j], 0,
-                                0, 0);
+                            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8, fa[j]), __builtin_bit_cast(bf16x8, fb[i]), acc.v[i][j],
+                                0, 0, 0);
                         } else {
                             const f32x4 va = __builtin_bit_cast(f32x4, fa[j]);
                             const f32x4 vb = __builtin_bit_cast(f32x4, fb[i]);
 #pragma unroll
                             for (int q = 0; q < 4; ++q)
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[q], vb[q], acc[i][j], 0, 0, 0);
+                                acc.v[i][j] =
+                                    __builtin_amdgcn_mfma_f32_32x32x2f32(va[q], vb[q], acc.v[i][j], 0, 0, 0);
                         }
                     }
             }
@@ -376,83 +496,111 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const t
         __syncthreads();  // every wave is done with the previous tile's buffers
 #pragma unroll
         for (int s0 = 0; s0 < S::S - 1; ++s0) {
-            if (s0 < nk)
-                issue(s0, s0 == 0 ? lds0 : s0 == 1 ? lds1 : lds2);
+            if (k0 + s0 < k1)
+                issue(k0 + s0, s0 == 0 ? lds0 : s0 == 1 ? lds1 : lds2);
         }
-        int kt = 0;
+        // slice k0 + n uses buffer n mod S
+        int kt = k0;
         if constexpr (S::S == 2) {
-            for (; kt + 2 <= nk; kt += 2) {
+            for (; kt + 2 <= k1; kt += 2) {
                 slice(kt, lds0, lds1);
                 slice(kt + 1, lds1, lds0);
             }
-            if (kt < nk)
+            if (kt < k1)
                 slice(kt, lds0, lds1);
         } else if constexpr (S::S == 3) {
-            for (; kt + 3 <= nk; kt += 3) {
+            for (; kt + 3 <= k1; kt += 3) {
                 slice(kt, lds0, lds2);
                 slice(kt + 1, lds1, lds0);
                 slice(kt + 2, lds2, lds1);
             }
-            if (kt < nk)
+            if (kt < k1)
                 slice(kt, lds0, lds2);
-            if (kt + 1 < nk)
+            if (kt + 1 < k1)
                 slice(kt + 1, lds1, lds0);
         } else {
-            for (; kt + 4 <= nk; kt += 4) {
+            for (; kt + 4 <= k1; kt += 4) {
                 slice(kt, lds0, lds3);
                 slice(kt + 1, lds1, lds0);
                 slice(kt + 2, lds2, lds1);
                 slice(kt + 3, lds3, lds2);
             }
-            if (kt < nk)
+            if (kt < k1)
                 slice(kt, lds0, lds3);
-            if (kt + 1 < nk)
+            if (kt + 1 < k1)
                 slice(kt + 1, lds1, lds0);
-            if (kt + 2 < nk)
+            if (kt + 2 < k1)
                 slice(kt + 2, lds2, lds1);
         }
 
-        // epilogue: lane holds rows m = .. + (lane & 31), 4 consecutive columns per group
+        if (slot < 0) {
+            store_tile<ET, S, EPI>(acc, C, t, Nout, ncols);
+        } else {
+            float* dst = partial + (size_t)slot * S::kTileFloats;
 #pragma unroll
-        for (int i = 0; i < S::kFM; ++i) {
-            const int m = wm * S::kWaveM + i * 32 + (lane & 31);
-            if (m >= rows)
-                continue;
-            T* crow = C + (size_t)(row0 + m) * Nout;
-            constexpr int kJ = (EPI == EPI_SWIGLU) ? S::kFN / 2 : S::kFN;
+            for (int i = 0; i < S::kFM; ++i)
 #pragma unroll
-            for (int j = 0; j < kJ; ++j) {
+                for (int j = 0; j < S::kFN; ++j)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int nl = j * 32 + 8 * g4 + 4 * (lane >> 5);
-                    float v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float u = acc[i][j][4 * g4 + q];
-                        if (EPI == EPI_RELU)
-                            u = fmaxf(u, 0.0f);
-                        if (EPI == EPI_SWIGLU) {
-                            const float up = acc[i][j + S::kFN / 2][4 * g4 + q];
-                            u = u / (1.0f + __expf(-u)) * up;
-                        }
-                        v[q] = u;
-                    }
-                    const int n = n0 + ((EPI == EPI_SWIGLU) ? wn * (S::kWaveN / 2) : wn * S::kWaveN) + nl;
-                    if (n < ncols) {
-                        if constexpr (ET::kBytes == 2) {
-                            uint2 o;
-                            o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                            o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                            *reinterpret_cast<uint2*>(crow + n) = o;
-                        } else {
-                            *reinterpret_cast<float4*>(crow + n) = make_float4(v[0], v[1], v[2], v[3]);
-                        }
-                    }
-                }
-            }
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<float4*>(dst + partial_index<S>(wave, i, j, g, lane)) =
+                            make_float4(acc.v[i][j][4 * g], acc.v[i][j][4 * g + 1], acc.v[i][j][4 * g + 2],
+                                        acc.v[i][j][4 * g + 3]);
         }
     }
 #endif
+}
+
+// Second pass of the tail split: one block per split tile adds its K parts in
+// part order and stores the tile through the same epilogue.
+template <typename ET, typename S, int EPI>
+__global__ __launch_bounds__(S::kThreads) void moe_grouped_gemm_tail_kernel(
+    typename ET::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E, int K, int Nout, int F,
+    int max_rows, int G, const float* __restrict__ partial)
+{
+    __shared__ int32_t s_pref[kGemmMaxE + 1];
+    __shared__ int32_t s_wsum[S::kWaves];
+    const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
+    const int ncols = (EPI == EPI_SWIGLU) ? F : Nout;
+    const int ntn = (ncols + tile_cols - 1) / tile_cols;
+    tile_prefix<S::kThreads>(offsets, E, max_rows, S::BM, ntn, s_pref, s_wsum);
+    const int total = s_pref[E];
+    const int nk = K / S::kBK;
+    const int parts = split_parts(total, G, nk, true);
+    if (parts <= 1)
+        return;
+    const int full = total - total % G;
+    const int tail = total - full;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    for (int j = blockIdx.x; j < tail; j += gridDim.x) {
+        const TileDec t = decode_tile<S>(full + j, s_pref, offsets, E, max_rows, ntn, tile_cols);
+        Acc<S> acc;
+#pragma unroll
+        for (int i = 0; i < S::kFM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < S::kFN; ++jj)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc.v[i][jj][v] = 0.0f;
+        for (int part = 0; part < parts; ++part) {
+            const float* src = partial + (size_t)(j * parts + part) * S::kTileFloats;
+#pragma unroll
+            for (int i = 0; i < S::kFM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < S::kFN; ++jj)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 p =
+                            *reinterpret_cast<const float4*>(src + partial_index<S>(wave, i, jj, g, lane));
+                        acc.v[i][jj][4 * g] += p.x;
+                        acc.v[i][jj][4 * g + 1] += p.y;
+                        acc.v[i][jj][4 * g + 2] += p.z;
+                        acc.v[i][jj][4 * g + 3] += p.w;
+                    }
+        }
+        store_tile<ET, S, EPI>(acc, C, t, Nout, ncols);
+    }
 }
 
 }  // namespace moe
@@ -461,8 +609,9 @@ namespace {
 using namespace moe;
 
 template <typename ET, typename S, int EPI>
-hipError_t launch_one(const void* A, const void* W, void* C, const int32_t* offsets, int E, int K, int Nw, int Nout,
-                      int F, int max_rows, int ncu, hipStream_t stream)
+hipError_t launch_one(const void* A, const int32_t* gather, int gather_rows, const void* W, void* C,
+                      const int32_t* offsets, int E, int K, int Nw, int Nout, int F, int max_rows, int ncu,
+                      float* partial, hipStream_t stream)
 {
     typedef typename ET::storage T;
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
@@ -470,26 +619,37 @@ hipError_t launch_one(const void* A, const void* W, void* C, const int32_t* offs
     const long long ntn = (ncols + tile_cols - 1) / tile_cols;
     // upper bound on m-tiles: floor(P/BM) full tiles plus one partial per expert
     const long long mt_max = max_rows / S::BM + (long long)(E < max_rows ? E : max_rows);
-    long long tiles_max = mt_max * ntn;
+    const long long tiles_max = mt_max * ntn;
     long long grid = (long long)ncu * S::OCC;  // persistent: as many blocks as are resident at once
-    if (tiles_max < grid)
+    // without the split a grid beyond the tile count only idles; with it the
+    // spare blocks take K parts of the tiles
+    if (tiles_max < grid && partial == nullptr)
         grid = (tiles_max + 7) / 8 * 8;
     if (grid < 1)
         grid = 1;
     moe_grouped_gemm_kernel<ET, S, EPI><<<dim3((unsigned)grid), dim3(S::kThreads), 0, stream>>>(
-        (const T*)A, (const T*)W, (T*)C, offsets, E, K, Nw, Nout, F, max_rows);
+        (const T*)A, gather, gather_rows, (const T*)W, (T*)C, offsets, E, K, Nw, Nout, F, max_rows, partial);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || partial == nullptr)
+        return err;
+    moe_grouped_gemm_tail_kernel<ET, S, EPI><<<dim3(kSplitSlots / 2), dim3(S::kThreads), 0, stream>>>(
+        (T*)C, offsets, E, K, Nout, F, max_rows, (int)grid, partial);
     return hipGetLastError();
 }
 
 template <typename ET, typename S>
-hipError_t launch_epi(int epi, const void* A, const void* W, void* C, const int32_t* offsets, int E, int K, int Nw,
-                      int Nout, int F, int max_rows, int ncu, hipStream_t stream)
+hipError_t launch_epi(int epi, const void* A, const int32_t* gather, int gather_rows, const void* W, void* C,
+                      const int32_t* offsets, int E, int K, int Nw, int Nout, int F, int max_rows, int ncu,
+                      float* partial, hipStream_t stream)
 {
     if (epi == EPI_RELU)
-        return launch_one<ET, S, EPI_RELU>(A, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, stream);
+        return launch_one<ET, S, EPI_RELU>(A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu,
+                                           partial, stream);
     if (epi == EPI_SWIGLU)
-        return launch_one<ET, S, EPI_SWIGLU>(A, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, stream);
-    return launch_one<ET, S, EPI_NONE>(A, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, stream);
+        return launch_one<ET, S, EPI_SWIGLU>(A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows,
+                                             ncu, partial, stream);
+    return launch_one<ET, S, EPI_NONE>(A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu,
+                                       partial, stream);
 }
 }  // namespace
 
@@ -500,8 +660,8 @@ hipError_t launch_epi(int epi, const void* A, const void* W, void* C, const int3
 //           64 each), the densest tile that fits the register file; 2 x 64 KB
 //           of LDS stages
 //   medium  128..511 rows: 128 x 128 tiles, 4 waves, 2 blocks per CU
-//   small   < 128 rows: 64 x 256 tiles, 4 waves (short
-//           segments, so tall tiles would mostly compute padding)
+//   small   < 128 rows: 64 x 256 tiles, 4 waves (short segments, so tall
+//           tiles would mostly compute padding)
 #ifndef MOE_LARGE_TILE
 #define MOE_LARGE_TILE 256, 256, 2, 4, 128, 2, 1, 8
 #endif
@@ -512,22 +672,42 @@ hipError_t launch_epi(int epi, const void* A, const void* W, void* C, const int3
 #define MOE_SMALL_TILE 64, 256, 1, 4, 128, 2, 1, 4
 #endif
 
+// Workspace bytes the tail split needs for a problem with this mean rows per
+// expert (the partial tiles of the configuration the launcher picks).
+extern "C" size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows)
+{
+    size_t tile_floats;
+    if (dtype == 0)
+        tile_floats = GemmShape<f32_t, 128, 128, 2, 2, 128, 2, 1, 4>::kTileFloats;
+    else if (mean_rows >= 512)
+        tile_floats = GemmShape<bf16_t, MOE_LARGE_TILE>::kTileFloats;
+    else if (mean_rows >= 128)
+        tile_floats = GemmShape<bf16_t, MOE_MEDIUM_TILE>::kTileFloats;
+    else
+        tile_floats = GemmShape<bf16_t, MOE_SMALL_TILE>::kTileFloats;
+    return (size_t)kSplitSlots * tile_floats * sizeof(float);
+}
+
 // epi: 0 none, 1 ReLU, 2 SwiGLU.  Nw = weight rows per expert, Nout = output
 // row stride (= output columns).  max_rows bounds offsets[E]; mean_rows is the
-// expected rows per expert (selects the tile configuration).
-extern "C" hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const void* W, void* C,
-                                              const int32_t* offsets, int E, int K, int Nw, int Nout, int F,
-                                              int max_rows, int mean_rows, int ncu, hipStream_t stream)
+// expected rows per expert (selects the tile configuration).  gather
+// (nullable) maps each permuted row to its row of A (gather_rows rows).
+// partial (nullable) is the tail-split workspace of
+// moe_grouped_gemm_partial_bytes bytes; NULL disables the split.
+extern "C" hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const int32_t* gather,
+                                              int gather_rows, const void* W, void* C, const int32_t* offsets, int E,
+                                              int K, int Nw, int Nout, int F, int max_rows, int mean_rows, int ncu,
+                                              float* partial, hipStream_t stream)
 {
     if (dtype == 0)
-        return launch_epi<f32_t, GemmShape<f32_t, 128, 128, 2, 2, 128, 2, 1, 4>>(epi, A, W, C, offsets, E, K, Nw,
-                                                                                 Nout, F, max_rows, ncu, stream);
+        return launch_epi<f32_t, GemmShape<f32_t, 128, 128, 2, 2, 128, 2, 1, 4>>(
+            epi, A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, partial, stream);
     if (mean_rows >= 512)
-        return launch_epi<bf16_t, GemmShape<bf16_t, MOE_LARGE_TILE>>(epi, A, W, C, offsets, E, K, Nw, Nout, F,
-                                                                      max_rows, ncu, stream);
+        return launch_epi<bf16_t, GemmShape<bf16_t, MOE_LARGE_TILE>>(epi, A, gather, gather_rows, W, C, offsets, E,
+                                                                      K, Nw, Nout, F, max_rows, ncu, partial, stream);
     if (mean_rows >= 128)
-        return launch_epi<bf16_t, GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, A, W, C, offsets, E, K, Nw, Nout, F,
-                                                                       max_rows, ncu, stream);
-    return launch_epi<bf16_t, GemmShape<bf16_t, MOE_SMALL_TILE>>(epi, A, W, C, offsets, E, K, Nw, Nout, F,
-                                                                  max_rows, ncu, stream);
+        return launch_epi<bf16_t, GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, A, gather, gather_rows, W, C, offsets, E,
+                                                                       K, Nw, Nout, F, max_rows, ncu, partial, stream);
+    return launch_epi<bf16_t, GemmShape<bf16_t, MOE_SMALL_TILE>>(epi, A, gather, gather_rows, W, C, offsets, E, K,
+                                                                  Nw, Nout, F, max_rows, ncu, partial, stream);
 }

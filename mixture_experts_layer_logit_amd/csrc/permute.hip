@@ -211,6 +211,8 @@ __global__ __launch_bounds__(256) void moe_gather_kernel(const typename ET::stor
 
 }  // namespace moe
 
+// x_perm == NULL skips the row copy (a caller that reads the rows of x
+// through src_token itself).
 extern "C" hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, const void* x, int T, int d, int E,
                                          int k, long long C, int32_t* counts, int32_t* offsets, int32_t* slot,
                                          int32_t* src_token, void* x_perm, int32_t* chunk_cnt,
@@ -221,6 +223,8 @@ extern "C" hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, con
     moe_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, chunk_cnt);
     moe_scan_kernel<<<1, 1024, 0, stream>>>(chunk_cnt, nchunks, E, C, counts, offsets);
     moe_scatter_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, C, chunk_cnt, offsets, slot, src_token);
+    if (x_perm == nullptr)
+        return hipGetLastError();
     const dim3 grid((T + 3) / 4);
     if (dtype == 0)
         moe_gather_kernel<f32_t><<<grid, 256, 0, stream>>>((const float*)x, slot, T, d, k, (float*)x_perm);

@@ -41,18 +41,37 @@ def test_capacity_matches_oracle(T, E, k, cf):
     assert moe.moe_capacity(p) == oracle.capacity(T, E, k, cf)
 
 
-def workspace_formula(T, d, E, k, F, b):
+def partial_floats(T, E, k, b, cf):
+    """One partial output tile of the grouped GEMM's K-split last round, by
+    the tile shape the expected rows per expert select."""
+    rows = T * k // E
+    C = oracle.capacity(T, E, k, cf)
+    if C >= 0:
+        rows = min(rows, C)
+    if b == 4:
+        return 128 * 128
+    return 256 * 256 if rows >= 512 else 128 * 128 if rows >= 128 else 64 * 256
+
+
+def workspace_formula(T, d, E, k, F, b, cf=0.0):
     r = lambda n: (n + 255) // 256 * 256
     nch = max((T + 255) // 256, 1)
+    gather = T * d * b < 0xF0000000  # else x_perm is kept in the workspace
     return (r(T * k * 4) * 4 + r(E * 4) + r((E + 1) * 4) + r(nch * E * 4) + r(T * E * 4)
-            + r(T * k * d * b) * 2 + r(T * k * F * b))
+            + r(256 * partial_floats(T, E, k, b, cf) * 4) + r(T * k * F * b) + r(T * k * d * b)
+            + (0 if gather else r(T * k * d * b)))
 
 
-@pytest.mark.parametrize("T,d,E,k,F,dt", [(256, 64, 4, 2, 128, "f32"), (4096, 4096, 8, 2, 14336, "bf16"),
-                                          (1, 64, 1, 1, 64, "bf16"), (16384, 1024, 512, 2, 512, "bf16")])
-def test_workspace_size(T, d, E, k, F, dt):
-    p = moe.problem(T, d, E, k, F, dtype=dt)
-    assert moe.moe_workspace_size(p) == workspace_formula(T, d, E, k, F, 4 if dt == "f32" else 2)
+@pytest.mark.parametrize("T,d,E,k,F,dt,cf", [(256, 64, 4, 2, 128, "f32", 0.0),
+                                             (4096, 4096, 8, 2, 14336, "bf16", 0.0),
+                                             (1, 64, 1, 1, 64, "bf16", 0.0),
+                                             (16384, 1024, 512, 2, 512, "bf16", 0.0),
+                                             (8192, 2048, 16, 2, 1408, "bf16", 1.25),
+                                             (8192, 2048, 64, 2, 1408, "bf16", 0.25),
+                                             (1 << 21, 2048, 64, 2, 1024, "bf16", 0.0)])
+def test_workspace_size(T, d, E, k, F, dt, cf):
+    p = moe.problem(T, d, E, k, F, dtype=dt, cf=cf)
+    assert moe.moe_workspace_size(p) == workspace_formula(T, d, E, k, F, 4 if dt == "f32" else 2, cf)
 
 
 BAD = [
@@ -106,8 +125,22 @@ def test_bad_pointers_rejected_before_launch():
         moe.MOE_ERR_INVALID_ARG
     # null outputs
     assert lib.moe_combine(pp, FAKE, FAKE, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_up(pp, FAKE, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_down(pp, FAKE, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_up(pp, FAKE, None, FAKE, FAKE, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(pp, FAKE, FAKE, None, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    # a workspace, when given, must be large enough
+    assert lib.moe_expert_up(pp, FAKE, None, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_down(pp, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == moe.MOE_ERR_WORKSPACE
+    # misaligned gather index
+    assert lib.moe_expert_up(pp, FAKE, FAKE + 1, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_gather_limited_to_32_bit_offsets():
+    # x of 8 GiB cannot be read through src_token; x_perm must be passed
+    p = moe.problem(1 << 21, 2048, 64, 2, 1024)
+    lib = moe.load()
+    pp = ctypes.byref(p)
+    assert lib.moe_expert_up(pp, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED
+    assert b"gather" in lib.moe_last_error()
 
 
 def test_empty_problem_is_a_no_op():

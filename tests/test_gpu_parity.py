@@ -233,25 +233,100 @@ def test_expert_up_and_down(name):
     xp_d = torch.zeros(rows_cap, case.d, dtype=dt, device="cuda")
     xp_d[:P] = dev(xp)
     off_d = dev(disp["offsets"])
+    src_d = torch.full((rows_cap,), -1, dtype=torch.int32, device="cuda")
+    src_d[:P] = dev(disp["src_token"])
+    W1 = dev(inp["W1"])
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
     h = torch.zeros(rows_cap, case.F, dtype=dt, device="cuda")
-    moe.moe_expert_up(p, xp_d, off_d, dev(inp["W1"]), h)
+    moe.moe_expert_up(p, xp_d, None, off_d, W1, h)
+    # the same rows gathered from x through src_token: the same tiles in the
+    # same order, so bit-identical
+    hg = torch.zeros(rows_cap, case.F, dtype=dt, device="cuda")
+    moe.moe_expert_up(p, dev(inp["x"]), src_d, off_d, W1, hg, ws=ws)
+    hw = torch.zeros(rows_cap, case.F, dtype=dt, device="cuda")
+    moe.moe_expert_up(p, xp_d, None, off_d, W1, hw, ws=ws)
     torch.cuda.synchronize()
     ref_y, ref_h = oracle.ffn_rows(xp, disp["offsets"], inp["W1"], inp["W2"], act_code(case), case.F, want_h=True)
     assert maxrel(host(h)[:P], ref_h) <= TOL[case.dtype]
+    assert maxrel(host(hw)[:P], ref_h) <= TOL[case.dtype]
+    assert np.array_equal(host(hg)[:P], host(hw)[:P])
     # down on synthetic hidden rows
     hs = moe_inputs._cast(RNG.standard_normal((P, case.F)).astype(np.float32), case.dtype)
     hs_d = torch.zeros(rows_cap, case.F, dtype=dt, device="cuda")
     hs_d[:P] = dev(hs)
     yp = torch.zeros(rows_cap, case.d, dtype=dt, device="cuda")
-    moe.moe_expert_down(p, hs_d, off_d, dev(inp["W2"]), yp)
+    moe.moe_expert_down(p, hs_d, off_d, dev(inp["W2"]), yp, ws=ws)
     torch.cuda.synchronize()
     assert maxrel(host(yp)[:P], oracle.down_rows(hs, disp["offsets"], inp["W2"])) <= TOL[case.dtype]
     # both layers through moe_grouped_ffn (h in the workspace)
-    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
     yp2 = torch.zeros(rows_cap, case.d, dtype=dt, device="cuda")
-    moe.moe_grouped_ffn(p, xp_d, off_d, dev(inp["W1"]), dev(inp["W2"]), yp2, ws)
+    moe.moe_grouped_ffn(p, xp_d, off_d, W1, dev(inp["W2"]), yp2, ws)
     torch.cuda.synchronize()
     assert maxrel(host(yp2)[:P], ref_y) <= TOL[case.dtype]
+
+
+# Hand-made segment layouts whose last round of output tiles is partly
+# filled, so that, given a workspace, the grouped GEMM splits those tiles
+# along K (one per tile configuration: large, medium, small and fp32).
+SPLIT_CASES = {
+    # name: (dtype, act, T, d, E, k, F, segment rows)
+    "large_relu": ("bf16", "relu", 1024, 1024, 4, 2, 1536, [700, 300, 512, 536]),
+    "large_ragged": ("bf16", "relu", 1024, 1024, 4, 2, 1024, [1, 0, 1019, 1000]),
+    "medium_swiglu": ("bf16", "swiglu", 512, 512, 4, 2, 512, [300, 0, 257, 300]),
+    "small_relu": ("bf16", "relu", 512, 1024, 16, 2, 512, [64] * 14 + [1, 63]),
+    "f32_relu": ("f32", "relu", 512, 512, 4, 1, 512, [130, 0, 200, 150]),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_expert_split_tail(name):
+    dtype, act, T, d, E, k, F, seg = SPLIT_CASES[name]
+    print(f"[ffn-split] {name}", flush=True)
+    assert sum(seg) <= T * k and len(seg) == E
+    p = moe.problem(T, d, E, k, F, act=act, dtype=dtype)
+    offsets = np.concatenate([[0], np.cumsum(seg)]).astype(np.int32)
+    P = int(offsets[-1])
+    rng = np.random.default_rng(4242 + len(name))
+    n1 = 2 * F if act == "swiglu" else F
+    x = moe_inputs._cast(rng.standard_normal((T, d)).astype(np.float32), dtype)
+    src = rng.integers(0, T, size=P).astype(np.int32)
+    xp = x[src]
+    W1 = moe_inputs._cast((rng.standard_normal((E, n1, d)) / np.sqrt(d)).astype(np.float32), dtype)
+    W2 = moe_inputs._cast((rng.standard_normal((E, d, F)) / np.sqrt(F)).astype(np.float32), dtype)
+    hs = moe_inputs._cast(np.abs(rng.standard_normal((P, F))).astype(np.float32), dtype)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rows_cap = T * k
+    xp_d = torch.zeros(rows_cap, d, dtype=dt, device="cuda")
+    xp_d[:P] = dev(xp)
+    src_d = torch.full((rows_cap,), -1, dtype=torch.int32, device="cuda")
+    src_d[:P] = dev(src)
+    hs_d = torch.zeros(rows_cap, F, dtype=dt, device="cuda")
+    hs_d[:P] = dev(hs)
+    off_d, W1_d, W2_d = dev(offsets), dev(W1), dev(W2)
+    # poisoned workspace: the split must write its partial tiles there
+    ws = torch.full((moe.moe_workspace_size(p),), 0xFF, dtype=torch.uint8, device="cuda")
+    h0 = torch.zeros(rows_cap, F, dtype=dt, device="cuda")
+    h1, h2 = torch.zeros_like(h0), torch.zeros_like(h0)
+    moe.moe_expert_up(p, xp_d, None, off_d, W1_d, h0)
+    moe.moe_expert_up(p, xp_d, None, off_d, W1_d, h1, ws=ws)
+    torch.cuda.synchronize()
+    assert int((ws != 0xFF).sum()) > 0, "the K split did not run"
+    moe.moe_expert_up(p, dev(x), src_d, off_d, W1_d, h2, ws=ws)
+    y0 = torch.zeros(rows_cap, d, dtype=dt, device="cuda")
+    y1 = torch.zeros_like(y0)
+    moe.moe_expert_down(p, hs_d, off_d, W2_d, y0)
+    moe.moe_expert_down(p, hs_d, off_d, W2_d, y1, ws=ws)
+    torch.cuda.synchronize()
+    act_c = oracle.SWIGLU if act == "swiglu" else oracle.RELU
+    _y, ref_h = oracle.ffn_rows(xp, offsets, W1, W2, act_c, F, want_h=True)
+    ref_y = oracle.down_rows(hs, offsets, W2)
+    for got in (h0, h1, h2):
+        assert maxrel(host(got)[:P], ref_h) <= TOL[dtype]
+    assert np.array_equal(host(h1)[:P], host(h2)[:P])
+    for got in (y0, y1):
+        assert maxrel(host(got)[:P], ref_y) <= TOL[dtype]
+    # rows past the kept ones are never written
+    assert not host(h1)[P:].any() and not host(y1)[P:].any()
 
 
 # ------------------------------------------------------------------ combine
