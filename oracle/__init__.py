@@ -77,6 +77,7 @@ def _load():
     lib.orc_ffn_rows.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, P]
     lib.orc_combine.argtypes = [I, I, I, I, P, P, P, P]
     lib.orc_down_rows.argtypes = [I, I, I, I, P, P, P, I, P, P]
+    lib.orc_router_stats.argtypes = [I, I, I, I, D, P, P, ctypes.c_longlong, P, P, P]
     _lib = lib
     return lib
 
@@ -286,3 +287,39 @@ def moe_forward(x, Wg, bg, W1, W2, *, k, F, act, normalize_flag=False, lam=1.0, 
     out = {"z_exact": z_exact, "z32": z32, "topk_idx": idx, "topk_w": w, "C": C, "y": y}
     out.update(disp)
     return out
+
+
+def router_stats(z32, counts, kept, k, normalize_flag=False, lam=1.0):
+    """Router by-products of a routed batch (see orc_router_stats): a dict
+    with frac [E], mean_prob [E] and the scalars aux, z_loss, drop_rate, all
+    float64.  z32 are the fp32 logits the routing used, counts the per-expert
+    assignment counts before the capacity clip, kept the assignments kept."""
+    z = _c(z32, np.float32)
+    T, E = z.shape
+    cnt = _c(counts, np.int32)
+    frac = np.empty(E, np.float64)
+    mp = np.empty(E, np.float64)
+    out3 = np.empty(3, np.float64)
+    _load().orc_router_stats(T, E, int(k), int(bool(normalize_flag)), float(lam), _ptr(z), _ptr(cnt), int(kept),
+                             _ptr(frac), _ptr(mp), _ptr(out3))
+    return {"frac": frac, "mean_prob": mp, "aux": out3[0], "z_loss": out3[1], "drop_rate": out3[2]}
+
+
+def shared_expert(x, Ws1, Ws2, act, Fs):
+    """Shared expert: one more expert FFN that every token passes through,
+    ungated (industry overview page, "MoE未來重點研究方向" item 4: DeepSeekMoE's
+    shared experts).  x [T,d]; Ws1 [n1,d] (SwiGLU gate rows first), Ws2 [d,Fs].
+    It is the expert FFN of a single expert whose segment holds all T rows.
+    Returns float64 [T,d]."""
+    x = _c(x)
+    T = x.shape[0]
+    offsets = np.array([0, T], np.int32)
+    return ffn_rows(x, offsets, np.asarray(Ws1)[None], np.asarray(Ws2)[None], act, Fs)
+
+
+def combine_shared(y_perm, slot, topk_w, y_shared):
+    """Combine with a shared expert: y[t] = y_shared[t] + sum over the kept
+    choices j of w[t,j] * y_perm[slot[t,j]] (the shared expert's output enters
+    with weight one).  y_shared is float64 or a stored fp32/bf16 array."""
+    ys = to_f64(np.asarray(y_shared)) if np.asarray(y_shared).dtype != np.float64 else np.asarray(y_shared)
+    return ys + combine(y_perm, slot, topk_w, ys.shape[0])

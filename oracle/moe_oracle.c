@@ -40,6 +40,18 @@
  *                 up_proj fused into one weight, order matters).  No biases.
  *   - combine:    y_t = sum over the token's kept choices j, in selection
  *                 order, of w[t,j] * expert_j(x_t).
+ *   - router by-products: the quantities the load-balancing auxiliary loss,
+ *                 its adaptive coefficient and the Z-loss are built from
+ *                 (Megatron-Core page, "MoE负载均衡的挑战与应对": an auxiliary
+ *                 loss pushes experts towards equal token counts, and
+ *                 "关键特性": Z-Loss among the balancing methods; Skywork-MoE
+ *                 news item, "技术创新 2. 自适应的Aux Loss", and slides, slide 7:
+ *                 the coefficient follows the token drop rate).  The pages
+ *                 give no formulas; the plainest readings are used: per
+ *                 expert the share of the T*k assignments f_e and the mean
+ *                 gate probability P_e, the loss E * sum_e f_e P_e (without
+ *                 its coefficient), the Z-loss mean_t (log sum_e exp z)^2 on
+ *                 the raw logits, and the drop rate = dropped / (T*k).
  *
  * Arithmetic: every floating-point sum and product is done in double; bf16
  * inputs are widened exactly (bf16 is the top half of an IEEE binary32).
@@ -366,4 +378,48 @@ void orc_down_rows(int E, int d, int F, int dtype, const int32_t* offsets, const
             out[(size_t)n * d + o] = s;
         }
     }
+}
+
+/* Router by-products of a routed batch.  z [T,E] fp32 logits (the ones the
+ * routing used), counts [E] assignments per expert before the capacity clip,
+ * kept = number of assignments kept after it.  Outputs (double):
+ *   frac[e]      = counts[e] / (T k)
+ *   mean_prob[e] = (1/T) sum_t p[t,e], p the gate probabilities (after the
+ *                  optional normalisation), tokens summed in order
+ *   out3[0]      = E * sum_e frac[e] * mean_prob[e]   (auxiliary loss)
+ *   out3[1]      = (1/T) sum_t (log sum_e exp z[t,e])^2   (Z-loss)
+ *   out3[2]      = (T k - kept) / (T k)   (drop rate) */
+void orc_router_stats(int T, int E, int k, int normalize, double lambda, const float* z,
+                      const int32_t* counts, long long kept, double* frac, double* mean_prob, double* out3)
+{
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    for (int e = 0; e < E; ++e)
+        mean_prob[e] = 0.0;
+    double zsum = 0.0;
+    for (int t = 0; t < T; ++t) {
+        const float* zt = z + (size_t)t * E;
+        orc_gate_probs(E, zt, normalize, lambda, p);
+        for (int e = 0; e < E; ++e)
+            mean_prob[e] += p[e];
+        double m = (double)zt[0];
+        for (int e = 1; e < E; ++e)
+            if ((double)zt[e] > m)
+                m = (double)zt[e];
+        double se = 0.0;
+        for (int e = 0; e < E; ++e)
+            se += exp((double)zt[e] - m);
+        double lse = m + log(se);
+        zsum += lse * lse;
+    }
+    const double n = (double)T * (double)k;
+    double aux = 0.0;
+    for (int e = 0; e < E; ++e) {
+        mean_prob[e] /= (double)T;
+        frac[e] = (double)counts[e] / n;
+        aux += frac[e] * mean_prob[e];
+    }
+    out3[0] = (double)E * aux;
+    out3[1] = zsum / (double)T;
+    out3[2] = (n - (double)kept) / n;
+    free(p);
 }

@@ -424,3 +424,126 @@ def test_down_rows_is_second_linear_layer(dtype):
     ref = np.stack([hh[r] @ oracle.to_f64(W2b)[int(np.searchsorted(offsets, r, side="right") - 1)].T
                     for r in range(20)])
     assert np.max(np.abs(full - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------- router by-products
+# Definitions read for the pages' unnamed formulas (Megatron-Core page, "MoE负载
+# 均衡的挑战与应对" and "关键特性": auxiliary balancing loss, Z-Loss; Skywork
+# news item, "技术创新 2", and slides, slide 7: drop-rate-driven coefficient):
+# f_e = counts/(T k), P_e = mean_t p[t,e], aux = E sum f P, z = mean (lse z)^2,
+# drop = dropped/(T k).
+
+def test_router_stats_uniform_and_balanced_closed_forms():
+    T, E, k = 37, 6, 2
+    # all logits equal: P_e = 1/E, so aux = sum_e f_e = 1 whatever the counts;
+    # logsumexp = c + log E
+    z = np.full((T, E), 0.75, np.float32)
+    counts = np.array([20, 0, 30, 4, 10, 10], np.int32)
+    st = oracle.router_stats(z, counts, T * k, k)
+    assert np.allclose(st["mean_prob"], 1.0 / E, rtol=0, atol=1e-15)
+    assert abs(st["aux"] - 1.0) < 1e-14
+    assert abs(st["z_loss"] - (0.75 + math.log(E)) ** 2) < 1e-12
+    assert st["drop_rate"] == 0.0
+    # perfectly balanced counts: f_e = 1/E, so aux = sum_e P_e = 1 for any logits
+    T = 36
+    z = RNG.standard_normal((T, E)).astype(np.float32) * 3
+    bal = oracle.router_stats(z, np.full(E, T * k // E, np.int32), T * k, k)
+    assert abs(bal["aux"] - 1.0) < 1e-13
+
+
+def test_router_stats_against_library_routines():
+    T, E, k = 53, 7, 3
+    z = (RNG.standard_normal((T, E)) * 2).astype(np.float32)
+    idx, _w = oracle.route(z, k)
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    st = oracle.router_stats(z, counts, T * k - 5, k)
+    p = scipy.special.softmax(z.astype(np.float64), axis=1)
+    lse = scipy.special.logsumexp(z.astype(np.float64), axis=1)
+    assert np.allclose(st["mean_prob"], p.mean(axis=0), rtol=1e-13, atol=0)
+    assert np.allclose(st["frac"], counts / (T * k), rtol=0, atol=1e-16)
+    assert abs(st["aux"] - E * np.dot(counts / (T * k), p.mean(axis=0))) < 1e-13
+    assert abs(st["z_loss"] - np.mean(lse ** 2)) < 1e-12 * max(1.0, np.mean(lse ** 2))
+    assert abs(st["drop_rate"] - 5 / (T * k)) < 1e-16
+    # invariants: both distributions sum to one
+    assert abs(st["mean_prob"].sum() - 1.0) < 1e-13 and abs(st["frac"].sum() - 1.0) < 1e-15
+
+
+def test_router_stats_normalised_probs_are_affine_invariant():
+    # standardisation removes any positive scale and shift of a token's logits,
+    # so the normalised mean probabilities do not move; the Z-loss (raw
+    # logits) shifts by the closed form lse(z + c) = lse(z) + c
+    T, E, k = 40, 9, 2
+    z = RNG.standard_normal((T, E)).astype(np.float32)
+    counts = np.full(E, 1, np.int32)
+    a = oracle.router_stats(z, counts, T * k, k, True, 1.0)
+    z2 = (z * np.float32(4.0) + np.float32(2.0)).astype(np.float32)
+    b = oracle.router_stats(z2, counts, T * k, k, True, 1.0)
+    assert np.allclose(a["mean_prob"], b["mean_prob"], rtol=1e-6)
+    c = 3.0
+    zs = (z.astype(np.float64) + c).astype(np.float32)
+    lse = scipy.special.logsumexp(zs.astype(np.float64), axis=1)
+    assert abs(oracle.router_stats(zs, counts, T * k, k)["z_loss"] - np.mean(lse ** 2)) < 1e-12 * np.mean(lse ** 2)
+    # lambda sharpens: the top expert's mean probability grows with lambda
+    lo = oracle.router_stats(z, counts, T * k, k, True, 0.5)["mean_prob"]
+    hi = oracle.router_stats(z, counts, T * k, k, True, 2.0)["mean_prob"]
+    p_lo = np.array([oracle.gate_probs(z[t], True, 0.5) for t in range(T)])
+    assert np.allclose(lo, p_lo.mean(axis=0), rtol=1e-13)
+    assert abs(hi.sum() - 1) < 1e-13 and not np.allclose(lo, hi)
+
+
+def test_router_stats_drop_rate_matches_dispatch():
+    T, E, k = 300, 8, 2
+    z = (RNG.standard_normal((T, E)) + np.linspace(2, 0, E)).astype(np.float32)
+    idx, _ = oracle.route(z, k)
+    C = oracle.capacity(T, E, k, 0.5)
+    disp = oracle.dispatch(idx, E, C)
+    st = oracle.router_stats(z, disp["counts"], disp["P"], k)
+    dropped = int((disp["slot"] < 0).sum())
+    assert dropped > 0 and abs(st["drop_rate"] - dropped / (T * k)) < 1e-16
+    # f is measured before the clip: a hot expert's share exceeds C / (T k)
+    assert st["frac"].max() > C / (T * k)
+
+
+# ---------------------------------------------------------------- shared expert
+# DeepSeekMoE-style shared expert (industry overview page, "MoE未來重點研究方向"
+# item 4): an expert every token goes through, added with weight one.
+
+@pytest.mark.parametrize("act", [oracle.RELU, oracle.SWIGLU])
+def test_shared_expert_identity_weights_closed_form(act):
+    T, d = 23, 64
+    x = RNG.standard_normal((T, d)).astype(np.float32)
+    eye = np.eye(d, dtype=np.float32)
+    Ws1 = eye if act == oracle.RELU else np.concatenate([eye, eye])
+    ys = oracle.shared_expert(x, Ws1, eye, act, d)
+    xf = x.astype(np.float64)
+    ref = np.maximum(xf, 0) if act == oracle.RELU else xf * scipy.special.expit(xf) * xf
+    assert np.allclose(ys, ref, rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("act", [oracle.RELU, oracle.SWIGLU])
+def test_shared_expert_is_dense_ffn_and_adds_unweighted(act):
+    T, d, F, E, k = 31, 64, 128, 5, 2
+    n1 = 2 * F if act == oracle.SWIGLU else F
+    x = moe_inputs.f32_to_bf16_bits(RNG.standard_normal((T, d)).astype(np.float32))
+    Ws1 = moe_inputs.f32_to_bf16_bits((RNG.standard_normal((n1, d)) * 0.1).astype(np.float32))
+    Ws2 = moe_inputs.f32_to_bf16_bits((RNG.standard_normal((d, F)) * 0.1).astype(np.float32))
+    ys = oracle.shared_expert(x, Ws1, Ws2, act, F)
+    ref = dense_ffn(oracle.to_f64(x), oracle.to_f64(Ws1), oracle.to_f64(Ws2), act, F)
+    assert np.allclose(ys, ref, rtol=1e-12, atol=1e-12)
+    # the combine adds it with weight one on top of the routed mix
+    W1 = moe_inputs.f32_to_bf16_bits((RNG.standard_normal((E, n1, d)) * 0.1).astype(np.float32))
+    W2 = moe_inputs.f32_to_bf16_bits((RNG.standard_normal((E, d, F)) * 0.1).astype(np.float32))
+    z = RNG.standard_normal((T, E)).astype(np.float32)
+    idx, w = oracle.route(z, k)
+    disp = oracle.dispatch(idx, E, oracle.capacity(T, E, k, 0.7))
+    yp = oracle.ffn_rows(x[disp["src_token"]], disp["offsets"], W1, W2, act, F).astype(np.float32)
+    routed = oracle.combine(yp, disp["slot"], w, T)
+    both = oracle.combine_shared(yp, disp["slot"], w, ys)
+    assert np.array_equal(both, ys + routed)
+    # a token whose choices were all dropped still gets the shared expert
+    gone = np.all(disp["slot"] < 0, axis=1)
+    if gone.any():
+        assert np.array_equal(both[gone], ys[gone])
+    # zero shared weights leave the routed layer
+    zero = oracle.shared_expert(x, Ws1, np.zeros_like(Ws2), act, F)
+    assert not zero.any()
