@@ -16,6 +16,11 @@
  *   moe_grouped_ffn  moe_expert_up then moe_expert_down
  *   moe_combine      gate-weighted un-permute back to token order
  *   moe_forward      all of the above
+ *   moe_router_stats balancing statistics of a routed batch (aux / Z-loss
+ *                    inputs, drop rate)
+ *   moe_shared_expert, moe_combine_shared
+ *                    an ungated shared expert over all tokens, added in the
+ *                    combine
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -190,6 +195,45 @@ moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* 
 moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
                        const void* W2, void* y, float* logits, const moe_route_info* info, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* Router by-products (Megatron-Core page, "MoE负载均衡的挑战与应对": an
+ * auxiliary loss pushes experts towards equal token counts, "关键特性":
+ * Z-Loss; Skywork-MoE news item, "技术创新 2. 自适应的Aux Loss", and slides,
+ * slide 7: the loss coefficient follows the token drop rate).  The pages give
+ * no formulas; these are the plainest readings:
+ *   frac[e]      = counts[e] / (T k)          (share of the assignments)
+ *   mean_prob[e] = (1/T) sum_t p[t,e]         (p as in moe_route, after the
+ *                                              optional normalisation)
+ *   scalars[0]   = E * sum_e frac[e] mean_prob[e]   (auxiliary loss, without
+ *                                                    its coefficient)
+ *   scalars[1]   = (1/T) sum_t (log sum_e exp logits[t,e])^2   (Z-loss)
+ *   scalars[2]   = (T k - offsets[E]) / (T k)                   (drop rate)
+ * logits [T][E] fp32 are the ones the routing used; counts [E] and offsets
+ * [E+1] come from moe_permute.  Sums in fp64 in a fixed order (the same bits
+ * on every run), outputs fp32: frac [E], mean_prob [E], scalars [3].  Needs
+ * ws_bytes >= moe_workspace_size. */
+moe_status moe_router_stats(const moe_problem* p, const float* logits, const int32_t* counts,
+                            const int32_t* offsets, float* frac, float* mean_prob, float* scalars, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Shared expert (industry overview page, "MoE未來重點研究方向" item 4:
+ * DeepSeekMoE's shared experts): one more two-layer MLP that every token
+ * passes through, ungated, with hidden width Fs (a multiple of 64 in
+ * [64, 65536]) and the problem's activation:
+ *   y_shared[t] = Ws2 act(Ws1 x[t])
+ * Ws1 [n1s][d] (n1s = Fs, or 2Fs for SwiGLU, gate rows first), Ws2 [d][Fs],
+ * x and y_shared [T][d], all dtype.  The hidden rows live in the workspace:
+ * ws_bytes >= moe_shared_workspace_size(p, Fs). */
+moe_status moe_shared_workspace_size(const moe_problem* p, int32_t Fs, size_t* bytes);
+moe_status moe_shared_expert(const moe_problem* p, int32_t Fs, const void* x, const void* Ws1, const void* Ws2,
+                             void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_combine with the shared expert's output added with weight one:
+ * y[t] = y_shared[t] + sum over kept j of topk_w[t,j] * y_perm[slot[t,j]]
+ * (fp32 accumulation starting from y_shared[t], j in order).  A token whose
+ * choices were all dropped gets y_shared[t]. */
+moe_status moe_combine_shared(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w,
+                              const void* y_shared, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,8 @@ loading fails loudly when the library has not been built.
 
 Entry points (same names as the C ABI): moe_capacity, moe_workspace_size,
 moe_route, moe_permute, moe_expert_up, moe_expert_down, moe_grouped_ffn,
-moe_combine, moe_forward.
+moe_combine, moe_forward, moe_router_stats, moe_shared_workspace_size,
+moe_shared_expert, moe_combine_shared.
 """
 from __future__ import annotations
 
@@ -22,7 +23,8 @@ MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_capacity", "moe_workspace_size", "moe_route",
-           "moe_permute", "moe_expert_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_forward")
+           "moe_permute", "moe_expert_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_forward",
+           "moe_router_stats", "moe_shared_workspace_size", "moe_shared_expert", "moe_combine_shared")
 
 
 class MoeError(RuntimeError):
@@ -69,8 +71,11 @@ def load() -> ctypes.CDLL:
     lib.moe_grouped_ffn.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_combine.argtypes = [PP, P, P, P, P, P]
     lib.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), P, ctypes.c_size_t, P]
-    for name in ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_up",
-                 "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_forward"):
+    lib.moe_router_stats.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_shared_workspace_size.argtypes = [PP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_shared_expert.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_combine_shared.argtypes = [PP, P, P, P, P, P, P]
+    for name in EXPORTS[2:]:
         getattr(lib, name).restype = st
     _lib = lib
     return lib
@@ -172,3 +177,25 @@ def moe_forward(p, x, Wg, bg, W1, W2, y, logits=None, info=None, ws=None, stream
     _check(load().moe_forward(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(y),
                               _ptr(logits), ctypes.byref(ri) if ri is not None else None, _ptr(ws), _nbytes(ws),
                               _stream(stream)))
+
+
+def moe_router_stats(p, logits, counts, offsets, frac, mean_prob, scalars, ws, stream=None):
+    """scalars [3] = (aux loss without coefficient, Z-loss, drop rate)."""
+    _check(load().moe_router_stats(ctypes.byref(p), _ptr(logits), _ptr(counts), _ptr(offsets), _ptr(frac),
+                                   _ptr(mean_prob), _ptr(scalars), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_shared_workspace_size(p, Fs) -> int:
+    n = ctypes.c_size_t()
+    _check(load().moe_shared_workspace_size(ctypes.byref(p), int(Fs), ctypes.byref(n)))
+    return n.value
+
+
+def moe_shared_expert(p, Fs, x, Ws1, Ws2, y_shared, ws, stream=None):
+    _check(load().moe_shared_expert(ctypes.byref(p), int(Fs), _ptr(x), _ptr(Ws1), _ptr(Ws2), _ptr(y_shared),
+                                    _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_combine_shared(p, y_perm, slot, topk_w, y_shared, y, stream=None):
+    _check(load().moe_combine_shared(ctypes.byref(p), _ptr(y_perm), _ptr(slot), _ptr(topk_w), _ptr(y_shared),
+                                     _ptr(y), _stream(stream)))

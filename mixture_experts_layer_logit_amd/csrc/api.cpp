@@ -24,8 +24,12 @@ hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const int3
                                    const void* W, void* C, const int32_t* offsets, int E, int K, int Nw, int Nout,
                                    int F, int max_rows, int mean_rows, int ncu, float* partial, hipStream_t stream);
 size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows);
-hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w, int T, int d,
-                              int k, int max_rows, void* y, hipStream_t stream);
+hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w,
+                              const void* y_add, int T, int d, int k, int max_rows, void* y, hipStream_t stream);
+size_t moe_router_stats_partial_bytes(int T, int E);
+hipError_t moe_launch_router_stats(const float* logits, int T, int E, int k, int normalize, float lambda,
+                                   const int32_t* counts, const int32_t* offsets, double* partial, float* frac,
+                                   float* mean_prob, float* scalars, hipStream_t stream);
 }
 
 namespace {
@@ -129,7 +133,8 @@ bool gather_ok(const moe_problem* p)
 // Workspace layout of a problem: every piece 256-byte aligned.  x_perm is
 // only there (non-zero size) when x is too large to gather from directly.
 struct Layout {
-    size_t topk_idx, topk_w, counts, offsets, slot, src_token, chunk_cnt, logits, partial, h, y_perm, x_perm, total;
+    size_t topk_idx, topk_w, counts, offsets, slot, src_token, chunk_cnt, logits, stats, partial, h, y_perm, x_perm,
+        total;
 };
 
 int mean_rows_of(const moe_problem* p);
@@ -156,6 +161,7 @@ Layout layout_of(const moe_problem* p)
     L.src_token = take(T * k * 4);
     L.chunk_cnt = take(std::max<size_t>(nchunks, 1) * E * 4);
     L.logits = take(T * E * 4);
+    L.stats = take(moe_router_stats_partial_bytes(p->T, p->E));
     L.partial = take(moe_grouped_gemm_partial_bytes(p->dtype, mean_rows_of(p)));
     L.h = take(T * k * F * b);
     L.y_perm = take(T * k * d * b);
@@ -252,10 +258,39 @@ moe_status do_down(const moe_problem* p, const void* h, const int32_t* offsets, 
                       "expert down launch");
 }
 
-moe_status do_combine(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w, void* y,
-                      hipStream_t s)
+moe_status do_combine(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w,
+                      const void* y_add, void* y, hipStream_t s)
 {
-    return hip_status(moe_launch_combine(p->dtype, y_perm, slot, topk_w, p->T, p->d, p->k, p->T * p->k, y, s), "combine launch");
+    return hip_status(moe_launch_combine(p->dtype, y_perm, slot, topk_w, y_add, p->T, p->d, p->k, p->T * p->k, y, s),
+                      "combine launch");
+}
+
+// ---- shared expert: a dense expert FFN over all T rows (E = 1, no offsets)
+moe_status check_shared(const moe_problem* p, int32_t Fs)
+{
+    CHECK(check_problem(p));
+    if (Fs < 64 || Fs > kMaxDim || Fs % 64)
+        return fail(MOE_ERR_UNSUPPORTED, "Fs=%d must be a multiple of 64 in [64, %d]", Fs, kMaxDim);
+    const long long n1s = p->act == MOE_ACT_SWIGLU ? 2LL * Fs : Fs;
+    if ((long long)p->T * std::max<long long>(n1s, p->d) >= (1LL << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "problem too large");
+    if (n1s * p->d * (long long)elem_bytes(p) >= (1LL << 31) ||
+        (long long)p->d * Fs * (long long)elem_bytes(p) >= (1LL << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "the shared expert's weights must stay below 2 GiB");
+    return MOE_OK;
+}
+
+struct SharedLayout {
+    size_t h, partial, total;
+};
+
+SharedLayout shared_layout_of(const moe_problem* p, int32_t Fs)
+{
+    SharedLayout L;
+    L.h = 0;
+    L.partial = round_up((size_t)p->T * Fs * elem_bytes(p));
+    L.total = L.partial + round_up(moe_grouped_gemm_partial_bytes(p->dtype, p->T));
+    return L;
 }
 
 }  // namespace
@@ -407,7 +442,7 @@ moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* 
     CHECK(check_ptr(slot, "slot", 4));
     CHECK(check_ptr(topk_w, "topk_w", 4));
     CHECK(check_ptr(y, "y", 16));
-    CHECK(do_combine(p, y_perm, slot, topk_w, y, (hipStream_t)stream));
+    CHECK(do_combine(p, y_perm, slot, topk_w, nullptr, y, (hipStream_t)stream));
     return ok();
 }
 
@@ -466,7 +501,80 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, cons
         CHECK(do_up(p, x_perm, nullptr, offsets, W1, h, partial, s));
     }
     CHECK(do_down(p, h, offsets, W2, y_perm, partial, s));
-    CHECK(do_combine(p, y_perm, slot, topk_w, y, s));
+    CHECK(do_combine(p, y_perm, slot, topk_w, nullptr, y, s));
+    return ok();
+}
+
+moe_status moe_router_stats(const moe_problem* p, const float* logits, const int32_t* counts,
+                            const int32_t* offsets, float* frac, float* mean_prob, float* scalars, void* ws,
+                            size_t ws_bytes, void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(logits, "logits", 4));
+    CHECK(check_ptr(counts, "counts", 4));
+    CHECK(check_ptr(offsets, "offsets", 4));
+    CHECK(check_ptr(frac, "frac", 4));
+    CHECK(check_ptr(mean_prob, "mean_prob", 4));
+    CHECK(check_ptr(scalars, "scalars", 4));
+    CHECK(check_ws(p, ws, ws_bytes));
+    double* partial = at<double>(ws, layout_of(p).stats);
+    CHECK(hip_status(moe_launch_router_stats(logits, p->T, p->E, p->k, p->normalize, p->lambda, counts, offsets,
+                                             partial, frac, mean_prob, scalars, (hipStream_t)stream),
+                     "router statistics launch"));
+    return ok();
+}
+
+moe_status moe_shared_workspace_size(const moe_problem* p, int32_t Fs, size_t* bytes)
+{
+    CHECK(check_shared(p, Fs));
+    if (!bytes)
+        return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = shared_layout_of(p, Fs).total;
+    return ok();
+}
+
+moe_status moe_shared_expert(const moe_problem* p, int32_t Fs, const void* x, const void* Ws1, const void* Ws2,
+                             void* y_shared, void* ws, size_t ws_bytes, void* stream)
+{
+    CHECK(check_shared(p, Fs));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(x, "x", 16));
+    CHECK(check_ptr(Ws1, "Ws1", 16));
+    CHECK(check_ptr(Ws2, "Ws2", 16));
+    CHECK(check_ptr(y_shared, "y_shared", 16));
+    const SharedLayout L = shared_layout_of(p, Fs);
+    if (ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, L.total);
+    CHECK(check_ptr(ws, "ws", 16));
+    void* h = at<char>(ws, L.h);
+    float* partial = at<float>(ws, L.partial);
+    const int epi = p->act == MOE_ACT_SWIGLU ? 2 : 1;
+    const int n1s = p->act == MOE_ACT_SWIGLU ? 2 * Fs : Fs;
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, epi, x, nullptr, 0, Ws1, h, nullptr, 1, p->d, n1s, Fs, Fs,
+                                             p->T, p->T, cu_count(), partial, s),
+                     "shared expert up launch"));
+    CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, 0, h, nullptr, 0, Ws2, y_shared, nullptr, 1, Fs, p->d, p->d,
+                                             Fs, p->T, p->T, cu_count(), partial, s),
+                     "shared expert down launch"));
+    return ok();
+}
+
+moe_status moe_combine_shared(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w,
+                              const void* y_shared, void* y, void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(y_perm, "y_perm", 16));
+    CHECK(check_ptr(slot, "slot", 4));
+    CHECK(check_ptr(topk_w, "topk_w", 4));
+    CHECK(check_ptr(y_shared, "y_shared", 16));
+    CHECK(check_ptr(y, "y", 16));
+    CHECK(do_combine(p, y_perm, slot, topk_w, y_shared, y, (hipStream_t)stream));
     return ok();
 }
 

@@ -8,7 +8,10 @@
 // reads the row y_perm[slot] with 16-byte loads and accumulates
 // topk_w[t,j] * row in fp32 (fma, fixed order, so results are reproducible),
 // then writes y[t] once.  Each lane owns up to 8 16-byte vectors per pass.
-// Slots at or past the row count (T*k) are treated as dropped.
+// Slots at or past the row count (T*k) are treated as dropped.  With y_add
+// (the shared expert's output, industry overview page, "MoE未來重點研究方向"
+// item 4: DeepSeekMoE's shared experts) the sum starts from y_add[t]: every
+// token gets it with weight one.
 #include "common.h"
 
 namespace moe {
@@ -16,8 +19,10 @@ namespace moe {
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::storage* __restrict__ y_perm,
                                                           const int32_t* __restrict__ slot,
-                                                          const float* __restrict__ topk_w, int T, int d, int k,
-                                                          int max_rows, typename ET::storage* __restrict__ y)
+                                                          const float* __restrict__ topk_w,
+                                                          const typename ET::storage* __restrict__ y_add, int T,
+                                                          int d, int k, int max_rows,
+                                                          typename ET::storage* __restrict__ y)
 {
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -41,6 +46,24 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::sto
 #pragma unroll
             for (int q = 0; q < kPer; ++q)
                 acc[u][q] = 0.0f;
+        if (y_add) {
+            const uint4* src = reinterpret_cast<const uint4*>(y_add + (size_t)t * d);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int v = v0 + u * kWave + lane;
+                if (v < nvec) {
+                    const uint4 raw = src[v];
+                    if constexpr (ET::kBytes == 2) {
+                        unpack8(raw, acc[u], bf16_t{});
+                    } else {
+                        acc[u][0] = __uint_as_float(raw.x);
+                        acc[u][1] = __uint_as_float(raw.y);
+                        acc[u][2] = __uint_as_float(raw.z);
+                        acc[u][3] = __uint_as_float(raw.w);
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if (rows[j] < 0)
@@ -91,16 +114,19 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::sto
 
 }  // namespace moe
 
+// y_add (nullable): added to every token's sum with weight one.
 extern "C" hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w,
-                                         int T, int d, int k, int max_rows, void* y, hipStream_t stream)
+                                         const void* y_add, int T, int d, int k, int max_rows, void* y,
+                                         hipStream_t stream)
 {
     using namespace moe;
     const dim3 grid((T + 3) / 4), block(256);
     if (dtype == 0)
-        moe_combine_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)y_perm, slot, topk_w, T, d, k, max_rows,
-                                                              (float*)y);
+        moe_combine_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)y_perm, slot, topk_w,
+                                                              (const float*)y_add, T, d, k, max_rows, (float*)y);
     else
-        moe_combine_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)y_perm, slot, topk_w, T, d, k,
-                                                               max_rows, (uint16_t*)y);
+        moe_combine_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)y_perm, slot, topk_w,
+                                                               (const uint16_t*)y_add, T, d, k, max_rows,
+                                                               (uint16_t*)y);
     return hipGetLastError();
 }

@@ -9,7 +9,8 @@
 //
 //   up:    C[r, n] = act( sum_k A[r, k] * W[e, n, k] )   A = x_perm, W = W1
 //   down:  C[r, n] =      sum_k A[r, k] * W[e, n, k]     A = h,      W = W2
-// for every expert e and row r in [offsets[e], offsets[e+1]).  Both operands
+// for every expert e and row r in [offsets[e], offsets[e+1]) (or, without
+// offsets, one weight matrix over all rows: the shared expert).  Both operands
 // have K contiguous ("X W^T"), fp32 accumulation, output stored in the input
 // type.  SwiGLU: C[r, f] = silu(u_f) * u_{F+f}, silu(g) = g / (1 + exp(-g)).
 // With a gather index, A row r is read from row gather[r] of A (the up
@@ -30,7 +31,7 @@
 //    fixed order and applies the epilogue (deterministic, no atomics).
 //  * Block tile BM x BN, K in 128-byte slices (64 bf16 / 32 fp32), loaded
 //    straight from memory into LDS (buffer_load ... lds: no staging
-//    registers), double-buffered, one barrier per slice.  Each wave load
+//    registers) through a ring of S LDS stages, one barrier per slice.  Each wave load
 //    fills a contiguous 1 KB LDS block (8 rows); the 16-byte chunks of an LDS
 //    row are XOR-swizzled (see swz) by choosing which chunk each lane fetches,
 //    so the MFMA operand reads hit every LDS bank once.
@@ -82,7 +83,7 @@ struct GemmShape {
     static_assert(BM % (kRowsPerBlk * kWaves) == 0 && BN % (kRowsPerBlk * kWaves) == 0,
                   "DMA blocks must split evenly across waves");
     static_assert(S >= 2 && S <= 4, "2 to 4 stages");
-    static_assert((S - 2) * kLoads <= 63, "vmcnt range");
+    static_assert((S - 1) * kLoads <= 63, "vmcnt range");
     static_assert(kWaves % 2 == 0, "block parity must be fixed per wave");
 };
 
@@ -101,9 +102,15 @@ __device__ __forceinline__ uint32_t swz(int row, int c)
 
 // Rows of expert e, with the offsets clamped into [0, max_rows] and made
 // non-decreasing, so that no offsets array can send a tile out of bounds.
+// offsets == NULL: one segment of all max_rows rows (a dense layer, E = 1).
 __device__ __forceinline__ void seg_bounds(const int32_t* __restrict__ offsets, int e, int max_rows, int& lo,
                                            int& rows)
 {
+    if (offsets == nullptr) {
+        lo = 0;
+        rows = max_rows;
+        return;
+    }
     lo = min(max(offsets[e], 0), max_rows);
     const int hi = min(max(offsets[e + 1], lo), max_rows);
     rows = hi - lo;
@@ -219,18 +226,25 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes)
     return r;
 }
 
+// Byte address of a shared-memory object in the LDS address space.
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
 // 16 bytes per lane from buffer `rsrc` at voff + soff straight into LDS at
-// lds + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base).
+// byte address lds + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the
+// LDS base).
 // Issued from asm so that the compiler does not track the LDS writes: they
 // are ordered by the kernel's own vmcnt waits and barriers (the compiler
 // would otherwise make LDS reads wait for all loads in flight).  The
 // instruction has no destination register; its address operands are read at
 // issue.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, const uint8_t* lds, uint32_t voff, uint32_t soff)
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds, uint32_t voff, uint32_t soff)
 {
     // scalar operands: wave-uniform by construction; readfirstlane makes the
     // compiler place them in SGPRs (and keeps the offset off the immediate field)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     uint32_t so = __builtin_amdgcn_readfirstlane(soff);
     __asm__("" : "+s"(so));
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -264,6 +278,13 @@ __device__ __forceinline__ void wait_vmcnt()
 template <typename S>
 struct Acc {
     f32x16 v[S::kFM][S::kFN];
+};
+
+// One k-step's MFMA operands of a wave: 16 bytes per lane of each of its
+// kFN weight blocks (a) and kFM activation blocks (b).
+template <typename S>
+struct Frag {
+    uint4 a[S::kFN], b[S::kFM];
 };
 
 // Epilogue: activation and store of a tile from the wave's accumulators.
@@ -343,9 +364,21 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: keeps DMA bases scalar
     const int wm = wave / S::WN, wn = wave % S::WN;
     const uint32_t rowK = (uint32_t)K * ET::kBytes;  // bytes of one row
+    // LDS byte addresses of the stages
+    const uint32_t stage_addr[4] = {lds_addr(lds0), lds_addr(lds1), lds_addr(lds2), lds_addr(lds3)};
+    // per-lane LDS read offsets of each k-step's first 32-row block; blocks
+    // 32 rows apart keep the same swizzle term, so the others sit at fixed
+    // offsets from these
+    uint32_t rdA[S::kKSteps], rdB[S::kKSteps];
+#pragma unroll
+    for (int kk = 0; kk < S::kKSteps; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        rdA[kk] = swz<S>(wm * S::kWaveM + (lane & 31), c);
+        rdB[kk] = S::kLdsA + swz<S>(wn * S::kWaveN + (lane & 31), c);
+    }
     // lane's place inside a 1 KB DMA block of rows [R0, R0 + 1024/RB): row
     // R0 + lane / kNch, physical chunk lane % kNch, which holds the logical
     // chunk of swz().  The swizzle term depends on the block only through the
@@ -420,14 +453,15 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             voffB[i] = (uint32_t)(wrow + lrow) * rowK + lane_chunk;
         }
 
-        auto issue = [&](int kt, uint8_t* dst) {
+        auto issue = [&](int kt, int stage) {
             const uint32_t soff = (uint32_t)kt * S::RB;
+            const uint32_t dst = stage_addr[stage] + wave * 1024;
 #pragma unroll
             for (int i = 0; i < S::kBlkA; ++i)
-                dma16(rsA, dst + (wave + kWaves * i) * 1024, voffA[i], soff);
+                dma16(rsA, dst + kWaves * i * 1024, voffA[i], soff);
 #pragma unroll
             for (int i = 0; i < S::kBlkB; ++i)
-                dma16(rsW, dst + S::kLdsA + (wave + kWaves * i) * 1024, voffB[i], soff);
+                dma16(rsW, dst + S::kLdsA + kWaves * i * 1024, voffB[i], soff);
         };
 
         Acc<S> acc;
@@ -439,98 +473,122 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 for (int v = 0; v < 16; ++v)
                     acc.v[i][j][v] = 0.0f;
 
-        // Wait until at most n slices of this wave's loads are in flight.
+        // Wait until at most n (< S) slices of this wave's loads are in flight.
         auto wait_slices = [&](int n) {
-            if (S::S >= 4 && n >= 2)
-                wait_vmcnt<(S::S >= 4 ? 2 : 0) * S::kLoads>();
-            else if (S::S >= 3 && n >= 1)
-                wait_vmcnt<(S::S >= 3 ? 1 : 0) * S::kLoads>();
+            if (S::S >= 4 && n >= 3)
+                wait_vmcnt<(S::S >= 4 ? 3 : 0) * S::kLoads>();
+            else if (S::S >= 3 && n >= 2)
+                wait_vmcnt<(S::S >= 3 ? 2 : 0) * S::kLoads>();
+            else if (n >= 1)
+                wait_vmcnt<S::kLoads>();
             else
                 wait_vmcnt<0>();
         };
 
-        // One K slice kt held in `cur`: wait for it (later slices may stay in
-        // flight), meet the other waves (they have finished slice kt-1, so its
-        // buffer `nxt` is free), start loading slice kt+S-1 into `nxt`, then
-        // multiply.  Buffers are distinct LDS arrays known at compile time.
-        auto slice = [&](int kt, const uint8_t* cur, uint8_t* nxt) {
-            wait_slices(min(S::S - 2, k1 - 1 - kt));
-            lds_barrier();
-            if (kt + S::S - 1 < k1)
-                issue(kt + S::S - 1, nxt);
-            const uint8_t* bufA = cur;
-            const uint8_t* bufB = cur + S::kLdsA;
+        // MFMA operand fragments of one k-step, double-buffered in registers
+        // so that a k-step's LDS reads can be issued before the previous
+        // k-step's MFMAs.
+        Frag<S> fr0, fr1;
+        auto read_frags = [&](const uint8_t* buf, int kk, Frag<S>& f) {
 #pragma unroll
-            for (int kk = 0; kk < S::kKSteps; ++kk) {
-                const int c = 2 * kk + (lane >> 5);
-                uint4 fa[S::kFN], fb[S::kFM];
+            for (int j = 0; j < S::kFN; ++j)
+                f.a[j] = *reinterpret_cast<const uint4*>(buf + rdB[kk] + j * 32 * S::RB);
 #pragma unroll
-                for (int j = 0; j < S::kFN; ++j)
-                    fa[j] = *reinterpret_cast<const uint4*>(bufB +
-                                                            swz<S>(wn * S::kWaveN + j * 32 + (lane & 31), c));
-#pragma unroll
-                for (int i = 0; i < S::kFM; ++i)
-                    fb[i] = *reinterpret_cast<const uint4*>(bufA +
-                                                            swz<S>(wm * S::kWaveM + i * 32 + (lane & 31), c));
-#pragma unroll
-                for (int i = 0; i < S::kFM; ++i)
-#pragma unroll
-                    for (int j = 0; j < S::kFN; ++j) {
-                        if constexpr (ET::kBytes == 2) {
-                            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8, fa[j]), __builtin_bit_cast(bf16x8, fb[i]), acc.v[i][j],
-                                0, 0, 0);
-                        } else {
-                            const f32x4 va = __builtin_bit_cast(f32x4, fa[j]);
-                            const f32x4 vb = __builtin_bit_cast(f32x4, fb[i]);
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                acc.v[i][j] =
-                                    __builtin_amdgcn_mfma_f32_32x32x2f32(va[q], vb[q], acc.v[i][j], 0, 0, 0);
-                        }
-                    }
-            }
+            for (int i = 0; i < S::kFM; ++i)
+                f.b[i] = *reinterpret_cast<const uint4*>(buf + rdA[kk] + i * 32 * S::RB);
         };
+        auto mfmas = [&](const Frag<S>& f) {
+#pragma unroll
+            for (int i = 0; i < S::kFM; ++i)
+#pragma unroll
+                for (int j = 0; j < S::kFN; ++j) {
+                    if constexpr (ET::kBytes == 2) {
+                        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, f.a[j]), __builtin_bit_cast(bf16x8, f.b[i]), acc.v[i][j],
+                            0, 0, 0);
+                    } else {
+                        const f32x4 va = __builtin_bit_cast(f32x4, f.a[j]);
+                        const f32x4 vb = __builtin_bit_cast(f32x4, f.b[i]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[q], vb[q], acc.v[i][j], 0, 0, 0);
+                    }
+                }
+        };
+        // One K slice kt held in `cur` (stage cur_stage), whose first k-step
+        // fragments are already in fr0.  Each k-step reads the next one's
+        // fragments, then runs its MFMAs.  Before the last k-step's MFMAs the
+        // slice boundary is crossed: wait for this wave's loads of slice
+        // kt+1, meet the other waves (after which slice kt+1 is in LDS
+        // everywhere and every wave's reads of `cur` are done), start loading
+        // slice kt+S into `cur`, and read slice kt+1's first fragments from
+        // `nxt`, so that the barrier and that LDS latency are hidden behind
+        // the last k-step's MFMAs.  Buffers are distinct LDS arrays known at
+        // compile time.
+        static_assert(S::kKSteps == 2 || S::kKSteps == 4, "2 or 4 k-steps per slice");
+        auto slice = [&](int kt, const uint8_t* cur, int cur_stage, const uint8_t* nxt) {
+            read_frags(cur, 1, fr1);
+            mfmas(fr0);
+            if constexpr (S::kKSteps == 4) {
+                read_frags(cur, 2, fr0);
+                mfmas(fr1);
+                read_frags(cur, 3, fr1);
+                mfmas(fr0);
+            }
+            if (kt + 1 < k1) {
+                wait_slices(min(S::S - 2, k1 - 2 - kt));
+                lds_barrier();
+                if (kt + S::S < k1)
+                    issue(kt + S::S, cur_stage);
+                read_frags(nxt, 0, fr0);
+            }
+            mfmas(fr1);
+        };
+        static_assert(S::kKSteps % 2 == 0, "k-steps per slice must be even");
 
         wait_vmcnt<0>();  // the previous tile's stores are out of the vmcnt count
         __syncthreads();  // every wave is done with the previous tile's buffers
+        // fill the ring: slices k0 .. k0+S-1, then wait for the first
 #pragma unroll
-        for (int s0 = 0; s0 < S::S - 1; ++s0) {
+        for (int s0 = 0; s0 < S::S; ++s0) {
             if (k0 + s0 < k1)
-                issue(k0 + s0, s0 == 0 ? lds0 : s0 == 1 ? lds1 : lds2);
+                issue(k0 + s0, s0);
         }
+        wait_slices(min(S::S - 1, k1 - 1 - k0));
+        lds_barrier();
+        read_frags(lds0, 0, fr0);
         // slice k0 + n uses buffer n mod S
         int kt = k0;
         if constexpr (S::S == 2) {
             for (; kt + 2 <= k1; kt += 2) {
-                slice(kt, lds0, lds1);
-                slice(kt + 1, lds1, lds0);
+                slice(kt, lds0, 0, lds1);
+                slice(kt + 1, lds1, 1, lds0);
             }
             if (kt < k1)
-                slice(kt, lds0, lds1);
+                slice(kt, lds0, 0, lds1);
         } else if constexpr (S::S == 3) {
             for (; kt + 3 <= k1; kt += 3) {
-                slice(kt, lds0, lds2);
-                slice(kt + 1, lds1, lds0);
-                slice(kt + 2, lds2, lds1);
+                slice(kt, lds0, 0, lds1);
+                slice(kt + 1, lds1, 1, lds2);
+                slice(kt + 2, lds2, 2, lds0);
             }
             if (kt < k1)
-                slice(kt, lds0, lds2);
+                slice(kt, lds0, 0, lds1);
             if (kt + 1 < k1)
-                slice(kt + 1, lds1, lds0);
+                slice(kt + 1, lds1, 1, lds2);
         } else {
             for (; kt + 4 <= k1; kt += 4) {
-                slice(kt, lds0, lds3);
-                slice(kt + 1, lds1, lds0);
-                slice(kt + 2, lds2, lds1);
-                slice(kt + 3, lds3, lds2);
+                slice(kt, lds0, 0, lds1);
+                slice(kt + 1, lds1, 1, lds2);
+                slice(kt + 2, lds2, 2, lds3);
+                slice(kt + 3, lds3, 3, lds0);
             }
             if (kt < k1)
-                slice(kt, lds0, lds3);
+                slice(kt, lds0, 0, lds1);
             if (kt + 1 < k1)
-                slice(kt + 1, lds1, lds0);
+                slice(kt + 1, lds1, 1, lds2);
             if (kt + 2 < k1)
-                slice(kt + 2, lds2, lds1);
+                slice(kt + 2, lds2, 2, lds3);
         }
 
         if (slot < 0) {

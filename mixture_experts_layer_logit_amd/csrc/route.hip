@@ -146,26 +146,14 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return v;
 }
 
+// Gate probabilities of one token held by a wavefront: z[i] is the logit of
+// expert lane + 64 i (0 past E).  Scores s in fp64 are the logit, or
+// lambda * (z - mu) / sigma (population sigma over the E experts; sigma == 0
+// gives s = 0); p_e = ex[i] / denom with ex = exp(s - max s).
 template <int VPL>
-__global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                         int normalize, float lambda,
-                                                         int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_w)
+__device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int E, int normalize, float lambda,
+                                            double (&ex)[VPL], double& denom)
 {
-    const int lane = lane_id();
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (t >= T)
-        return;
-    const float* zt = logits + (size_t)t * E;
-    float z[VPL];
-    uint64_t key[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
-        z[i] = e < E ? zt[e] : 0.0f;
-        key[i] = e < E ? ((uint64_t)ordered_key(z[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
-    }
-    // scores s (fp64): the logit, or lambda * (z - mu) / sigma
     double s[VPL];
     if (normalize) {
         double part = 0.0;
@@ -194,14 +182,36 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
         if (lane + kWave * i < E)
             m = fmax(m, s[i]);
     m = wave_max(m);
-    double ex[VPL];
     double part = 0.0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         ex[i] = (lane + kWave * i < E) ? exp(s[i] - m) : 0.0;
         part += ex[i];
     }
-    const double denom = wave_sum(part);
+    denom = wave_sum(part);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int normalize, float lambda,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w)
+{
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T)
+        return;
+    const float* zt = logits + (size_t)t * E;
+    float z[VPL];
+    uint64_t key[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        z[i] = e < E ? zt[e] : 0.0f;
+        key[i] = e < E ? ((uint64_t)ordered_key(z[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
+    }
+    double ex[VPL], denom;
+    token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
 
     for (int j = 0; j < k; ++j) {
         uint64_t best = 0;
@@ -225,6 +235,118 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
             topk_idx[(size_t)t * k + j] = e;
             topk_w[(size_t)t * k + j] = (float)pe;
         }
+    }
+}
+
+// ---------------------------------------------------------------- router by-products
+// Sums over tokens for the balancing statistics (Megatron-Core page, "MoE负载
+// 均衡的挑战与应对" and "关键特性": auxiliary loss, Z-Loss; Skywork news item,
+// "技术创新 2", and slides, slide 7: the drop-rate-driven coefficient).
+//
+// Pass 1: block b takes tokens b*4 + wave, stepping by 4 * gridDim.x; each
+// wavefront adds its tokens' gate probabilities (fp64, the same arithmetic as
+// the router) per expert and (logsumexp z)^2 of the raw logits; the block's
+// 4 wavefronts are added in wave order and stored as partial[b][0..E-1] and
+// partial[b][E].  Pass 2 adds the blocks in block order.  The grid depends
+// only on T, so the sums are the same on every run.
+constexpr int kStatsBlocks = 256;
+
+template <int VPL>
+__global__ __launch_bounds__(256) void moe_router_stats_kernel(const float* __restrict__ logits, int T, int E,
+                                                               int normalize, float lambda,
+                                                               double* __restrict__ partial)
+{
+    __shared__ double s_acc[4][VPL * kWave + 1];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    double psum[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        psum[i] = 0.0;
+    double zsum = 0.0;
+    for (int t = blockIdx.x * 4 + wave; t < T; t += 4 * gridDim.x) {
+        const float* zt = logits + (size_t)t * E;
+        float z[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int e = lane + kWave * i;
+            z[i] = e < E ? zt[e] : 0.0f;
+        }
+        double ex[VPL], denom;
+        token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            psum[i] += ex[i] / denom;
+        // logsumexp of the raw logits
+        double m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (lane + kWave * i < E)
+                m = fmax(m, (double)z[i]);
+        m = wave_max(m);
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            part += (lane + kWave * i < E) ? exp((double)z[i] - m) : 0.0;
+        const double lse = m + log(wave_sum(part));
+        zsum += lse * lse;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        s_acc[wave][lane + kWave * i] = psum[i];
+    if (lane == 0)
+        s_acc[wave][VPL * kWave] = zsum;
+    __syncthreads();
+    double* dst = partial + (size_t)blockIdx.x * (E + 1);
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        dst[e] = ((s_acc[0][e] + s_acc[1][e]) + s_acc[2][e]) + s_acc[3][e];
+    if (threadIdx.x == 0)
+        dst[E] = ((s_acc[0][VPL * kWave] + s_acc[1][VPL * kWave]) + s_acc[2][VPL * kWave]) + s_acc[3][VPL * kWave];
+}
+
+// Pass 2, one block of 1024 threads (thread e owns expert e):
+//   mean_prob[e] = sum_b partial[b][e] / T,  frac[e] = counts[e] / (T k),
+//   scalars = {E * sum_e frac[e] mean_prob[e], sum_b partial[b][E] / T,
+//              (T k - offsets[E]) / (T k)}
+// The sum over experts is a fixed tree (wavefront shuffles, then the 16
+// wavefronts in order).
+__global__ __launch_bounds__(1024) void moe_router_stats_final_kernel(const double* __restrict__ partial,
+                                                                      int nblocks, int T, int E, int k,
+                                                                      const int32_t* __restrict__ counts,
+                                                                      const int32_t* __restrict__ offsets,
+                                                                      float* __restrict__ frac,
+                                                                      float* __restrict__ mean_prob,
+                                                                      float* __restrict__ scalars)
+{
+    __shared__ double s_w[1024 / kWave];
+    const int e = threadIdx.x;
+    const double n = (double)T * (double)k;
+    double term = 0.0;
+    if (e < E) {
+        double s = 0.0;
+        for (int b = 0; b < nblocks; ++b)
+            s += partial[(size_t)b * (E + 1) + e];
+        const double mp = s / (double)T;
+        const double f = (double)counts[e] / n;
+        mean_prob[e] = (float)mp;
+        frac[e] = (float)f;
+        term = f * mp;
+    }
+    term = wave_sum(term);
+    if (lane_id() == 0)
+        s_w[threadIdx.x / kWave] = term;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double aux = 0.0;
+        for (int w = 0; w < 1024 / kWave; ++w)
+            aux += s_w[w];
+        double zs = 0.0;
+        for (int b = 0; b < nblocks; ++b)
+            zs += partial[(size_t)b * (E + 1) + E];
+        const int kept = min(max(offsets[E], 0), T * k);
+        scalars[0] = (float)((double)E * aux);
+        scalars[1] = (float)(zs / (double)T);
+        scalars[2] = (float)((n - (double)kept) / n);
     }
 }
 
@@ -261,5 +383,38 @@ extern "C" hipError_t moe_launch_router(const float* logits, int T, int E, int k
         moe_router_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
     else
         moe_router_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    return hipGetLastError();
+}
+
+// Workspace of the statistics' first pass, in bytes.
+extern "C" size_t moe_router_stats_partial_bytes(int T, int E)
+{
+    const int nb = T < 4 * moe::kStatsBlocks ? (T + 3) / 4 : moe::kStatsBlocks;
+    return (size_t)(nb > 0 ? nb : 1) * (E + 1) * sizeof(double);
+}
+
+extern "C" hipError_t moe_launch_router_stats(const float* logits, int T, int E, int k, int normalize, float lambda,
+                                              const int32_t* counts, const int32_t* offsets, double* partial,
+                                              float* frac, float* mean_prob, float* scalars, hipStream_t stream)
+{
+    using namespace moe;
+    const int nb = T < 4 * kStatsBlocks ? (T + 3) / 4 : kStatsBlocks;
+    const int vpl = (E + kWave - 1) / kWave;
+    const dim3 grid(nb), block(256);
+    if (vpl <= 1)
+        moe_router_stats_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, normalize, lambda, partial);
+    else if (vpl <= 2)
+        moe_router_stats_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, normalize, lambda, partial);
+    else if (vpl <= 4)
+        moe_router_stats_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, normalize, lambda, partial);
+    else if (vpl <= 8)
+        moe_router_stats_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, normalize, lambda, partial);
+    else
+        moe_router_stats_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, normalize, lambda, partial);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    moe_router_stats_final_kernel<<<1, 1024, 0, stream>>>(partial, nb, T, E, k, counts, offsets, frac, mean_prob,
+                                                           scalars);
     return hipGetLastError();
 }

@@ -57,7 +57,8 @@ def workspace_formula(T, d, E, k, F, b, cf=0.0):
     r = lambda n: (n + 255) // 256 * 256
     nch = max((T + 255) // 256, 1)
     gather = T * d * b < 0xF0000000  # else x_perm is kept in the workspace
-    return (r(T * k * 4) * 4 + r(E * 4) + r((E + 1) * 4) + r(nch * E * 4) + r(T * E * 4)
+    nstat = max((T + 3) // 4 if T < 1024 else 256, 1)  # blocks of the router statistics' first pass
+    return (r(T * k * 4) * 4 + r(E * 4) + r((E + 1) * 4) + r(nch * E * 4) + r(T * E * 4) + r(nstat * (E + 1) * 8)
             + r(256 * partial_floats(T, E, k, b, cf) * 4) + r(T * k * F * b) + r(T * k * d * b)
             + (0 if gather else r(T * k * d * b)))
 
@@ -150,3 +151,40 @@ def test_empty_problem_is_a_no_op():
     # T == 0: nothing to do, no pointer is touched
     assert lib.moe_forward(pp, None, None, None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
     assert lib.moe_route(pp, None, None, None, None, None, None, None) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("T,d,F,Fs,dt", [(4096, 4096, 14336, 1408, "bf16"), (100, 64, 64, 128, "f32"),
+                                         (600, 256, 448, 2048, "bf16")])
+def test_shared_workspace_size(T, d, F, Fs, dt):
+    p = moe.problem(T, d, 8, 2, F, dtype=dt)
+    b = 4 if dt == "f32" else 2
+    r = lambda n: (n + 255) // 256 * 256
+    # hidden rows [T][Fs], then the K-split partial tiles of a T-row segment
+    tile = 128 * 128 if b == 4 else 256 * 256 if T >= 512 else 128 * 128 if T >= 128 else 64 * 256
+    assert moe.moe_shared_workspace_size(p, Fs) == r(T * Fs * b) + r(256 * tile * 4)
+
+
+def test_new_entry_points_reject_bad_arguments():
+    p = moe.problem(64, 64, 8, 2, 64)
+    ws = moe.moe_workspace_size(p)
+    lib = moe.load()
+    pp = ctypes.byref(p)
+    # statistics: null output, short workspace
+    assert lib.moe_router_stats(pp, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_stats(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == moe.MOE_ERR_WORKSPACE
+    # shared expert: bad hidden width, short workspace, null weights
+    for Fs in (0, 96, 1 << 17):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_shared_workspace_size(p, Fs)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    sws = moe.moe_shared_workspace_size(p, 128)
+    assert lib.moe_shared_expert(pp, 128, FAKE, FAKE, FAKE, FAKE, FAKE, sws - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_shared_expert(pp, 128, FAKE, None, FAKE, FAKE, FAKE, sws, None) == moe.MOE_ERR_INVALID_ARG
+    # combine with a shared output: misaligned y_shared
+    assert lib.moe_combine_shared(pp, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # T == 0 is a no-op for all of them
+    p0 = moe.problem(0, 64, 8, 2, 64)
+    p0p = ctypes.byref(p0)
+    assert lib.moe_router_stats(p0p, None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
+    assert lib.moe_shared_expert(p0p, 128, None, None, None, None, None, 0, None) == moe.MOE_OK
+    assert lib.moe_combine_shared(p0p, None, None, None, None, None, None) == moe.MOE_OK
