@@ -10,12 +10,18 @@ top-2, SwiGLU 4096->14336->4096, bf16, Zipf(1.2)-skewed gate bias); every input
 is resident in HBM before the timed region starts.
 
 Prints ONE JSON line: tokens/s of the whole job (value), the roofline of the
-dominant kernel (the expert up-projection grouped GEMM) from HIP events on the
-stream it runs on, and the CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+dominant kernel (the expert up-projection grouped GEMM, with its split-K
+reduction) from HIP events on the stream it runs on, and the CPU oracle timed
+on a bounded sample of the same workload on this host's cores.  The same line
+also carries the router statistics and a shared expert (width F) timed on the
+same workload ("next_rows"), and the step timing of the other workloads
+("other_configs": routing inputs from the seeded generator, expert weights
+drawn on the device with the same distribution, since their values do not
+change the work).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
-                  [--no-cpu-baseline] [--mode copy]
+                  [--no-cpu-baseline] [--no-other-configs] [--no-next-rows]
+                  [--mode copy]
 """
 from __future__ import annotations
 
@@ -117,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mode", default="layer", choices=["layer", "copy"])
     args = ap.parse_args()
@@ -138,90 +146,21 @@ def main():
     import mixture_experts_layer_logit_amd as moe
     import moe_inputs
 
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
     case = moe_inputs.get(args.config)
     log(f"[bench] generating inputs for {case.name}")
     inp = moe_inputs.make(case)
-    torch.cuda.set_device(0)
-    stream = torch.cuda.Stream()
-    dt = torch.float32 if case.dtype == "f32" else torch.bfloat16
-
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(a).cuda()
-
-    T, d, E, k, F = case.T, case.d, case.E, case.k, case.F
-    n1 = 2 * F if case.act == "swiglu" else F
-    p = moe.problem(T, d, E, k, F, act=case.act, dtype=case.dtype, normalize=case.normalize, lam=case.lam,
-                    cf=case.cf)
     with torch.cuda.stream(stream):
-        x = dev(inp["x"])
-        Wg = dev(inp["Wg"]) if inp["Wg"] is not None else None
-        bg = dev(inp["bg"]) if inp["bg"] is not None else None
-        W1 = dev(inp["W1"])
-        W2 = dev(inp["W2"])
-        logits = dev(inp["logits"]) if case.logits == "given" else torch.empty(T, E, dtype=torch.float32,
-                                                                               device="cuda")
-        idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
-        w = torch.empty(T, k, dtype=torch.float32, device="cuda")
-        counts = torch.empty(E, dtype=torch.int32, device="cuda")
-        offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-        slot = torch.empty(T, k, dtype=torch.int32, device="cuda")
-        src = torch.empty(T * k, dtype=torch.int32, device="cuda")
-        h = torch.empty(T * k, F, dtype=dt, device="cuda")
-        y_perm = torch.empty(T * k, d, dtype=dt, device="cuda")
-        y = torch.empty(T, d, dtype=dt, device="cuda")
-        ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    s = stream.cuda_stream
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        moe.moe_route(p, x if Wg is not None else None, Wg, bg, logits, idx, w, stream=s)
-        if ev is not None:
-            ev[1].record(stream)
-        # no x_perm copy: the up projection gathers the rows of x through src
-        moe.moe_permute(p, idx, None, counts, offsets, slot, src, None, ws, stream=s)
-        if ev is not None:
-            ev[2].record(stream)
-        moe.moe_expert_up(p, x, src, offsets, W1, h, ws=ws, stream=s)
-        if ev is not None:
-            ev[3].record(stream)
-        moe.moe_expert_down(p, h, offsets, W2, y_perm, ws=ws, stream=s)
-        if ev is not None:
-            ev[4].record(stream)
-        moe.moe_combine(p, y_perm, slot, w, y, stream=s)
-        if ev is not None:
-            ev[5].record(stream)
-
+        dev_w = {"W1": to_dev(inp["W1"]), "W2": to_dev(inp["W2"])}
+    lay = Layer(moe, case, inp, dev_w, stream)
     log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    names = ["route", "permute", "expert_up", "expert_down", "combine"]
-    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, n in enumerate(names)}
-    P = int(offsets[-1].item())
-    dropped = T * k - P
-    up_flops = 2.0 * P * d * n1
-    down_flops = 2.0 * P * F * d
-    gate_flops = 2.0 * T * d * E if case.logits == "gate" else 0.0
+    res = lay.time(args.steps, args.warmup)
+    T, d, E, k, F = case.T, case.d, case.E, case.k, case.F
+    stage_ms, elapsed, P = res["stage_ms"], res["elapsed"], res["P"]
     ms_per_step = elapsed * 1e3 / args.steps
     peak = PEAK_TFLOPS[case.dtype]
-    up_tflops = up_flops / (stage_ms["expert_up"] * 1e-3) / 1e12
-    ffn_tflops = (up_flops + down_flops) / ((stage_ms["expert_up"] + stage_ms["expert_down"]) * 1e-3) / 1e12
-    row_bytes = d * (4 if case.dtype == "f32" else 2)
-    combine_gbps = (T + P) * row_bytes / (stage_ms["combine"] * 1e-3) / 1e9
+    up_tflops = lay.up_flops(P) / (stage_ms["expert_up"] * 1e-3) / 1e12
 
     result = {
         "metric": METRIC,
@@ -236,26 +175,211 @@ def main():
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{case.name}: T={T} d={d} E={E} k={k} F={F} {case.act} {case.dtype}"
-                               + (f" lambda-normalised" if case.normalize else "")
-                               + (f" cf={case.cf}" if case.cf > 0 else " dropless")
-                               + (" Zipf(1.2) gate bias" if case.bias == "zipf" else ""),
-                   "T": T, "d": d, "E": E, "k": k, "F": F, "parallelism": "single GPU"},
+        "config": {"workload": workload_name(case), "T": T, "d": d, "E": E, "k": k, "F": F,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": up_tflops / peak, "traffic": stored_traffic(case.name),
-                     "kernel": "moe_grouped_gemm_kernel (expert up-projection + activation)"},
-        "tflops": (up_flops + down_flops + gate_flops) / (ms_per_step * 1e-3) / 1e12,
-        "grouped_gemm_pct_of_bf16_peak": 100.0 * ffn_tflops / peak,
-        "stage_ms": stage_ms,
-        "combine_hbm_frac": combine_gbps / HBM_GBPS,
-        "kept_rows": P,
-        "dropped_assignments": dropped,
-        "expert_loads": counts.cpu().tolist(),
+                     "kernel": "moe_expert_up: moe_grouped_gemm_kernel (up-projection + activation) and its K-split reduction"},
     }
+    result.update(lay.summary(res, ms_per_step))
+
+    # rows beyond the layer step: router statistics, shared expert
+    if not args.no_next_rows:
+        log("[bench] router statistics and shared expert")
+        result["next_rows"] = lay.time_next_rows(args.steps, res)
+
+    if not args.no_other_configs:
+        others = {}
+        for name in moe_inputs.FULL:
+            if name == case.name:
+                continue
+            c = moe_inputs.get(name)
+            log(f"[bench] {name}: routing inputs from the seeded generator, expert weights drawn on the device")
+            ri = moe_inputs.make(c, weights=False)
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(c.seed)
+            n1 = 2 * c.F if c.act == "swiglu" else c.F
+            dt = torch.float32 if c.dtype == "f32" else torch.bfloat16
+            with torch.cuda.stream(stream):
+                w = {"W1": (torch.randn(c.E, n1, c.d, generator=gen, device="cuda") * c.w_std).to(dt),
+                     "W2": (torch.randn(c.E, c.d, c.F, generator=gen, device="cuda") * c.w_std).to(dt)}
+            lo = Layer(moe, c, ri, w, stream)
+            steps = max(args.steps // 2, 3)
+            r = lo.time(steps, max(args.warmup // 2, 2))
+            msps = r["elapsed"] * 1e3 / steps
+            o = {"workload": workload_name(c), "tokens_per_s": c.T * steps / r["elapsed"], "ms_per_step": msps}
+            o.update(lo.summary(r, msps))
+            others[name] = o
+            del lo, w, ri
+            torch.cuda.empty_cache()
+        result["other_configs"] = others
+
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(case, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def workload_name(case):
+    return (f"{case.name}: T={case.T} d={case.d} E={case.E} k={case.k} F={case.F} {case.act} {case.dtype}"
+            + (" lambda-normalised" if case.normalize else "")
+            + (f" cf={case.cf}" if case.cf > 0 else " dropless")
+            + (" Zipf(1.2) gate bias" if case.bias == "zipf" else "")
+            + (" given logits" if case.logits == "given" else ""))
+
+
+class Layer:
+    """Device buffers and the timed step of one workload.  One step = gate +
+    routing, permutation (indices only: the up projection gathers the token
+    rows itself), expert up and down layers, weighted combine, all on one
+    stream with an event between the stages."""
+
+    NAMES = ["route", "permute", "expert_up", "expert_down", "combine"]
+
+    def __init__(self, moe, case, inp, w, stream):
+        import torch
+        self.moe, self.case, self.stream = moe, case, stream
+        T, d, E, k, F = case.T, case.d, case.E, case.k, case.F
+        self.n1 = 2 * F if case.act == "swiglu" else F
+        self.p = moe.problem(T, d, E, k, F, act=case.act, dtype=case.dtype, normalize=case.normalize,
+                             lam=case.lam, cf=case.cf)
+        dt = torch.float32 if case.dtype == "f32" else torch.bfloat16
+        self.dt = dt
+        with torch.cuda.stream(stream):
+            self.x = to_dev(inp["x"])
+            self.Wg = to_dev(inp["Wg"]) if inp.get("Wg") is not None else None
+            self.bg = to_dev(inp["bg"]) if inp.get("bg") is not None else None
+            self.W1, self.W2 = w["W1"], w["W2"]
+            self.logits = to_dev(inp["logits"]) if case.logits == "given" else \
+                torch.empty(T, E, dtype=torch.float32, device="cuda")
+            self.idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+            self.w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+            self.counts = torch.empty(E, dtype=torch.int32, device="cuda")
+            self.offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+            self.slot = torch.empty(T, k, dtype=torch.int32, device="cuda")
+            self.src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+            self.h = torch.empty(T * k, F, dtype=dt, device="cuda")
+            self.y_perm = torch.empty(T * k, d, dtype=dt, device="cuda")
+            self.y = torch.empty(T, d, dtype=dt, device="cuda")
+            self.ws = torch.empty(moe.moe_workspace_size(self.p), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        moe, p, s = self.moe, self.p, self.stream.cuda_stream
+        rec = (lambda i: ev[i].record(self.stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        moe.moe_route(p, self.x if self.Wg is not None else None, self.Wg, self.bg, self.logits, self.idx, self.w,
+                      stream=s)
+        rec(1)
+        moe.moe_permute(p, self.idx, None, self.counts, self.offsets, self.slot, self.src, None, self.ws, stream=s)
+        rec(2)
+        moe.moe_expert_up(p, self.x, self.src, self.offsets, self.W1, self.h, ws=self.ws, stream=s)
+        rec(3)
+        moe.moe_expert_down(p, self.h, self.offsets, self.W2, self.y_perm, ws=self.ws, stream=s)
+        rec(4)
+        moe.moe_combine(p, self.y_perm, self.slot, self.w, self.y, stream=s)
+        rec(5)
+
+    def time(self, steps, warmup):
+        import numpy as np
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(events[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
+                    for i, n in enumerate(self.NAMES)}
+        return {"stage_ms": stage_ms, "elapsed": elapsed, "P": int(self.offsets[-1].item())}
+
+    def up_flops(self, P):
+        return 2.0 * P * self.case.d * self.n1
+
+    def summary(self, res, ms_per_step):
+        c = self.case
+        stage_ms, P = res["stage_ms"], res["P"]
+        up, down = self.up_flops(P), 2.0 * P * c.F * c.d
+        gate = 2.0 * c.T * c.d * c.E if c.logits == "gate" else 0.0
+        peak = PEAK_TFLOPS[c.dtype]
+        ffn_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
+        b = 4 if c.dtype == "f32" else 2
+        combine_bytes = (c.T + P) * c.d * b + 8.0 * c.T * c.k
+        return {
+            "tflops": (up + down + gate) / (ms_per_step * 1e-3) / 1e12,
+            "grouped_gemm_pct_of_peak": 100.0 * (up + down) / (ffn_ms * 1e-3) / 1e12 / peak,
+            "stage_ms": stage_ms,
+            "combine_hbm_frac": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9 / HBM_GBPS,
+            "kept_rows": P,
+            "dropped_assignments": c.T * c.k - P,
+            "expert_loads": self.counts.cpu().tolist() if c.E <= 64 else
+            {"min": int(self.counts.min()), "max": int(self.counts.max())},
+        }
+
+    def time_next_rows(self, steps, res):
+        """Router statistics on the step's routing; a shared expert of width F
+        over all tokens and the combine that adds it."""
+        import numpy as np
+        import torch
+        moe, p, c, s = self.moe, self.p, self.case, self.stream.cuda_stream
+        T, d, E, F = c.T, c.d, c.E, c.F
+        b = 4 if c.dtype == "f32" else 2
+        with torch.cuda.stream(self.stream):
+            frac = torch.empty(E, dtype=torch.float32, device="cuda")
+            mp = torch.empty(E, dtype=torch.float32, device="cuda")
+            sc = torch.empty(3, dtype=torch.float32, device="cuda")
+            Fs = F
+            n1s = 2 * Fs if c.act == "swiglu" else Fs
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(c.seed + 7)
+            Ws1 = (torch.randn(n1s, d, generator=gen, device="cuda") * c.w_std).to(self.dt)
+            Ws2 = (torch.randn(d, Fs, generator=gen, device="cuda") * c.w_std).to(self.dt)
+            ysh = torch.empty(T, d, dtype=self.dt, device="cuda")
+            sws = torch.empty(moe.moe_shared_workspace_size(p, Fs), dtype=torch.uint8, device="cuda")
+        calls = {
+            "router_stats": lambda: moe.moe_router_stats(p, self.logits, self.counts, self.offsets, frac, mp, sc,
+                                                         self.ws, stream=s),
+            "shared_expert": lambda: moe.moe_shared_expert(p, Fs, self.x, Ws1, Ws2, ysh, sws, stream=s),
+            "combine_shared": lambda: moe.moe_combine_shared(p, self.y_perm, self.slot, self.w, ysh, self.y,
+                                                             stream=s),
+        }
+        out = {}
+        for name, fn in calls.items():
+            for _ in range(2):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            ev[0].record(self.stream)
+            for i in range(steps):
+                fn()
+                ev[i + 1].record(self.stream)
+            torch.cuda.synchronize()
+            out[name] = {"ms": float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))}
+        P = res["P"]
+        st = out["router_stats"]
+        st["bytes"] = 4.0 * T * E + 8.0 * E + 12
+        st["hbm_frac"] = st["bytes"] / (st["ms"] * 1e-3) / 1e9 / HBM_GBPS
+        st["values"] = {"aux": float(sc[0]), "z_loss": float(sc[1]), "drop_rate": float(sc[2])}
+        sh = out["shared_expert"]
+        sh["Fs"] = Fs
+        sh["tflops"] = (2.0 * T * d * n1s + 2.0 * T * Fs * d) / (sh["ms"] * 1e-3) / 1e12
+        sh["mfma_frac"] = sh["tflops"] / PEAK_TFLOPS[c.dtype]
+        cs = out["combine_shared"]
+        cs["bytes"] = (P + 2 * T) * d * b + 8.0 * T * c.k
+        cs["hbm_frac"] = cs["bytes"] / (cs["ms"] * 1e-3) / 1e9 / HBM_GBPS
+        return out
 
 
 if __name__ == "__main__":

@@ -289,13 +289,13 @@ struct Frag {
 
 // Epilogue: activation and store of a tile from the wave's accumulators.
 // Lane holds row m = .. + (lane & 31), 4 consecutive columns per group.
+// `wave` is the wave slot of the tile whose accumulators these are.
 template <typename ET, typename S, int EPI>
 __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename ET::storage* __restrict__ C, const TileDec& t,
-                                           int Nout, int ncols)
+                                           int Nout, int ncols, int wave)
 {
     typedef typename ET::storage T;
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
     const int wm = wave / S::WN, wn = wave % S::WN;
 #pragma unroll
     for (int i = 0; i < S::kFM; ++i) {
@@ -592,7 +592,7 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         }
 
         if (slot < 0) {
-            store_tile<ET, S, EPI>(acc, C, t, Nout, ncols);
+            store_tile<ET, S, EPI>(acc, C, t, Nout, ncols, wave);
         } else {
             float* dst = partial + (size_t)slot * S::kTileFloats;
 #pragma unroll
@@ -609,19 +609,20 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
 #endif
 }
 
-// Second pass of the tail split: one block per split tile adds its K parts in
-// part order and stores the tile through the same epilogue.
+// Second pass of the tail split: one wavefront per (split tile, wave slot)
+// adds that slot's K parts in part order and stores its share of the tile
+// through the same epilogue (so every CU takes part, not one block per tile).
 template <typename ET, typename S, int EPI>
-__global__ __launch_bounds__(S::kThreads) void moe_grouped_gemm_tail_kernel(
+__global__ __launch_bounds__(256) void moe_grouped_gemm_tail_kernel(
     typename ET::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E, int K, int Nout, int F,
     int max_rows, int G, const float* __restrict__ partial)
 {
     __shared__ int32_t s_pref[kGemmMaxE + 1];
-    __shared__ int32_t s_wsum[S::kWaves];
+    __shared__ int32_t s_wsum[256 / kWave];
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
     const int ncols = (EPI == EPI_SWIGLU) ? F : Nout;
     const int ntn = (ncols + tile_cols - 1) / tile_cols;
-    tile_prefix<S::kThreads>(offsets, E, max_rows, S::BM, ntn, s_pref, s_wsum);
+    tile_prefix<256>(offsets, E, max_rows, S::BM, ntn, s_pref, s_wsum);
     const int total = s_pref[E];
     const int nk = K / S::kBK;
     const int parts = split_parts(total, G, nk, true);
@@ -630,8 +631,9 @@ __global__ __launch_bounds__(S::kThreads) void moe_grouped_gemm_tail_kernel(
     const int full = total - total % G;
     const int tail = total - full;
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    for (int j = blockIdx.x; j < tail; j += gridDim.x) {
+    const int nwork = tail * S::kWaves;
+    for (int wk = blockIdx.x * 4 + threadIdx.x / kWave; wk < nwork; wk += gridDim.x * 4) {
+        const int j = wk / S::kWaves, wave = wk % S::kWaves;
         const TileDec t = decode_tile<S>(full + j, s_pref, offsets, E, max_rows, ntn, tile_cols);
         Acc<S> acc;
 #pragma unroll
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(S::kThreads) void moe_grouped_gemm_tail_kernel(
                         acc.v[i][jj][4 * g + 3] += p.w;
                     }
         }
-        store_tile<ET, S, EPI>(acc, C, t, Nout, ncols);
+        store_tile<ET, S, EPI>(acc, C, t, Nout, ncols, wave);
     }
 }
 
@@ -690,7 +692,8 @@ hipError_t launch_one(const void* A, const int32_t* gather, int gather_rows, con
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || partial == nullptr)
         return err;
-    moe_grouped_gemm_tail_kernel<ET, S, EPI><<<dim3(kSplitSlots / 2), dim3(S::kThreads), 0, stream>>>(
+    // at most kSplitSlots / 2 split tiles (each has >= 2 parts) x kWaves wave slots, 4 per block
+    moe_grouped_gemm_tail_kernel<ET, S, EPI><<<dim3(kSplitSlots / 2 * S::kWaves / 4), dim3(256), 0, stream>>>(
         (T*)C, offsets, E, K, Nout, F, max_rows, (int)grid, partial);
     return hipGetLastError();
 }

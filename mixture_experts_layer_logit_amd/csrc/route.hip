@@ -17,15 +17,17 @@ namespace moe {
 // tiling.  Routing decisions therefore do not depend on how this kernel (or
 // any other correct gate) orders its sums.
 //
-// Work split: a block of 4 wavefronts takes 16 tokens, each wavefront 4 of
-// them; the 64 lanes split the model dimension in 8-element chunks (lane l
-// takes chunks l, l+64, ...), so the x rows and Wg rows are read with 16-byte
-// coalesced loads.  Experts go in groups of 8.  The 4 x 8 partial sums of a
-// lane are reduced across the wavefront by recursive halving: each exchange
-// halves the values a lane holds, so 32 values need 16+8+4+2+1+1 shuffles.
-constexpr int kGateTokPerWave = 4;
+// Work split: a block of 4 wavefronts takes 4 tokens; the model dimension is
+// cut into 8-element chunks and thread j of the block takes chunks j,
+// j + 256, ..., so the x rows and Wg rows are read with 16-byte coalesced
+// loads and every wavefront covers a quarter of the row (T/4 blocks keep
+// enough loads in flight to stream x).  Experts go in groups of 8.  A lane's
+// 4 x 8 partial sums are reduced across its wavefront by recursive halving
+// (each exchange halves the values a lane holds: 32 values need
+// 16+8+4+2+1+1 shuffles), then the 4 wavefronts' sums are added in wave
+// order through LDS.  Wg rows are re-read per block from L2.
+constexpr int kGateTokPerBlock = 4;
 constexpr int kGateExpGroup = 8;
-constexpr int kGateTokPerBlock = 4 * kGateTokPerWave;
 
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET::storage* __restrict__ x,
@@ -33,21 +35,23 @@ __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET:
                                                               const float* __restrict__ bg,
                                                               float* __restrict__ logits, int T, int d, int E)
 {
+    constexpr int kVals = kGateTokPerBlock * kGateExpGroup;  // 32 sums per lane
+    __shared__ double s_part[4][kVals];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    const int t0 = blockIdx.x * kGateTokPerBlock + wave * kGateTokPerWave;
+    const int t0 = blockIdx.x * kGateTokPerBlock;  // block-uniform
     if (t0 >= T)
         return;
     const int nchunk = d / 8;
     for (int e0 = 0; e0 < E; e0 += kGateExpGroup) {
-        double acc[kGateTokPerWave * kGateExpGroup];
+        double acc[kVals];
 #pragma unroll
-        for (int v = 0; v < kGateTokPerWave * kGateExpGroup; ++v)
+        for (int v = 0; v < kVals; ++v)
             acc[v] = 0.0;
-        for (int c = lane; c < nchunk; c += kWave) {
-            double xd[kGateTokPerWave][8];
+        for (int c = threadIdx.x; c < nchunk; c += 256) {
+            double xd[kGateTokPerBlock][8];
 #pragma unroll
-            for (int tt = 0; tt < kGateTokPerWave; ++tt) {
+            for (int tt = 0; tt < kGateTokPerBlock; ++tt) {
                 float xf[8];
                 const int t = min(t0 + tt, T - 1);  // rows past T are computed but not stored
                 load8(x + (size_t)t * d + (size_t)c * 8, xf);
@@ -64,7 +68,7 @@ __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET:
                 for (int i = 0; i < 8; ++i) {
                     const double wd = (double)wf[i];
 #pragma unroll
-                    for (int tt = 0; tt < kGateTokPerWave; ++tt)
+                    for (int tt = 0; tt < kGateTokPerBlock; ++tt)
                         acc[tt * kGateExpGroup + ee] = fma(xd[tt][i], wd, acc[tt * kGateExpGroup + ee]);
                 }
             }
@@ -72,13 +76,13 @@ __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET:
         // Recursive halving over lane bits 5..1: after the exchange across
         // bit b a lane keeps the half of its values selected by its own bit b.
         double* v = acc;
-        int n = kGateTokPerWave * kGateExpGroup;  // 32
+        int n = kVals;
 #pragma unroll
         for (int bit = 5; bit >= 1; --bit) {
             const int half = n / 2;
             const bool upper = (lane >> bit) & 1;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < kVals / 2; ++i) {
                 if (i < half) {
                     const double keep = upper ? v[half + i] : v[i];
                     const double send = upper ? v[i] : v[half + i];
@@ -87,15 +91,23 @@ __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET:
             }
             n = half;
         }
-        double s = v[0] + __shfl_xor(v[0], 1);
+        const double s = v[0] + __shfl_xor(v[0], 1);
         // lane l now holds value index (l >> 1): token (l >> 4), expert ((l >> 1) & 7)
-        const int t = t0 + (lane >> 4);
-        const int e = e0 + ((lane >> 1) & 7);
-        if ((lane & 1) == 0 && t < T && e < E) {
-            if (bg)
-                s += (double)bg[e];
-            logits[(size_t)t * E + e] = (float)s;
+        if ((lane & 1) == 0)
+            s_part[wave][lane >> 1] = s;
+        __syncthreads();
+        if (threadIdx.x < kVals) {
+            const int t = t0 + threadIdx.x / kGateExpGroup;
+            const int e = e0 + threadIdx.x % kGateExpGroup;
+            double sum = ((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
+                         s_part[3][threadIdx.x];
+            if (t < T && e < E) {
+                if (bg)
+                    sum += (double)bg[e];
+                logits[(size_t)t * E + e] = (float)sum;
+            }
         }
+        __syncthreads();  // s_part is reused by the next expert group
     }
 }
 
@@ -247,8 +259,8 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
 // wavefront adds its tokens' gate probabilities (fp64, the same arithmetic as
 // the router) per expert and (logsumexp z)^2 of the raw logits; the block's
 // 4 wavefronts are added in wave order and stored as partial[b][0..E-1] and
-// partial[b][E].  Pass 2 adds the blocks in block order.  The grid depends
-// only on T, so the sums are the same on every run.
+// partial[b][E].  Passes 2 and 3 add the blocks and then the experts in fixed
+// orders.  The grid depends only on T, so the sums are the same on every run.
 constexpr int kStatsBlocks = 256;
 
 template <int VPL>
@@ -304,34 +316,51 @@ __global__ __launch_bounds__(256) void moe_router_stats_kernel(const float* __re
         dst[E] = ((s_acc[0][VPL * kWave] + s_acc[1][VPL * kWave]) + s_acc[2][VPL * kWave]) + s_acc[3][VPL * kWave];
 }
 
-// Pass 2, one block of 1024 threads (thread e owns expert e):
-//   mean_prob[e] = sum_b partial[b][e] / T,  frac[e] = counts[e] / (T k),
-//   scalars = {E * sum_e frac[e] mean_prob[e], sum_b partial[b][E] / T,
-//              (T k - offsets[E]) / (T k)}
-// The sum over experts is a fixed tree (wavefront shuffles, then the 16
+// Pass 2, one wavefront per item e in [0, E] (E is the Z-loss sum): lanes
+// add partial[b][e] for b = lane, lane + 64, ... in order, then a fixed
+// shuffle tree adds the lanes.  Writes mean_prob[e] = sum / T and
+// frac[e] = counts[e] / (T k) and keeps terms[e] = frac[e] * mean_prob[e]
+// (terms[E] = Z-loss sum) for pass 3.
+__global__ __launch_bounds__(256) void moe_router_stats_reduce_kernel(const double* __restrict__ partial,
+                                                                       int nblocks, int T, int E, int k,
+                                                                       const int32_t* __restrict__ counts,
+                                                                       float* __restrict__ frac,
+                                                                       float* __restrict__ mean_prob,
+                                                                       double* __restrict__ terms)
+{
+    const int e = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (e > E)
+        return;
+    const int lane = lane_id();
+    double s = 0.0;
+    for (int b = lane; b < nblocks; b += kWave)
+        s += partial[(size_t)b * (E + 1) + e];
+    s = wave_sum(s);
+    if (lane == 0) {
+        if (e < E) {
+            const double mp = s / (double)T;
+            const double f = (double)counts[e] / ((double)T * (double)k);
+            mean_prob[e] = (float)mp;
+            frac[e] = (float)f;
+            terms[e] = f * mp;
+        } else {
+            terms[E] = s;
+        }
+    }
+}
+
+// Pass 3, one block of 1024 threads (thread e owns expert e):
+//   scalars = {E * sum_e terms[e], terms[E] / T, (T k - offsets[E]) / (T k)}
+// with the sum over experts a fixed tree (wavefront shuffles, then the 16
 // wavefronts in order).
-__global__ __launch_bounds__(1024) void moe_router_stats_final_kernel(const double* __restrict__ partial,
-                                                                      int nblocks, int T, int E, int k,
-                                                                      const int32_t* __restrict__ counts,
+__global__ __launch_bounds__(1024) void moe_router_stats_final_kernel(const double* __restrict__ terms, int T,
+                                                                      int E, int k,
                                                                       const int32_t* __restrict__ offsets,
-                                                                      float* __restrict__ frac,
-                                                                      float* __restrict__ mean_prob,
                                                                       float* __restrict__ scalars)
 {
     __shared__ double s_w[1024 / kWave];
     const int e = threadIdx.x;
-    const double n = (double)T * (double)k;
-    double term = 0.0;
-    if (e < E) {
-        double s = 0.0;
-        for (int b = 0; b < nblocks; ++b)
-            s += partial[(size_t)b * (E + 1) + e];
-        const double mp = s / (double)T;
-        const double f = (double)counts[e] / n;
-        mean_prob[e] = (float)mp;
-        frac[e] = (float)f;
-        term = f * mp;
-    }
+    double term = e < E ? terms[e] : 0.0;
     term = wave_sum(term);
     if (lane_id() == 0)
         s_w[threadIdx.x / kWave] = term;
@@ -340,12 +369,10 @@ __global__ __launch_bounds__(1024) void moe_router_stats_final_kernel(const doub
         double aux = 0.0;
         for (int w = 0; w < 1024 / kWave; ++w)
             aux += s_w[w];
-        double zs = 0.0;
-        for (int b = 0; b < nblocks; ++b)
-            zs += partial[(size_t)b * (E + 1) + E];
+        const double n = (double)T * (double)k;
         const int kept = min(max(offsets[E], 0), T * k);
         scalars[0] = (float)((double)E * aux);
-        scalars[1] = (float)(zs / (double)T);
+        scalars[1] = (float)(terms[E] / (double)T);
         scalars[2] = (float)((n - (double)kept) / n);
     }
 }
@@ -386,11 +413,12 @@ extern "C" hipError_t moe_launch_router(const float* logits, int T, int E, int k
     return hipGetLastError();
 }
 
-// Workspace of the statistics' first pass, in bytes.
+// Workspace of the statistics, in bytes: the first pass's block partials,
+// then the E + 1 per-item sums of the second.
 extern "C" size_t moe_router_stats_partial_bytes(int T, int E)
 {
     const int nb = T < 4 * moe::kStatsBlocks ? (T + 3) / 4 : moe::kStatsBlocks;
-    return (size_t)(nb > 0 ? nb : 1) * (E + 1) * sizeof(double);
+    return (size_t)((nb > 0 ? nb : 1) + 1) * (E + 1) * sizeof(double);
 }
 
 extern "C" hipError_t moe_launch_router_stats(const float* logits, int T, int E, int k, int normalize, float lambda,
@@ -414,7 +442,12 @@ extern "C" hipError_t moe_launch_router_stats(const float* logits, int T, int E,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    moe_router_stats_final_kernel<<<1, 1024, 0, stream>>>(partial, nb, T, E, k, counts, offsets, frac, mean_prob,
-                                                           scalars);
+    double* terms = partial + (size_t)nb * (E + 1);
+    moe_router_stats_reduce_kernel<<<dim3((E + 1 + 3) / 4), dim3(256), 0, stream>>>(partial, nb, T, E, k, counts,
+                                                                                   frac, mean_prob, terms);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    moe_router_stats_final_kernel<<<1, 1024, 0, stream>>>(terms, T, E, k, offsets, scalars);
     return hipGetLastError();
 }

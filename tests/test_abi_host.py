@@ -58,7 +58,8 @@ def workspace_formula(T, d, E, k, F, b, cf=0.0):
     nch = max((T + 255) // 256, 1)
     gather = T * d * b < 0xF0000000  # else x_perm is kept in the workspace
     nstat = max((T + 3) // 4 if T < 1024 else 256, 1)  # blocks of the router statistics' first pass
-    return (r(T * k * 4) * 4 + r(E * 4) + r((E + 1) * 4) + r(nch * E * 4) + r(T * E * 4) + r(nstat * (E + 1) * 8)
+    return (r(T * k * 4) * 4 + r(E * 4) + r((E + 1) * 4) + r(nch * E * 4) + r(T * E * 4)
+            + r((nstat + 1) * (E + 1) * 8)
             + r(256 * partial_floats(T, E, k, b, cf) * 4) + r(T * k * F * b) + r(T * k * d * b)
             + (0 if gather else r(T * k * d * b)))
 
