@@ -78,6 +78,17 @@ def _load():
     lib.orc_combine.argtypes = [I, I, I, I, P, P, P, P]
     lib.orc_down_rows.argtypes = [I, I, I, I, P, P, P, I, P, P]
     lib.orc_router_stats.argtypes = [I, I, I, I, D, P, P, ctypes.c_longlong, P, P, P]
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_decode.restype = D
+    lib.orc_e4m3_encode.argtypes = [D]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_fp8_scale_exp.argtypes = [D]
+    lib.orc_fp8_scale_exp.restype = I
+    lib.orc_quant_rows_fp8.argtypes = [ctypes.c_longlong, I, I, P, P, P]
+    lib.orc_expert_ffn_fp8.argtypes = [I, I, I, P, P, P, P, I, P, D, P, P]
+    lib.orc_ffn_rows_fp8.argtypes = [I, I, I, I, P, P, P, P, P, P, P, I, P, P, P]
+    lib.orc_down_rows_fp8.argtypes = [I, I, I, P, P, P, P, P, I, P, P]
+    lib.orc_forward_tokens_fp8.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P]
     _lib = lib
     return lib
 
@@ -323,3 +334,112 @@ def combine_shared(y_perm, slot, topk_w, y_shared):
     with weight one).  y_shared is float64 or a stored fp32/bf16 array."""
     ys = to_f64(np.asarray(y_shared)) if np.asarray(y_shared).dtype != np.float64 else np.asarray(y_shared)
     return ys + combine(y_perm, slot, topk_w, ys.shape[0])
+
+
+# ---------------------------------------------------------------- FP8 (E4M3)
+# Expert weights and activations as OCP FP8 E4M3 codes with power-of-two row
+# scales (see the FP8 entry of moe_oracle.c's header for the reading).
+
+def e4m3_decode(codes):
+    """Values (float64) of E4M3 codes (uint8 array)."""
+    c = np.asarray(codes, np.uint8)
+    lib = _load()
+    table = np.array([lib.orc_e4m3_decode(i) for i in range(256)], np.float64)
+    return table[c]
+
+
+def e4m3_encode(values):
+    """Nearest E4M3 codes (ties to even, saturating at 448) of finite values."""
+    v = np.asarray(values, np.float64)
+    lib = _load()
+    out = np.empty(v.shape, np.uint8)
+    flat_in, flat_out = v.ravel(), out.ravel()
+    for i in range(flat_in.size):
+        flat_out[i] = lib.orc_e4m3_encode(float(flat_in[i]))
+    return out
+
+
+def fp8_scale_exp(amax):
+    return _load().orc_fp8_scale_exp(float(amax))
+
+
+def quant_rows_fp8(src):
+    """Per-row power-of-two quantisation of a [R, K] array (float32, uint16
+    bf16 bits or float64): returns (codes uint8 [R, K], scales float32 [R])."""
+    a = np.asarray(src)
+    if a.dtype == np.float64:
+        a = np.ascontiguousarray(a)
+        code = 2
+    else:
+        a = _c(a)
+        code = _dtype_code(a)
+    R, K = a.shape
+    codes = np.empty((R, K), np.uint8)
+    scales = np.empty(R, np.float32)
+    _load().orc_quant_rows_fp8(R, K, code, _ptr(a), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def ffn_rows_fp8(xq, xs, offsets, W1q, w1s, W2q, w2s, act, F, rows=None, want_h=False):
+    """FP8 expert FFN of permuted quantised rows (float64 [n, d]); h, when
+    asked for, is the activation output before its quantisation."""
+    xq = np.ascontiguousarray(xq, np.uint8)
+    xs = np.ascontiguousarray(xs, np.float32)
+    W1q = np.ascontiguousarray(W1q, np.uint8)
+    W2q = np.ascontiguousarray(W2q, np.uint8)
+    w1s = np.ascontiguousarray(w1s, np.float32)
+    w2s = np.ascontiguousarray(w2s, np.float32)
+    off = _c(offsets, np.int32)
+    E = off.shape[0] - 1
+    d = W2q.shape[1]
+    rr = None if rows is None else _c(rows, np.int32)
+    n = xq.shape[0] if rr is None else rr.shape[0]
+    out = np.empty((n, d), np.float64)
+    h = np.empty((n, F), np.float64) if want_h else None
+    _load().orc_ffn_rows_fp8(E, d, F, int(act), _ptr(off), _ptr(xq), _ptr(xs), _ptr(W1q), _ptr(w1s), _ptr(W2q),
+                             _ptr(w2s), n, _ptr(rr), _ptr(out), _ptr(h))
+    return (out, h) if want_h else out
+
+
+def down_rows_fp8(hq, hs, offsets, W2q, w2s, rows=None):
+    """Second FP8 layer on given quantised hidden rows (float64 [n, d])."""
+    hq = np.ascontiguousarray(hq, np.uint8)
+    hs = np.ascontiguousarray(hs, np.float32)
+    W2q = np.ascontiguousarray(W2q, np.uint8)
+    w2s = np.ascontiguousarray(w2s, np.float32)
+    off = _c(offsets, np.int32)
+    E = off.shape[0] - 1
+    d, F = W2q.shape[1], W2q.shape[2]
+    rr = None if rows is None else _c(rows, np.int32)
+    n = hq.shape[0] if rr is None else rr.shape[0]
+    out = np.empty((n, d), np.float64)
+    _load().orc_down_rows_fp8(E, d, F, _ptr(off), _ptr(hq), _ptr(hs), _ptr(W2q), _ptr(w2s), n, _ptr(rr), _ptr(out))
+    return out
+
+
+def forward_tokens_fp8(x, W1q, w1s, W2q, w2s, topk_idx, topk_w, slot, act, F, tokens=None):
+    """FP8 layer output rows (float64 [n, d]) for the given tokens."""
+    x = _c(x)
+    T, d = x.shape
+    W1q = np.ascontiguousarray(W1q, np.uint8)
+    W2q = np.ascontiguousarray(W2q, np.uint8)
+    w1s = np.ascontiguousarray(w1s, np.float32)
+    w2s = np.ascontiguousarray(w2s, np.float32)
+    idx = _c(topk_idx, np.int32)
+    k = idx.shape[1]
+    w = _c(topk_w, np.float64)
+    sl = _c(slot, np.int32)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n = T if tok is None else tok.shape[0]
+    y = np.empty((n, d), np.float64)
+    _load().orc_forward_tokens_fp8(d, k, F, int(act), _dtype_code(x), _ptr(x), _ptr(W1q), _ptr(w1s), _ptr(W2q),
+                                   _ptr(w2s), _ptr(idx), _ptr(w), _ptr(sl), n, _ptr(tok), _ptr(y))
+    return y
+
+
+def quant_weights_fp8(W):
+    """E4M3 codes and per-row scales of an expert weight stack [E, rows, K]."""
+    W = np.asarray(W)
+    E, R, K = W.shape
+    codes, scales = quant_rows_fp8(W.reshape(E * R, K))
+    return codes.reshape(E, R, K), scales.reshape(E, R)

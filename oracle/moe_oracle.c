@@ -40,6 +40,16 @@
  *                 up_proj fused into one weight, order matters).  No biases.
  *   - combine:    y_t = sum over the token's kept choices j, in selection
  *                 order, of w[t,j] * expert_j(x_t).
+ *   - FP8 experts: expert weights stored as OCP FP8 E4M3 codes (Skywork-MoE
+ *                 model card links an FP8 checkpoint; news item "4090推理":
+ *                 FP8-quantised inference on 8 RTX 4090s; Megatron-Core page,
+ *                 "关键特性": FP8 training among the coming features).  The
+ *                 pages fix no scheme; the plainest one used here: every row
+ *                 of a weight matrix, every token row of x and every row of h
+ *                 carries a power-of-two scale s, the smallest with
+ *                 max|row| <= 448 s, and its codes are the E4M3 values
+ *                 nearest to v / s (ties to even, saturating at 448).  The
+ *                 products are of the dequantised values code * s.
  *   - router by-products: the quantities the load-balancing auxiliary loss,
  *                 its adaptive coefficient and the Z-loss are built from
  *                 (Megatron-Core page, "MoE负载均衡的挑战与应对": an auxiliary
@@ -422,4 +432,201 @@ void orc_router_stats(int T, int E, int k, int normalize, double lambda, const f
     out3[1] = zsum / (double)T;
     out3[2] = (n - (double)kept) / n;
     free(p);
+}
+
+/* ---------------------------------------------------------------- FP8 (E4M3) */
+
+/* Value of an OCP FP8 E4M3FN code: sign, 4 exponent bits (bias 7), 3
+ * mantissa bits; exponent 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN. */
+double orc_e4m3_decode(uint8_t c)
+{
+    const int sgn = c >> 7, ex = (c >> 3) & 15, m = c & 7;
+    if (ex == 15 && m == 7)
+        return NAN;
+    const double mag = ex == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, ex - 7);
+    return sgn ? -mag : mag;
+}
+
+/* Nearest E4M3 code to a finite v, ties to the even code; magnitudes at or
+ * above 448 (the largest finite value) give +-448. */
+uint8_t orc_e4m3_encode(double v)
+{
+    const uint8_t sgn = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs(v);
+    if (a >= 448.0)
+        return sgn | 0x7E;
+    if (a < ldexp(1.0, -6)) {                       /* subnormal range, step 2^-9 */
+        const double q = nearbyint(ldexp(a, 9));    /* 0..8; 8 is the smallest normal */
+        return sgn | (uint8_t)q;
+    }
+    int e;
+    const double fr = frexp(a, &e);                 /* a = fr * 2^e, fr in [0.5, 1) */
+    int ex = e - 1;                                 /* a = (2 fr) * 2^ex, 2 fr in [1, 2) */
+    double q = nearbyint(fr * 16.0);                /* 8..16: 1 + mantissa/8 in eighths */
+    if (q == 16.0) {
+        q = 8.0;
+        ex += 1;
+    }
+    return sgn | (uint8_t)(((ex + 7) << 3) | ((int)q - 8));
+}
+
+/* Exponent e of the power-of-two row scale: the smallest integer with
+ * amax <= 448 * 2^e (0 for amax == 0).  448 = 0.875 * 2^9, so with
+ * amax = m * 2^x, m in [0.5, 1): e = x - 9 if m <= 0.875, else x - 8. */
+int orc_fp8_scale_exp(double amax)
+{
+    if (!(amax > 0.0))
+        return 0;
+    int x;
+    const double m = frexp(amax, &x);
+    return m <= 0.875 ? x - 9 : x - 8;
+}
+
+/* Quantise R rows of K values (fp32 / bf16, or double when dtype == 2):
+ * codes[r][i] = encode(v[r][i] / s_r), scales[r] = s_r = 2^e. */
+void orc_quant_rows_fp8(long long R, int K, int dtype, const void* src, uint8_t* codes, float* scales)
+{
+#pragma omp parallel for schedule(static)
+    for (long long r = 0; r < R; ++r) {
+        double amax = 0.0;
+        for (int i = 0; i < K; ++i) {
+            const size_t at = (size_t)r * K + i;
+            const double v = dtype == 2 ? ((const double*)src)[at] : elem(dtype, src, at);
+            if (fabs(v) > amax)
+                amax = fabs(v);
+        }
+        const int e = orc_fp8_scale_exp(amax);
+        for (int i = 0; i < K; ++i) {
+            const size_t at = (size_t)r * K + i;
+            const double v = dtype == 2 ? ((const double*)src)[at] : elem(dtype, src, at);
+            codes[at] = orc_e4m3_encode(ldexp(v, -e));
+        }
+        scales[r] = (float)ldexp(1.0, e);
+    }
+}
+
+/* One quantised input row (codes xq [d], scale xs) through FP8 expert e.
+ * W1q [E][n1][d] codes with w1s [E][n1] row scales, W2q [E][d][F] with
+ * w2s [E][d].  h (nullable, [F]) receives the activation output before it is
+ * quantised; out [d] = W2^ * quant(h), ^ meaning dequantised. */
+void orc_expert_ffn_fp8(int d, int F, int act, const uint8_t* W1q, const float* w1s, const uint8_t* W2q,
+                        const float* w2s, int e, const uint8_t* xq, double xs, double* out, double* h)
+{
+    const size_t n1 = (act == ORC_SWIGLU) ? 2 * (size_t)F : (size_t)F;
+    double* hh = h ? h : (double*)malloc(sizeof(double) * (size_t)F);
+    double* xin = (double*)malloc(sizeof(double) * (size_t)d);
+    uint8_t* hq = (uint8_t*)malloc((size_t)F);
+    for (int i = 0; i < d; ++i)
+        xin[i] = orc_e4m3_decode(xq[i]) * xs;
+    for (int f = 0; f < F; ++f) {
+        const size_t row_g = (size_t)e * n1 + f;
+        double u = 0.0;
+        for (int i = 0; i < d; ++i)
+            u += orc_e4m3_decode(W1q[row_g * d + i]) * (double)w1s[row_g] * xin[i];
+        if (act == ORC_RELU) {
+            hh[f] = u > 0.0 ? u : 0.0;
+        } else {
+            const size_t row_u = (size_t)e * n1 + F + f;
+            double v = 0.0;
+            for (int i = 0; i < d; ++i)
+                v += orc_e4m3_decode(W1q[row_u * d + i]) * (double)w1s[row_u] * xin[i];
+            hh[f] = u / (1.0 + exp(-u)) * v;
+        }
+    }
+    float hs;
+    orc_quant_rows_fp8(1, F, 2, hh, hq, &hs);
+    for (int o = 0; o < d; ++o) {
+        const size_t row = (size_t)e * d + o;
+        double s = 0.0;
+        for (int f = 0; f < F; ++f)
+            s += orc_e4m3_decode(W2q[row * F + f]) * (double)w2s[row] * orc_e4m3_decode(hq[f]) * (double)hs;
+        out[o] = s;
+    }
+    free(hq);
+    free(xin);
+    if (!h)
+        free(hh);
+}
+
+/* FP8 expert FFN of permuted rows (codes xq [*][d], row scales xs): as
+ * orc_ffn_rows.  h (nullable) [nrows][F] gets the activation before it is
+ * quantised. */
+void orc_ffn_rows_fp8(int E, int d, int F, int act, const int32_t* offsets, const uint8_t* xq, const float* xs,
+                      const uint8_t* W1q, const float* w1s, const uint8_t* W2q, const float* w2s, int nrows,
+                      const int32_t* rows, double* out, double* h)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int n = 0; n < nrows; ++n) {
+        int r = rows ? rows[n] : n;
+        int e = 0;
+        while (e < E && !(offsets[e] <= r && r < offsets[e + 1]))
+            ++e;
+        if (e < E) {
+            orc_expert_ffn_fp8(d, F, act, W1q, w1s, W2q, w2s, e, xq + (size_t)r * d, (double)xs[r],
+                               out + (size_t)n * d, h ? h + (size_t)n * F : NULL);
+        } else {
+            for (int o = 0; o < d; ++o)
+                out[(size_t)n * d + o] = 0.0;
+            if (h)
+                for (int f = 0; f < F; ++f)
+                    h[(size_t)n * F + f] = 0.0;
+        }
+    }
+}
+
+/* Second FP8 layer alone on given quantised hidden rows (codes hq [*][F],
+ * row scales hs): out[n] = W2^[e] * hq^[r] for r = rows[n]. */
+void orc_down_rows_fp8(int E, int d, int F, const int32_t* offsets, const uint8_t* hq, const float* hs,
+                       const uint8_t* W2q, const float* w2s, int nrows, const int32_t* rows, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int n = 0; n < nrows; ++n) {
+        int r = rows ? rows[n] : n;
+        int e = 0;
+        while (e < E && !(offsets[e] <= r && r < offsets[e + 1]))
+            ++e;
+        for (int o = 0; o < d; ++o) {
+            double s = 0.0;
+            if (e < E) {
+                const size_t row = (size_t)e * d + o;
+                for (int f = 0; f < F; ++f)
+                    s += orc_e4m3_decode(W2q[row * F + f]) * (double)w2s[row] *
+                         orc_e4m3_decode(hq[(size_t)r * F + f]) * (double)hs[r];
+            }
+            out[(size_t)n * d + o] = s;
+        }
+    }
+}
+
+/* FP8 layer output for ntok tokens: x_t (fp32 / bf16) is quantised per
+ * token, each kept choice runs orc_expert_ffn_fp8, and the outputs are mixed
+ * with the gate weights as in orc_forward_tokens. */
+void orc_forward_tokens_fp8(int d, int k, int F, int act, int dtype, const void* x, const uint8_t* W1q,
+                            const float* w1s, const uint8_t* W2q, const float* w2s, const int32_t* idx,
+                            const double* w, const int32_t* slot, int ntok, const int32_t* tokens, double* y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int n = 0; n < ntok; ++n) {
+        int t = tokens ? tokens[n] : n;
+        uint8_t* xq = (uint8_t*)malloc((size_t)d);
+        float xs;
+        double* o = (double*)malloc(sizeof(double) * (size_t)d);
+        double* yn = y + (size_t)n * d;
+        if (dtype == ORC_F32)
+            orc_quant_rows_fp8(1, d, dtype, (const float*)x + (size_t)t * d, xq, &xs);
+        else
+            orc_quant_rows_fp8(1, d, dtype, (const uint16_t*)x + (size_t)t * d, xq, &xs);
+        for (int i = 0; i < d; ++i)
+            yn[i] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            size_t a = (size_t)t * k + j;
+            if (slot[a] < 0)
+                continue;
+            orc_expert_ffn_fp8(d, F, act, W1q, w1s, W2q, w2s, idx[a], xq, (double)xs, o, NULL);
+            for (int i = 0; i < d; ++i)
+                yn[i] += w[a] * o[i];
+        }
+        free(o);
+        free(xq);
+    }
 }

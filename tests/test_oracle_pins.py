@@ -547,3 +547,123 @@ def test_shared_expert_is_dense_ffn_and_adds_unweighted(act):
     # zero shared weights leave the routed layer
     zero = oracle.shared_expert(x, Ws1, np.zeros_like(Ws2), act, F)
     assert not zero.any()
+
+
+# ---------------------------------------------------------------- FP8 experts
+# OCP FP8 E4M3 codes with power-of-two row scales (Skywork-MoE FP8 checkpoint and
+# "4090推理" FP8 inference; Megatron-Core page "关键特性": FP8 among the coming
+# features).  torch's float8_e4m3fn is the independent reference for the format.
+import torch  # noqa: E402
+
+
+def torch_e4m3(v):
+    """Codes of in-range values by torch's own conversion (ties to even)."""
+    t = torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_matches_torch_and_round_trips():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    finite = ~np.isnan(ref)
+    assert finite.sum() == 254 and np.array_equal(ours[finite], ref[finite]) and np.isnan(ours[~finite]).all()
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+    # every finite code is its own nearest code
+    assert np.array_equal(oracle.e4m3_encode(ours[finite]), codes[finite])
+
+
+def test_e4m3_encode_nearest_even_and_saturating():
+    v = np.concatenate([RNG.uniform(-448, 448, 3000), RNG.standard_normal(3000) * 0.01,
+                        RNG.uniform(-2 ** -6, 2 ** -6, 1000)]).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_encode(v), torch_e4m3(v))
+    # exact midpoints between neighbouring codes go to the even mantissa
+    vals = oracle.e4m3_decode(np.arange(0, 0x7E, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    enc = oracle.e4m3_encode(mids)
+    assert np.all(enc % 2 == 0)
+    assert np.array_equal(enc, torch_e4m3(mids))
+    # saturation instead of NaN above the largest finite value
+    assert list(oracle.e4m3_encode([448.0, 449.0, 464.0, 470.0, 479.9, 480.0, 1e6, -1e6, -470.0])) == \
+        [0x7E] * 7 + [0xFE, 0xFE]
+
+
+def test_fp8_row_scale_is_smallest_power_of_two():
+    for amax in list(RNG.uniform(1e-6, 1e4, 500)) + [448.0, 224.0, 224.0001, 1.0, 0.875 * 2 ** -3]:
+        e = oracle.fp8_scale_exp(amax)
+        assert amax <= 448 * 2.0 ** e and amax > 448 * 2.0 ** (e - 1)
+    assert oracle.fp8_scale_exp(0.0) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64"])
+def test_fp8_quant_rows_against_independent_quantiser(dtype):
+    R, K = 37, 96
+    v = (RNG.standard_normal((R, K)) * np.exp(RNG.uniform(-8, 8, (R, 1)))).astype(np.float32)
+    v[3] = 0.0
+    src = v if dtype == "f32" else moe_inputs.f32_to_bf16_bits(v) if dtype == "bf16" else v.astype(np.float64)
+    vals = oracle.to_f64(src) if dtype != "f64" else src
+    codes, scales = oracle.quant_rows_fp8(src)
+    for r in range(R):
+        amax = np.abs(vals[r]).max()
+        m, x = np.frexp(amax)
+        e = 0 if amax == 0 else (x - 9 if m <= 0.875 else x - 8)
+        assert scales[r] == np.float32(2.0 ** e)
+        assert np.array_equal(codes[r], torch_e4m3(vals[r] / 2.0 ** e))
+    deq = oracle.e4m3_decode(codes) * scales[:, None]
+    # within half a code step: relative 2^-4 for normals
+    assert np.all(np.abs(deq - vals) <= np.abs(vals) * 2.0 ** -4 + scales[:, None] * 2.0 ** -10)
+    assert not codes[3].any() and scales[3] == 1.0
+
+
+@pytest.mark.parametrize("act", [oracle.RELU, oracle.SWIGLU])
+def test_fp8_ffn_is_dequantised_dense_ffn(act):
+    E, d, F, n = 3, 64, 128, 41
+    n1 = 2 * F if act == oracle.SWIGLU else F
+    W1 = moe_inputs.f32_to_bf16_bits((RNG.standard_normal((E, n1, d)) * 0.05).astype(np.float32))
+    W2 = moe_inputs.f32_to_bf16_bits((RNG.standard_normal((E, d, F)) * 0.05).astype(np.float32))
+    W1q, w1s = oracle.quant_weights_fp8(W1)
+    W2q, w2s = oracle.quant_weights_fp8(W2)
+    x = moe_inputs.f32_to_bf16_bits(RNG.standard_normal((n, d)).astype(np.float32))
+    xq, xs = oracle.quant_rows_fp8(x)
+    offsets = np.array([0, 15, 15, n], np.int32)
+    out, h = oracle.ffn_rows_fp8(xq, xs, offsets, W1q, w1s, W2q, w2s, act, F, want_h=True)
+    W1d = oracle.e4m3_decode(W1q) * w1s[:, :, None]
+    W2d = oracle.e4m3_decode(W2q) * w2s[:, :, None]
+    xd = oracle.e4m3_decode(xq) * xs[:, None]
+    for r in range(n):
+        e = 0 if r < 15 else 2
+        u = W1d[e] @ xd[r]
+        hr = np.maximum(u, 0) if act == oracle.RELU else u[:F] * scipy.special.expit(u[:F]) * u[F:]
+        assert np.allclose(h[r], hr, rtol=1e-12, atol=1e-14)
+        # h is quantised per row by the independent quantiser before the down layer
+        m, xe = np.frexp(np.abs(hr).max())
+        es = xe - 9 if m <= 0.875 else xe - 8
+        hd = torch.from_numpy((hr / 2.0 ** es).astype(np.float32)).to(torch.float8_e4m3fn).double().numpy() * 2.0 ** es
+        assert np.allclose(out[r], W2d[e] @ hd, rtol=1e-12, atol=1e-14)
+    # the down layer alone on given quantised rows
+    hq, hs = oracle.quant_rows_fp8(h)
+    down = oracle.down_rows_fp8(hq, hs, offsets, W2q, w2s)
+    assert np.allclose(down, out, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_forward_tokens_recomposes_rows_and_combine():
+    T, d, E, k, F = 60, 64, 4, 2, 64
+    x = moe_inputs.f32_to_bf16_bits(RNG.standard_normal((T, d)).astype(np.float32))
+    W1q, w1s = oracle.quant_weights_fp8(moe_inputs.f32_to_bf16_bits(
+        (RNG.standard_normal((E, 2 * F, d)) * 0.05).astype(np.float32)))
+    W2q, w2s = oracle.quant_weights_fp8(moe_inputs.f32_to_bf16_bits(
+        (RNG.standard_normal((E, d, F)) * 0.05).astype(np.float32)))
+    z = RNG.standard_normal((T, E)).astype(np.float32)
+    idx, w = oracle.route(z, k)
+    disp = oracle.dispatch(idx, E, oracle.capacity(T, E, k, 0.8))
+    y = oracle.forward_tokens_fp8(x, W1q, w1s, W2q, w2s, idx, w, disp["slot"], oracle.SWIGLU, F)
+    xq, xs = oracle.quant_rows_fp8(x)
+    src = disp["src_token"]
+    yp = oracle.ffn_rows_fp8(xq[src], xs[src], disp["offsets"], W1q, w1s, W2q, w2s, oracle.SWIGLU, F)
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            if disp["slot"][t, j] >= 0:
+                ref[t] += w[t, j] * yp[disp["slot"][t, j]]
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-15)
+    assert not y[np.all(disp["slot"] < 0, axis=1)].any()
