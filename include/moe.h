@@ -21,6 +21,8 @@
  *   moe_shared_expert, moe_combine_shared
  *                    an ungated shared expert over all tokens, added in the
  *                    combine
+ *   moe_quantize_fp8, moe_expert_up_fp8, moe_expert_down_fp8, moe_forward_fp8
+ *                    the layer with FP8 (E4M3) expert weights and activations
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -234,6 +236,53 @@ moe_status moe_shared_expert(const moe_problem* p, int32_t Fs, const void* x, co
  * choices were all dropped gets y_shared[t]. */
 moe_status moe_combine_shared(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w,
                               const void* y_shared, void* y, void* stream);
+
+/* ---------------------------------------------------------------- FP8 experts
+ * Expert weights as OCP FP8 E4M3 codes (Skywork-MoE model card: an FP8
+ * checkpoint; Skywork news item, "4090推理": FP8-quantised inference;
+ * Megatron-Core page, "关键特性": FP8 among the coming features).  The pages
+ * fix no scheme; this one: every row of a weight matrix, every token row of x
+ * and every row of h carries a power-of-two scale s, the smallest with
+ * max|row| <= 448 s, and holds the E4M3 codes nearest to v / s (ties to even,
+ * saturating at 448).  The expert GEMMs multiply codes on gfx950's FP8 MFMA
+ * (fp32 accumulation) and apply row scale x weight-row scale to each output
+ * before the activation; h, y_perm and y are bf16.  Routing is the bf16
+ * layer's (gate on the bf16 x).  Requirements beyond the common limits:
+ * problem->dtype == MOE_BF16 (the activation type), d and F multiples of 128.
+ *   W1q [E][n1][d] codes, w1s [E][n1] fp32 scales (gate rows first for SwiGLU)
+ *   W2q [E][d][F] codes,  w2s [E][d] fp32 scales
+ *   xq [T][d] codes, xs [T];  hq [T*k][F] codes, hs [T*k]
+ * Codes must be 16-byte aligned. */
+
+/* Quantise rows rows of K values (src_dtype MOE_F32 or MOE_BF16; K a multiple
+ * of 64): codes [rows][K], scales [rows] = 2^e as above.  Usable for weights
+ * (one expert's matrix is E*n1 rows) and activations.  No workspace. */
+moe_status moe_quantize_fp8(const void* src, int32_t src_dtype, int64_t rows, int32_t K, uint8_t* codes,
+                            float* scales, void* stream);
+
+/* Bytes of workspace for moe_forward_fp8 (the bf16 workspace plus the codes
+ * and scales of x and h).  Host only. */
+moe_status moe_fp8_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* FP8 first expert layer: as moe_expert_up, with aq the codes of x
+ * (src_token given, rows gathered on the fly) or of x_perm (src_token NULL)
+ * and as their row scales (indexed like aq's rows). */
+moe_status moe_expert_up_fp8(const moe_problem* p, const uint8_t* aq, const float* as, const int32_t* src_token,
+                             const int32_t* offsets, const uint8_t* W1q, const float* w1s, void* h, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* FP8 second expert layer: y_perm[r] = (W2q[e] w2s[e]) (hq[r] hs[r]), bf16 out.
+ * ws as in moe_expert_down. */
+moe_status moe_expert_down_fp8(const moe_problem* p, const uint8_t* hq, const float* hs, const int32_t* offsets,
+                               const uint8_t* W2q, const float* w2s, void* y_perm, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* The whole layer with FP8 experts: route and permute as moe_forward, then
+ * quantise x per token, FP8 up-projection, quantise h per row, FP8
+ * down-projection, combine.  Needs ws_bytes >= moe_fp8_workspace_size. */
+moe_status moe_forward_fp8(const moe_problem* p, const void* x, const void* Wg, const float* bg, const uint8_t* W1q,
+                           const float* w1s, const uint8_t* W2q, const float* w2s, void* y, float* logits,
+                           const moe_route_info* info, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ loading fails loudly when the library has not been built.
 Entry points (same names as the C ABI): moe_capacity, moe_workspace_size,
 moe_route, moe_permute, moe_expert_up, moe_expert_down, moe_grouped_ffn,
 moe_combine, moe_forward, moe_router_stats, moe_shared_workspace_size,
-moe_shared_expert, moe_combine_shared.
+moe_shared_expert, moe_combine_shared, moe_quantize_fp8, moe_fp8_workspace_size,
+moe_expert_up_fp8, moe_expert_down_fp8, moe_forward_fp8.
 """
 from __future__ import annotations
 
@@ -24,7 +25,9 @@ MOE_F32, MOE_BF16 = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_capacity", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_expert_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_forward",
-           "moe_router_stats", "moe_shared_workspace_size", "moe_shared_expert", "moe_combine_shared")
+           "moe_router_stats", "moe_shared_workspace_size", "moe_shared_expert", "moe_combine_shared",
+           "moe_quantize_fp8", "moe_fp8_workspace_size", "moe_expert_up_fp8", "moe_expert_down_fp8",
+           "moe_forward_fp8")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +78,12 @@ def load() -> ctypes.CDLL:
     lib.moe_shared_workspace_size.argtypes = [PP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_shared_expert.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_combine_shared.argtypes = [PP, P, P, P, P, P, P]
+    lib.moe_quantize_fp8.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, P]
+    lib.moe_fp8_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_expert_up_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_expert_down_fp8.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_forward_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), P, ctypes.c_size_t,
+                                    P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = st
     _lib = lib
@@ -199,3 +208,37 @@ def moe_shared_expert(p, Fs, x, Ws1, Ws2, y_shared, ws, stream=None):
 def moe_combine_shared(p, y_perm, slot, topk_w, y_shared, y, stream=None):
     _check(load().moe_combine_shared(ctypes.byref(p), _ptr(y_perm), _ptr(slot), _ptr(topk_w), _ptr(y_shared),
                                      _ptr(y), _stream(stream)))
+
+
+def moe_quantize_fp8(src, codes, scales, stream=None):
+    """Rows of src (fp32 or bf16 tensor [rows, K]) to E4M3 codes (uint8 [rows, K])
+    and power-of-two row scales (fp32 [rows])."""
+    import torch
+    dt = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}[src.dtype]
+    rows, K = src.shape[0], src.numel() // max(src.shape[0], 1)
+    _check(load().moe_quantize_fp8(_ptr(src), dt, rows, K, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_fp8_workspace_size(p) -> int:
+    n = ctypes.c_size_t()
+    _check(load().moe_fp8_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def moe_expert_up_fp8(p, aq, a_scale, src_token, offsets, W1q, w1s, h, ws=None, stream=None):
+    _check(load().moe_expert_up_fp8(ctypes.byref(p), _ptr(aq), _ptr(a_scale), _ptr(src_token), _ptr(offsets),
+                                    _ptr(W1q), _ptr(w1s), _ptr(h), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_expert_down_fp8(p, hq, hs, offsets, W2q, w2s, y_perm, ws=None, stream=None):
+    _check(load().moe_expert_down_fp8(ctypes.byref(p), _ptr(hq), _ptr(hs), _ptr(offsets), _ptr(W2q), _ptr(w2s),
+                                      _ptr(y_perm), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_forward_fp8(p, x, Wg, bg, W1q, w1s, W2q, w2s, y, logits=None, info=None, ws=None, stream=None):
+    ri = None
+    if info:
+        ri = RouteInfo(*[_ptr(info.get(f)) for f, _ in RouteInfo._fields_])
+    _check(load().moe_forward_fp8(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1q), _ptr(w1s), _ptr(W2q),
+                                  _ptr(w2s), _ptr(y), _ptr(logits), ctypes.byref(ri) if ri is not None else None,
+                                  _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -27,6 +27,12 @@ size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows);
 hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w,
                               const void* y_add, int T, int d, int k, int max_rows, void* y, hipStream_t stream);
 size_t moe_router_stats_partial_bytes(int T, int E);
+hipError_t moe_launch_quantize_fp8(int dtype, const void* src, long long R, int K, uint8_t* codes, float* scales,
+                                   hipStream_t stream);
+hipError_t moe_launch_grouped_gemm_fp8(int epi, const void* A, const int32_t* gather, int gather_rows, const void* W,
+                                       void* C, const int32_t* offsets, int E, int K, int Nw, int Nout, int F,
+                                       int max_rows, int mean_rows, int ncu, float* partial, const float* a_scale,
+                                       const float* w_scale, hipStream_t stream);
 hipError_t moe_launch_router_stats(const float* logits, int T, int E, int k, int normalize, float lambda,
                                    const int32_t* counts, const int32_t* offsets, double* partial, float* frac,
                                    float* mean_prob, float* scalars, hipStream_t stream);
@@ -291,6 +297,70 @@ SharedLayout shared_layout_of(const moe_problem* p, int32_t Fs)
     L.partial = round_up((size_t)p->T * Fs * elem_bytes(p));
     L.total = L.partial + round_up(moe_grouped_gemm_partial_bytes(p->dtype, p->T));
     return L;
+}
+
+// ---- FP8 experts: E4M3 weights and activations with power-of-two row scales
+moe_status check_fp8(const moe_problem* p)
+{
+    CHECK(check_problem(p));
+    if (p->dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "the FP8 path takes bf16 activations (dtype MOE_BF16)");
+    if (p->d % 128 || p->F % 128)
+        return fail(MOE_ERR_UNSUPPORTED, "the FP8 path needs d and F multiples of 128 (d=%d, F=%d)", p->d, p->F);
+    return MOE_OK;
+}
+
+// The bf16 layout, then the codes and scales of x and h.
+struct LayoutFp8 {
+    Layout base;
+    size_t xq, xs, hq, hs, total;
+};
+
+LayoutFp8 layout_fp8_of(const moe_problem* p)
+{
+    LayoutFp8 L;
+    L.base = layout_of(p);
+    const size_t T = (size_t)p->T, k = (size_t)p->k;
+    size_t off = L.base.total;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round_up(bytes);
+        return at;
+    };
+    L.xq = take(T * p->d);
+    L.xs = take(T * 4);
+    L.hq = take(T * k * p->F);
+    L.hs = take(T * k * 4);
+    L.total = off;
+    return L;
+}
+
+moe_status check_ws_fp8(const moe_problem* p, const void* ws, size_t ws_bytes)
+{
+    const size_t need = layout_fp8_of(p).total;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    return check_ptr(ws, "ws", 16);
+}
+
+moe_status do_up_fp8(const moe_problem* p, const void* xq, const float* xs, const int32_t* gather,
+                     const int32_t* offsets, const void* W1q, const float* w1s, void* h, float* partial,
+                     hipStream_t s)
+{
+    const int epi = p->act == MOE_ACT_SWIGLU ? 2 : 1;
+    return hip_status(moe_launch_grouped_gemm_fp8(epi, xq, gather, p->T, W1q, h, offsets, p->E, p->d, n1_of(p), p->F,
+                                                  p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, xs, w1s,
+                                                  s),
+                      "FP8 expert up launch");
+}
+
+moe_status do_down_fp8(const moe_problem* p, const void* hq, const float* hs, const int32_t* offsets,
+                       const void* W2q, const float* w2s, void* y_perm, float* partial, hipStream_t s)
+{
+    return hip_status(moe_launch_grouped_gemm_fp8(0, hq, nullptr, 0, W2q, y_perm, offsets, p->E, p->F, p->d, p->d,
+                                                  p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, hs, w2s,
+                                                  s),
+                      "FP8 expert down launch");
 }
 
 }  // namespace
@@ -575,6 +645,143 @@ moe_status moe_combine_shared(const moe_problem* p, const void* y_perm, const in
     CHECK(check_ptr(y_shared, "y_shared", 16));
     CHECK(check_ptr(y, "y", 16));
     CHECK(do_combine(p, y_perm, slot, topk_w, y_shared, y, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_fp8_workspace_size(const moe_problem* p, size_t* bytes)
+{
+    CHECK(check_fp8(p));
+    if (!bytes)
+        return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = layout_fp8_of(p).total;
+    return ok();
+}
+
+moe_status moe_quantize_fp8(const void* src, int32_t src_dtype, int64_t rows, int32_t K, uint8_t* codes,
+                            float* scales, void* stream)
+{
+    if (src_dtype != MOE_F32 && src_dtype != MOE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "src_dtype=%d is neither MOE_F32 nor MOE_BF16", src_dtype);
+    if (rows < 0)
+        return fail(MOE_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
+    if (K < 64 || K > kMaxDim || K % 64)
+        return fail(MOE_ERR_UNSUPPORTED, "K=%d must be a multiple of 64 in [64, %d]", K, kMaxDim);
+    if (rows > ((long long)1 << 40) / K)
+        return fail(MOE_ERR_UNSUPPORTED, "too many rows");
+    if (rows == 0)
+        return ok();
+    CHECK(check_ptr(src, "src", 16));
+    CHECK(check_ptr(codes, "codes", 8));
+    CHECK(check_ptr(scales, "scales", 4));
+    CHECK(hip_status(moe_launch_quantize_fp8(src_dtype == MOE_F32 ? 0 : 1, src, rows, K, codes, scales,
+                                             (hipStream_t)stream),
+                     "FP8 quantisation launch"));
+    return ok();
+}
+
+moe_status moe_expert_up_fp8(const moe_problem* p, const uint8_t* aq, const float* as, const int32_t* src_token,
+                             const int32_t* offsets, const uint8_t* W1q, const float* w1s, void* h, void* ws,
+                             size_t ws_bytes, void* stream)
+{
+    CHECK(check_fp8(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(aq, src_token ? "xq" : "x_perm codes", 16));
+    CHECK(check_ptr(as, "activation scales", 4));
+    if (src_token)
+        CHECK(check_ptr(src_token, "src_token", 4));
+    CHECK(check_ptr(offsets, "offsets", 4));
+    CHECK(check_ptr(W1q, "W1q", 16));
+    CHECK(check_ptr(w1s, "w1s", 4));
+    CHECK(check_ptr(h, "h", 16));
+    if (ws)
+        CHECK(check_ws(p, ws, ws_bytes));
+    float* partial = ws ? at<float>(ws, layout_of(p).partial) : nullptr;
+    CHECK(do_up_fp8(p, aq, as, src_token, offsets, W1q, w1s, h, partial, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_expert_down_fp8(const moe_problem* p, const uint8_t* hq, const float* hs, const int32_t* offsets,
+                               const uint8_t* W2q, const float* w2s, void* y_perm, void* ws, size_t ws_bytes,
+                               void* stream)
+{
+    CHECK(check_fp8(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(hq, "hq", 16));
+    CHECK(check_ptr(hs, "hs", 4));
+    CHECK(check_ptr(offsets, "offsets", 4));
+    CHECK(check_ptr(W2q, "W2q", 16));
+    CHECK(check_ptr(w2s, "w2s", 4));
+    CHECK(check_ptr(y_perm, "y_perm", 16));
+    if (ws)
+        CHECK(check_ws(p, ws, ws_bytes));
+    float* partial = ws ? at<float>(ws, layout_of(p).partial) : nullptr;
+    CHECK(do_down_fp8(p, hq, hs, offsets, W2q, w2s, y_perm, partial, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_forward_fp8(const moe_problem* p, const void* x, const void* Wg, const float* bg, const uint8_t* W1q,
+                           const float* w1s, const uint8_t* W2q, const float* w2s, void* y, float* logits,
+                           const moe_route_info* info, void* ws, size_t ws_bytes, void* stream)
+{
+    CHECK(check_fp8(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_ptr(x, "x", 16));
+    CHECK(check_ptr(W1q, "W1q", 16));
+    CHECK(check_ptr(w1s, "w1s", 4));
+    CHECK(check_ptr(W2q, "W2q", 16));
+    CHECK(check_ptr(w2s, "w2s", 4));
+    CHECK(check_ptr(y, "y", 16));
+    if (Wg) {
+        CHECK(check_ptr(Wg, "Wg", 16));
+        if (bg)
+            CHECK(check_ptr(bg, "bg", 4));
+        if (logits)
+            CHECK(check_ptr(logits, "logits", 4));
+    } else {
+        if (!logits)
+            return fail(MOE_ERR_INVALID_ARG, "logits must be given when Wg is NULL");
+        CHECK(check_ptr(logits, "logits", 4));
+    }
+    CHECK(check_ws_fp8(p, ws, ws_bytes));
+    const LayoutFp8 LF = layout_fp8_of(p);
+    const Layout& L = LF.base;
+    moe_route_info r = {};
+    if (info)
+        r = *info;
+#define PICK(field, type) (r.field ? r.field : at<type>(ws, L.field))
+    int32_t* topk_idx = PICK(topk_idx, int32_t);
+    float* topk_w = PICK(topk_w, float);
+    int32_t* counts = PICK(counts, int32_t);
+    int32_t* offsets = PICK(offsets, int32_t);
+    int32_t* slot = PICK(slot, int32_t);
+    int32_t* src_token = PICK(src_token, int32_t);
+#undef PICK
+    const void* ptrs[] = {topk_idx, topk_w, counts, offsets, slot, src_token};
+    for (const void* q : ptrs)
+        CHECK(check_ptr(q, "route info field", 4));
+    float* z = logits ? logits : at<float>(ws, L.logits);
+    float* partial = at<float>(ws, L.partial);
+    void* h = at<char>(ws, L.h);
+    void* y_perm = at<char>(ws, L.y_perm);
+    uint8_t* xq = at<uint8_t>(ws, LF.xq);
+    float* xs = at<float>(ws, LF.xs);
+    uint8_t* hq = at<uint8_t>(ws, LF.hq);
+    float* hs = at<float>(ws, LF.hs);
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(do_route(p, Wg ? x : nullptr, Wg, bg, z, topk_idx, topk_w, s));
+    CHECK(do_permute(p, topk_idx, x, counts, offsets, slot, src_token, nullptr, ws, s));
+    CHECK(hip_status(moe_launch_quantize_fp8(1, x, p->T, p->d, xq, xs, s), "FP8 quantisation launch"));
+    CHECK(do_up_fp8(p, xq, xs, src_token, offsets, W1q, w1s, h, partial, s));
+    // h rows past offsets[E] are not written by the GEMM; quantising all T*k
+    // rows keeps the launch free of a host read of offsets (those codes are
+    // never used)
+    CHECK(hip_status(moe_launch_quantize_fp8(1, h, (long long)p->T * p->k, p->F, hq, hs, s),
+                     "FP8 quantisation launch"));
+    CHECK(do_down_fp8(p, hq, hs, offsets, W2q, w2s, y_perm, partial, s));
+    CHECK(do_combine(p, y_perm, slot, topk_w, nullptr, y, s));
     return ok();
 }
 

@@ -21,6 +21,11 @@ struct bf16_t {
     typedef uint16_t storage;
     static constexpr int kBytes = 2;
 };
+// OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa bits).
+struct fp8_t {
+    typedef uint8_t storage;
+    static constexpr int kBytes = 1;
+};
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 

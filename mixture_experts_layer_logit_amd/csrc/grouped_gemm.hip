@@ -17,6 +17,11 @@
 // projection reads the token rows of x directly, so the permuted copy x_perm
 // need not be written and read back).
 //
+// FP8 experts: A and W hold OCP E4M3 codes, each A row and each W row with a
+// power-of-two scale; the MFMA multiplies the codes (32x32x64 f8f6f4, twice
+// the bf16 rate) and the epilogue applies a_scale[row] * w_scale[e][col]
+// before the activation; the output is bf16.
+//
 // Design (gfx950):
 //  * Persistent grid, one block per resident slot.  The per-expert tile
 //    counts come from the device offsets (no host round trip), scanned in
@@ -51,6 +56,9 @@ namespace moe {
 
 enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 constexpr int kGemmMaxE = 1024;
 constexpr int kMaxSplit = 4;         // K parts of a tail tile
 constexpr int kSplitSlots = 256;     // partial tiles the workspace holds
@@ -69,7 +77,14 @@ struct GemmShape {
     static constexpr int kNch = RB / 16;                  // 16-byte chunks per row
     static constexpr int kRowsPerBlk = 1024 / RB;         // rows per 1 KB DMA block
     static constexpr int kSwzShift = (RB == 128) ? 1 : 2;  // log2(256 / RB)
-    static constexpr int kKSteps = RB / 32;               // MFMA k-steps per slice
+    // bytes of a row one MFMA k-step consumes: 32 (bf16 32x32x16, fp32 4 x
+    // 32x32x2), 64 (fp8 32x32x64); a lane holds kChunks 16-byte chunks of it
+    static constexpr int kStepBytes = ET::kBytes == 1 ? 64 : 32;
+    static constexpr int kChunks = kStepBytes / 32;
+    static constexpr int kKSteps = RB / kStepBytes;       // MFMA k-steps per slice
+    // one lane's share of an operand block for one k-step (kept as one
+    // register tuple, the MFMA's operand)
+    typedef typename std::conditional<ET::kBytes == 1, i32x8, i32x4>::type frag_t;
     static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
     static constexpr int kFM = kWaveM / 32, kFN = kWaveN / 32;
     static constexpr int kLdsA = BM * RB, kLdsB = BN * RB;
@@ -211,7 +226,6 @@ __device__ __forceinline__ int split_parts(int total, int G, int nk, bool enable
     return max(1, min(min(kMaxSplit, slots / tail), nk / (kMinSplitSlices / 2)));
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
@@ -284,17 +298,27 @@ struct Acc {
 // kFN weight blocks (a) and kFM activation blocks (b).
 template <typename S>
 struct Frag {
-    uint4 a[S::kFN], b[S::kFM];
+    typename S::frag_t a[S::kFN], b[S::kFM];
 };
 
 // Epilogue: activation and store of a tile from the wave's accumulators.
 // Lane holds row m = .. + (lane & 31), 4 consecutive columns per group.
-// `wave` is the wave slot of the tile whose accumulators these are.
-template <typename ET, typename S, int EPI>
-__device__ __forceinline__ void store_tile(const Acc<S>& acc, typename ET::storage* __restrict__ C, const TileDec& t,
-                                           int Nout, int ncols, int wave)
+// Per-row scales of an FP8 GEMM (null pointers: no scaling): a[source row
+// of A] and w[e * Nw + weight row].
+struct Scales {
+    const float* a;
+    const float* w;
+};
+
+// `wave` is the wave slot of the tile whose accumulators these are; OT the
+// stored element type.  With scales, u = acc * a_scale(row) * w_scale(col)
+// enters the epilogue (a_scale of row r is a[gather[r]] with a gather index).
+template <typename OT, typename S, int EPI>
+__device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::storage* __restrict__ C, const TileDec& t,
+                                           int Nout, int ncols, int wave, Scales sc, const int32_t* gather, int Nw,
+                                           int F)
 {
-    typedef typename ET::storage T;
+    typedef typename OT::storage T;
     const int lane = lane_id();
     const int wm = wave / S::WN, wn = wave % S::WN;
 #pragma unroll
@@ -303,27 +327,35 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename ET::stora
         if (m >= t.rows)
             continue;
         T* crow = C + (size_t)(t.row0 + m) * Nout;
+        float as = 1.0f;
+        if (sc.a)
+            as = sc.a[gather ? gather[t.row0 + m] : t.row0 + m];
+        const float* wsc = sc.w ? sc.w + (size_t)t.e * Nw : nullptr;
         constexpr int kJ = (EPI == EPI_SWIGLU) ? S::kFN / 2 : S::kFN;
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int nl = j * 32 + 8 * g4 + 4 * (lane >> 5);
+                const int n = t.n0 + ((EPI == EPI_SWIGLU) ? wn * (S::kWaveN / 2) : wn * S::kWaveN) + nl;
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float u = acc.v[i][j][4 * g4 + q];
+                    float up = (EPI == EPI_SWIGLU) ? acc.v[i][j + S::kFN / 2][4 * g4 + q] : 0.0f;
+                    if (wsc && n + q < ncols) {
+                        u *= as * wsc[n + q];
+                        if (EPI == EPI_SWIGLU)
+                            up *= as * wsc[F + n + q];
+                    }
                     if (EPI == EPI_RELU)
                         u = fmaxf(u, 0.0f);
-                    if (EPI == EPI_SWIGLU) {
-                        const float up = acc.v[i][j + S::kFN / 2][4 * g4 + q];
+                    if (EPI == EPI_SWIGLU)
                         u = u / (1.0f + __expf(-u)) * up;
-                    }
                     v[q] = u;
                 }
-                const int n = t.n0 + ((EPI == EPI_SWIGLU) ? wn * (S::kWaveN / 2) : wn * S::kWaveN) + nl;
                 if (n < ncols) {
-                    if constexpr (ET::kBytes == 2) {
+                    if constexpr (OT::kBytes == 2) {
                         uint2 o;
                         o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
                         o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
@@ -346,12 +378,12 @@ __device__ __forceinline__ size_t partial_index(int wave, int i, int j, int g, i
     return ((((size_t)(wave * S::kFM + i) * S::kFN + j) * 4 + g) * kWave + lane) * 4;
 }
 
-template <typename ET, typename S, int EPI>
+template <typename ET, typename OT, typename S, int EPI>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
 void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const int32_t* __restrict__ gather,
                              int gather_rows, const typename ET::storage* __restrict__ W,
-                             typename ET::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E,
-                             int K, int Nw, int Nout, int F, int max_rows, float* __restrict__ partial)
+                             typename OT::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E,
+                             int K, int Nw, int Nout, int F, int max_rows, float* __restrict__ partial, Scales sc)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only types; the host pass needs the stub only
     constexpr int kWaves = S::kWaves;
@@ -372,13 +404,15 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
     // per-lane LDS read offsets of each k-step's first 32-row block; blocks
     // 32 rows apart keep the same swizzle term, so the others sit at fixed
     // offsets from these
-    uint32_t rdA[S::kKSteps], rdB[S::kKSteps];
+    uint32_t rdA[S::kKSteps][S::kChunks], rdB[S::kKSteps][S::kChunks];
 #pragma unroll
-    for (int kk = 0; kk < S::kKSteps; ++kk) {
-        const int c = 2 * kk + (lane >> 5);
-        rdA[kk] = swz<S>(wm * S::kWaveM + (lane & 31), c);
-        rdB[kk] = S::kLdsA + swz<S>(wn * S::kWaveN + (lane & 31), c);
-    }
+    for (int kk = 0; kk < S::kKSteps; ++kk)
+#pragma unroll
+        for (int h = 0; h < S::kChunks; ++h) {
+            const int c = S::kChunks * (2 * kk + (lane >> 5)) + h;  // logical 16-byte chunk of the row
+            rdA[kk][h] = swz<S>(wm * S::kWaveM + (lane & 31), c);
+            rdB[kk][h] = S::kLdsA + swz<S>(wn * S::kWaveN + (lane & 31), c);
+        }
     // lane's place inside a 1 KB DMA block of rows [R0, R0 + 1024/RB): row
     // R0 + lane / kNch, physical chunk lane % kNch, which holds the logical
     // chunk of swz().  The swizzle term depends on the block only through the
@@ -490,19 +524,36 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         // k-step's MFMAs.
         Frag<S> fr0, fr1;
         auto read_frags = [&](const uint8_t* buf, int kk, Frag<S>& f) {
+            auto rd = [&](uint32_t off) { return *reinterpret_cast<const i32x4*>(buf + off); };
 #pragma unroll
-            for (int j = 0; j < S::kFN; ++j)
-                f.a[j] = *reinterpret_cast<const uint4*>(buf + rdB[kk] + j * 32 * S::RB);
+            for (int j = 0; j < S::kFN; ++j) {
+                if constexpr (S::kChunks == 2) {
+                    f.a[j].lo = rd(rdB[kk][0] + j * 32 * S::RB);
+                    f.a[j].hi = rd(rdB[kk][1] + j * 32 * S::RB);
+                } else {
+                    f.a[j] = rd(rdB[kk][0] + j * 32 * S::RB);
+                }
+            }
 #pragma unroll
-            for (int i = 0; i < S::kFM; ++i)
-                f.b[i] = *reinterpret_cast<const uint4*>(buf + rdA[kk] + i * 32 * S::RB);
+            for (int i = 0; i < S::kFM; ++i) {
+                if constexpr (S::kChunks == 2) {
+                    f.b[i].lo = rd(rdA[kk][0] + i * 32 * S::RB);
+                    f.b[i].hi = rd(rdA[kk][1] + i * 32 * S::RB);
+                } else {
+                    f.b[i] = rd(rdA[kk][0] + i * 32 * S::RB);
+                }
+            }
         };
         auto mfmas = [&](const Frag<S>& f) {
 #pragma unroll
             for (int i = 0; i < S::kFM; ++i)
 #pragma unroll
                 for (int j = 0; j < S::kFN; ++j) {
-                    if constexpr (ET::kBytes == 2) {
+                    if constexpr (ET::kBytes == 1) {
+                        // E4M3 x E4M3, unit block scales (E8M0 127 = 2^0)
+                        acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[j], f.b[i], acc.v[i][j],
+                                                                                      0, 0, 0, 127, 0, 127);
+                    } else if constexpr (ET::kBytes == 2) {
                         acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             __builtin_bit_cast(bf16x8, f.a[j]), __builtin_bit_cast(bf16x8, f.b[i]), acc.v[i][j],
                             0, 0, 0);
@@ -527,6 +578,31 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         // compile time.
         static_assert(S::kKSteps == 2 || S::kKSteps == 4, "2 or 4 k-steps per slice");
         auto slice = [&](int kt, const uint8_t* cur, int cur_stage, const uint8_t* nxt) {
+            if constexpr (S::kChunks == 2) {
+                // FP8: a k-step's fragments are 32 bytes per operand block,
+                // too wide to double-buffer beside 128 accumulators; they are
+                // refilled in place once the k-step's MFMAs are issued
+                // (scheduling fences keep the compiler from hoisting later
+                // k-steps' reads above the MFMAs, which would need a second
+                // register set for the fragments)
+                static_assert(S::kKSteps == 2, "FP8 slices are 128 bytes: 2 k-steps");
+                mfmas(fr0);
+                __builtin_amdgcn_sched_barrier(0);
+                read_frags(cur, 1, fr0);
+                __builtin_amdgcn_sched_barrier(0);
+                const bool more = kt + 1 < k1;
+                if (more) {
+                    wait_slices(min(S::S - 2, k1 - 2 - kt));
+                    lds_barrier();
+                    if (kt + S::S < k1)
+                        issue(kt + S::S, cur_stage);
+                }
+                mfmas(fr0);  // one call site: the accumulators keep one register set
+                __builtin_amdgcn_sched_barrier(0);
+                read_frags(nxt, 0, fr0);  // unconditional: see below
+                __builtin_amdgcn_sched_barrier(0);
+                return;
+            }
             read_frags(cur, 1, fr1);
             mfmas(fr0);
             if constexpr (S::kKSteps == 4) {
@@ -540,8 +616,13 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 lds_barrier();
                 if (kt + S::S < k1)
                     issue(kt + S::S, cur_stage);
-                read_frags(nxt, 0, fr0);
             }
+            // After the last slice this reads stale data nobody uses (an
+            // in-bounds LDS read; the next tile's __syncthreads waits for it
+            // before any DMA reuses the buffer).  Reading unconditionally
+            // keeps the fragment registers free of a merge of old and new
+            // values, which would cost register copies.
+            read_frags(nxt, 0, fr0);
             mfmas(fr1);
         };
         static_assert(S::kKSteps % 2 == 0, "k-steps per slice must be even");
@@ -559,7 +640,16 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         read_frags(lds0, 0, fr0);
         // slice k0 + n uses buffer n mod S
         int kt = k0;
-        if constexpr (S::S == 2) {
+        if constexpr (S::kChunks == 2) {
+            // FP8: one slice per iteration (the unrolled form below gives the
+            // accumulators of the wide FP8 MFMA several merge points, which
+            // the register allocator resolves with copies and spills)
+            static_assert(S::S == 2, "FP8 tiles use 2 LDS stages");
+            for (; kt < k1; ++kt) {
+                const bool odd = (kt - k0) & 1;
+                slice(kt, odd ? lds1 : lds0, odd ? 1 : 0, odd ? lds0 : lds1);
+            }
+        } else if constexpr (S::S == 2) {
             for (; kt + 2 <= k1; kt += 2) {
                 slice(kt, lds0, 0, lds1);
                 slice(kt + 1, lds1, 1, lds0);
@@ -592,7 +682,7 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         }
 
         if (slot < 0) {
-            store_tile<ET, S, EPI>(acc, C, t, Nout, ncols, wave);
+            store_tile<OT, S, EPI>(acc, C, t, Nout, ncols, wave, sc, gather, Nw, F);
         } else {
             float* dst = partial + (size_t)slot * S::kTileFloats;
 #pragma unroll
@@ -612,10 +702,10 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
 // Second pass of the tail split: one wavefront per (split tile, wave slot)
 // adds that slot's K parts in part order and stores its share of the tile
 // through the same epilogue (so every CU takes part, not one block per tile).
-template <typename ET, typename S, int EPI>
+template <typename OT, typename S, int EPI>
 __global__ __launch_bounds__(256) void moe_grouped_gemm_tail_kernel(
-    typename ET::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E, int K, int Nout, int F,
-    int max_rows, int G, const float* __restrict__ partial)
+    typename OT::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E, int K, int Nw, int Nout, int F,
+    int max_rows, int G, const float* __restrict__ partial, Scales sc, const int32_t* __restrict__ gather)
 {
     __shared__ int32_t s_pref[kGemmMaxE + 1];
     __shared__ int32_t s_wsum[256 / kWave];
@@ -659,7 +749,7 @@ __global__ __launch_bounds__(256) void moe_grouped_gemm_tail_kernel(
                         acc.v[i][jj][4 * g + 3] += p.w;
                     }
         }
-        store_tile<ET, S, EPI>(acc, C, t, Nout, ncols, wave);
+        store_tile<OT, S, EPI>(acc, C, t, Nout, ncols, wave, sc, gather, Nw, F);
     }
 }
 
@@ -668,61 +758,71 @@ __global__ __launch_bounds__(256) void moe_grouped_gemm_tail_kernel(
 namespace {
 using namespace moe;
 
-template <typename ET, typename S, int EPI>
-hipError_t launch_one(const void* A, const int32_t* gather, int gather_rows, const void* W, void* C,
-                      const int32_t* offsets, int E, int K, int Nw, int Nout, int F, int max_rows, int ncu,
-                      float* partial, hipStream_t stream)
+struct GemmArgs {
+    const void* A;
+    const int32_t* gather;
+    int gather_rows;
+    const void* W;
+    void* C;
+    const int32_t* offsets;
+    int E, K, Nw, Nout, F, max_rows, ncu;
+    float* partial;
+    Scales sc;
+    hipStream_t stream;
+};
+
+template <typename ET, typename OT, typename S, int EPI>
+hipError_t launch_one(const GemmArgs& g)
 {
     typedef typename ET::storage T;
+    typedef typename OT::storage TO;
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
-    const int ncols = (EPI == EPI_SWIGLU) ? F : Nout;
+    const int ncols = (EPI == EPI_SWIGLU) ? g.F : g.Nout;
     const long long ntn = (ncols + tile_cols - 1) / tile_cols;
     // upper bound on m-tiles: floor(P/BM) full tiles plus one partial per expert
-    const long long mt_max = max_rows / S::BM + (long long)(E < max_rows ? E : max_rows);
+    const long long mt_max = g.max_rows / S::BM + (long long)(g.E < g.max_rows ? g.E : g.max_rows);
     const long long tiles_max = mt_max * ntn;
-    long long grid = (long long)ncu * S::OCC;  // persistent: as many blocks as are resident at once
+    long long grid = (long long)g.ncu * S::OCC;  // persistent: as many blocks as are resident at once
     // without the split a grid beyond the tile count only idles; with it the
     // spare blocks take K parts of the tiles
-    if (tiles_max < grid && partial == nullptr)
+    if (tiles_max < grid && g.partial == nullptr)
         grid = (tiles_max + 7) / 8 * 8;
     if (grid < 1)
         grid = 1;
-    moe_grouped_gemm_kernel<ET, S, EPI><<<dim3((unsigned)grid), dim3(S::kThreads), 0, stream>>>(
-        (const T*)A, gather, gather_rows, (const T*)W, (T*)C, offsets, E, K, Nw, Nout, F, max_rows, partial);
+    moe_grouped_gemm_kernel<ET, OT, S, EPI><<<dim3((unsigned)grid), dim3(S::kThreads), 0, g.stream>>>(
+        (const T*)g.A, g.gather, g.gather_rows, (const T*)g.W, (TO*)g.C, g.offsets, g.E, g.K, g.Nw, g.Nout, g.F,
+        g.max_rows, g.partial, g.sc);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || partial == nullptr)
+    if (err != hipSuccess || g.partial == nullptr)
         return err;
     // at most kSplitSlots / 2 split tiles (each has >= 2 parts) x kWaves wave slots, 4 per block
-    moe_grouped_gemm_tail_kernel<ET, S, EPI><<<dim3(kSplitSlots / 2 * S::kWaves / 4), dim3(256), 0, stream>>>(
-        (T*)C, offsets, E, K, Nout, F, max_rows, (int)grid, partial);
+    moe_grouped_gemm_tail_kernel<OT, S, EPI><<<dim3(kSplitSlots / 2 * S::kWaves / 4), dim3(256), 0, g.stream>>>(
+        (TO*)g.C, g.offsets, g.E, g.K, g.Nw, g.Nout, g.F, g.max_rows, (int)grid, g.partial, g.sc, g.gather);
     return hipGetLastError();
 }
 
-template <typename ET, typename S>
-hipError_t launch_epi(int epi, const void* A, const int32_t* gather, int gather_rows, const void* W, void* C,
-                      const int32_t* offsets, int E, int K, int Nw, int Nout, int F, int max_rows, int ncu,
-                      float* partial, hipStream_t stream)
+template <typename ET, typename OT, typename S>
+hipError_t launch_epi(int epi, const GemmArgs& g)
 {
     if (epi == EPI_RELU)
-        return launch_one<ET, S, EPI_RELU>(A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu,
-                                           partial, stream);
+        return launch_one<ET, OT, S, EPI_RELU>(g);
     if (epi == EPI_SWIGLU)
-        return launch_one<ET, S, EPI_SWIGLU>(A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows,
-                                             ncu, partial, stream);
-    return launch_one<ET, S, EPI_NONE>(A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu,
-                                       partial, stream);
+        return launch_one<ET, OT, S, EPI_SWIGLU>(g);
+    return launch_one<ET, OT, S, EPI_NONE>(g);
 }
 }  // namespace
 
-// bf16 tile configurations (BM, BN, WM, WN, slice bytes, stages, blocks per
-// CU, m-tile group), picked from the mean rows per expert, which the host
-// knows without reading the device-side offsets:
+// Tile configurations (BM, BN, WM, WN, slice bytes, stages, blocks per CU,
+// m-tile group), picked from the mean rows per expert, which the host knows
+// without reading the device-side offsets:
 //   large   >= 512 rows per expert: 256 x 256 tiles, 8 waves (2 per SIMD, 128 x
 //           64 each), the densest tile that fits the register file; 2 x 64 KB
 //           of LDS stages
 //   medium  128..511 rows: 128 x 128 tiles, 4 waves, 2 blocks per CU
 //   small   < 128 rows: 64 x 256 tiles, 4 waves (short segments, so tall
 //           tiles would mostly compute padding)
+// The same shapes serve bf16 and FP8 (a 128-byte slice is 64 bf16 or 128 FP8
+// values of K).
 #ifndef MOE_LARGE_TILE
 #define MOE_LARGE_TILE 256, 256, 2, 4, 128, 2, 1, 8
 #endif
@@ -732,14 +832,16 @@ hipError_t launch_epi(int epi, const void* A, const int32_t* gather, int gather_
 #ifndef MOE_SMALL_TILE
 #define MOE_SMALL_TILE 64, 256, 1, 4, 128, 2, 1, 4
 #endif
+#define MOE_F32_TILE 128, 128, 2, 2, 128, 2, 1, 4
 
 // Workspace bytes the tail split needs for a problem with this mean rows per
 // expert (the partial tiles of the configuration the launcher picks).
+// dtype: 0 fp32, 1 bf16, 2 FP8.
 extern "C" size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows)
 {
     size_t tile_floats;
     if (dtype == 0)
-        tile_floats = GemmShape<f32_t, 128, 128, 2, 2, 128, 2, 1, 4>::kTileFloats;
+        tile_floats = GemmShape<f32_t, MOE_F32_TILE>::kTileFloats;
     else if (mean_rows >= 512)
         tile_floats = GemmShape<bf16_t, MOE_LARGE_TILE>::kTileFloats;
     else if (mean_rows >= 128)
@@ -760,15 +862,32 @@ extern "C" hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A,
                                               int K, int Nw, int Nout, int F, int max_rows, int mean_rows, int ncu,
                                               float* partial, hipStream_t stream)
 {
+    const GemmArgs g = {A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, partial,
+                        Scales{nullptr, nullptr}, stream};
     if (dtype == 0)
-        return launch_epi<f32_t, GemmShape<f32_t, 128, 128, 2, 2, 128, 2, 1, 4>>(
-            epi, A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, partial, stream);
+        return launch_epi<f32_t, f32_t, GemmShape<f32_t, MOE_F32_TILE>>(epi, g);
     if (mean_rows >= 512)
-        return launch_epi<bf16_t, GemmShape<bf16_t, MOE_LARGE_TILE>>(epi, A, gather, gather_rows, W, C, offsets, E,
-                                                                      K, Nw, Nout, F, max_rows, ncu, partial, stream);
+        return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_LARGE_TILE>>(epi, g);
     if (mean_rows >= 128)
-        return launch_epi<bf16_t, GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, A, gather, gather_rows, W, C, offsets, E,
-                                                                       K, Nw, Nout, F, max_rows, ncu, partial, stream);
-    return launch_epi<bf16_t, GemmShape<bf16_t, MOE_SMALL_TILE>>(epi, A, gather, gather_rows, W, C, offsets, E, K,
-                                                                  Nw, Nout, F, max_rows, ncu, partial, stream);
+        return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, g);
+    return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_SMALL_TILE>>(epi, g);
+}
+
+// FP8 grouped GEMM: A [rows][K] and W [E][Nw][K] hold E4M3 codes, a_scale
+// the scale of each A row (indexed by the source row when gathering),
+// w_scale [E][Nw] the scale of each weight row; C is bf16.  K must be a
+// multiple of 128.  Other arguments as moe_launch_grouped_gemm.
+extern "C" hipError_t moe_launch_grouped_gemm_fp8(int epi, const void* A, const int32_t* gather, int gather_rows,
+                                                  const void* W, void* C, const int32_t* offsets, int E, int K,
+                                                  int Nw, int Nout, int F, int max_rows, int mean_rows, int ncu,
+                                                  float* partial, const float* a_scale, const float* w_scale,
+                                                  hipStream_t stream)
+{
+    const GemmArgs g = {A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, partial,
+                        Scales{a_scale, w_scale}, stream};
+    if (mean_rows >= 512)
+        return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_LARGE_TILE>>(epi, g);
+    if (mean_rows >= 128)
+        return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_MEDIUM_TILE>>(epi, g);
+    return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_SMALL_TILE>>(epi, g);
 }

@@ -1,0 +1,104 @@
+// Per-row FP8 (OCP E4M3) quantisation (gfx950).
+//
+// FP8 experts (Skywork-MoE model card: an FP8 checkpoint; news item
+// "4090推理": FP8-quantised inference; Megatron-Core page, "关键特性": FP8
+// among the coming features).  Every row gets the smallest power-of-two
+// scale s with max|row| <= 448 s, and each value v becomes the E4M3 code
+// nearest to v / s (ties to even, magnitudes >= 448 saturate to 448).  The
+// scale is a power of two, so v / s is exact and every code is decided
+// exactly: the rounding below is done on the exact value, in integer-exact
+// fp32 steps.
+//
+// One wavefront per row: pass 1 finds max|v| (16-byte loads), pass 2 re-reads
+// the row and writes the codes (8 bytes per 8 values).
+#include "common.h"
+
+namespace moe {
+
+// Exponent e of the row scale 2^e: the smallest integer with
+// amax <= 448 * 2^e (0 for amax == 0).  With amax = m * 2^x, m in [0.5, 1):
+// 448 = 0.875 * 2^9, so e = x - 9 when m <= 0.875, else x - 8.
+__device__ __forceinline__ int fp8_scale_exp(float amax)
+{
+    if (!(amax > 0.0f))
+        return 0;
+    int x;
+    const float m = frexpf(amax, &x);
+    return m <= 0.875f ? x - 9 : x - 8;
+}
+
+// E4M3 code nearest to a finite v (ties to even; |v| >= 448 gives +-448).
+__device__ __forceinline__ uint32_t e4m3_encode(float v)
+{
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sgn = (bits >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a >= 448.0f)
+        return sgn | 0x7Eu;
+    if (a < 0.015625f) {  // below 2^-6: subnormal codes, step 2^-9 (a * 512 is exact)
+        return sgn | (uint32_t)rintf(a * 512.0f);
+    }
+    const uint32_t ab = __float_as_uint(a);
+    int ex = (int)((ab >> 23) & 0xffu) - 127;                       // a = m * 2^ex, m in [1, 2)
+    const float m = __uint_as_float((ab & 0x007fffffu) | 0x3f800000u);
+    float q = rintf(m * 8.0f);                                       // 8..16, exact product
+    if (q == 16.0f) {
+        q = 8.0f;
+        ex += 1;
+    }
+    return sgn | (uint32_t)((ex + 7) << 3) | ((uint32_t)q - 8u);
+}
+
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_quantize_fp8_kernel(const typename ET::storage* __restrict__ src,
+                                                               long long R, int K, uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales)
+{
+    const int lane = lane_id();
+    const long long r = (long long)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (r >= R)
+        return;
+    const typename ET::storage* row = src + (size_t)r * K;
+    const int nvec = K / 8;  // 8 values per step (16 B of bf16, 32 B of fp32)
+    float amax = 0.0f;
+    for (int c = lane; c < nvec; c += kWave) {
+        float f[8];
+        load8(row + (size_t)c * 8, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(f[i]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o));
+    const int e = fp8_scale_exp(amax);
+    uint8_t* out = codes + (size_t)r * K;
+    for (int c = lane; c < nvec; c += kWave) {
+        float f[8];
+        load8(row + (size_t)c * 8, f);
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            w[i / 4] |= e4m3_encode(ldexpf(f[i], -e)) << (8 * (i % 4));
+        *reinterpret_cast<uint2*>(out + (size_t)c * 8) = make_uint2(w[0], w[1]);
+    }
+    if (lane == 0)
+        scales[r] = ldexpf(1.0f, e);
+}
+
+}  // namespace moe
+
+// src: R rows of K values (dtype 0 fp32, 1 bf16), K a multiple of 8.
+extern "C" hipError_t moe_launch_quantize_fp8(int dtype, const void* src, long long R, int K, uint8_t* codes,
+                                              float* scales, hipStream_t stream)
+{
+    using namespace moe;
+    if (R <= 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((R + 3) / 4)), block(256);
+    if (dtype == 0)
+        moe_quantize_fp8_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)src, R, K, codes, scales);
+    else
+        moe_quantize_fp8_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)src, R, K, codes, scales);
+    return hipGetLastError();
+}

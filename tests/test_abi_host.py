@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_entry_points():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -189,3 +189,32 @@ def test_new_entry_points_reject_bad_arguments():
     assert lib.moe_router_stats(p0p, None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
     assert lib.moe_shared_expert(p0p, 128, None, None, None, None, None, 0, None) == moe.MOE_OK
     assert lib.moe_combine_shared(p0p, None, None, None, None, None, None) == moe.MOE_OK
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    lib = moe.load()
+    # activations must be bf16, d and F multiples of 128
+    for kw in (dict(dtype="f32"), dict(d=192), dict(F=320)):
+        a = dict(T=64, d=256, E=8, k=2, F=256)
+        a.update(kw)
+        p = moe.problem(a.pop("T"), a.pop("d"), a.pop("E"), a.pop("k"), a.pop("F"), **a)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_fp8_workspace_size(p)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    p = moe.problem(64, 256, 8, 2, 256)
+    pp = ctypes.byref(p)
+    ws = moe.moe_fp8_workspace_size(p)
+    assert ws > moe.moe_workspace_size(p)
+    r = lambda n: (n + 255) // 256 * 256
+    assert ws == moe.moe_workspace_size(p) + r(64 * 256) + r(64 * 4) + r(128 * 256) + r(128 * 4)
+    # quantiser: bad dtype, bad K, misaligned codes; zero rows is a no-op
+    assert lib.moe_quantize_fp8(FAKE, 7, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(FAKE, moe.MOE_BF16, 4, 96, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_fp8(FAKE, moe.MOE_BF16, 4, 64, FAKE + 4, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(None, moe.MOE_BF16, 0, 64, None, None, None) == moe.MOE_OK
+    # forward: short workspace; up/down: null scales
+    assert lib.moe_forward_fp8(pp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws - 1,
+                               None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_up_fp8(pp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down_fp8(pp, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
