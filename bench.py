@@ -37,7 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer fwd tokens/sec at Mixtral shape; grouped-GEMM % of bf16 MFMA peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA peaks
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_logit_amd", "csrc", "grouped_gemm.hip")
@@ -379,7 +379,78 @@ class Layer:
         cs = out["combine_shared"]
         cs["bytes"] = (P + 2 * T) * d * b + 8.0 * T * c.k
         cs["hbm_frac"] = cs["bytes"] / (cs["ms"] * 1e-3) / 1e9 / HBM_GBPS
+        del Ws1, Ws2, ysh, sws
+        if c.dtype == "bf16" and d % 128 == 0 and F % 128 == 0:
+            out["fp8_layer"] = self.time_fp8(steps)
         return out
+
+    def time_fp8(self, steps):
+        """The same layer with FP8 (E4M3) expert weights and activations: the
+        bf16 weights are quantised on the device, then the FP8 step (route,
+        permute, quantise x, FP8 up, quantise h, FP8 down, combine) is timed
+        stage by stage."""
+        import numpy as np
+        import torch
+        moe, p, c, s = self.moe, self.p, self.case, self.stream.cuda_stream
+        T, d, E, k, F = c.T, c.d, c.E, c.k, c.F
+        n1 = self.n1
+        with torch.cuda.stream(self.stream):
+            W1q = torch.empty(E, n1, d, dtype=torch.uint8, device="cuda")
+            w1s = torch.empty(E, n1, dtype=torch.float32, device="cuda")
+            W2q = torch.empty(E, d, F, dtype=torch.uint8, device="cuda")
+            w2s = torch.empty(E, d, dtype=torch.float32, device="cuda")
+            moe.moe_quantize_fp8(self.W1.view(E * n1, d), W1q.view(E * n1, d), w1s.view(-1), stream=s)
+            moe.moe_quantize_fp8(self.W2.view(E * d, F), W2q.view(E * d, F), w2s.view(-1), stream=s)
+            xq = torch.empty(T, d, dtype=torch.uint8, device="cuda")
+            xs = torch.empty(T, dtype=torch.float32, device="cuda")
+            hq = torch.empty(T * k, F, dtype=torch.uint8, device="cuda")
+            hs = torch.empty(T * k, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        names = ["route", "permute", "quantize_x", "expert_up", "quantize_h", "expert_down", "combine"]
+
+        def step(ev=None):
+            rec = (lambda i: ev[i].record(self.stream)) if ev is not None else (lambda i: None)
+            rec(0)
+            moe.moe_route(p, self.x if self.Wg is not None else None, self.Wg, self.bg, self.logits, self.idx,
+                          self.w, stream=s)
+            rec(1)
+            moe.moe_permute(p, self.idx, None, self.counts, self.offsets, self.slot, self.src, None, self.ws,
+                            stream=s)
+            rec(2)
+            moe.moe_quantize_fp8(self.x, xq, xs, stream=s)
+            rec(3)
+            moe.moe_expert_up_fp8(p, xq, xs, self.src, self.offsets, W1q, w1s, self.h, ws=self.ws, stream=s)
+            rec(4)
+            moe.moe_quantize_fp8(self.h, hq, hs, stream=s)
+            rec(5)
+            moe.moe_expert_down_fp8(p, hq, hs, self.offsets, W2q, w2s, self.y_perm, ws=self.ws, stream=s)
+            rec(6)
+            moe.moe_combine(p, self.y_perm, self.slot, self.w, self.y, stream=s)
+            rec(7)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) for i, n in enumerate(names)}
+        P = int(self.offsets[-1].item())
+        up, down = 2.0 * P * d * n1, 2.0 * P * F * d
+        peak = PEAK_TFLOPS["fp8"]
+        return {
+            "tokens_per_s": T * steps / elapsed,
+            "ms_per_step": elapsed * 1e3 / steps,
+            "stage_ms": stage_ms,
+            "up_tflops": up / (stage_ms["expert_up"] * 1e-3) / 1e12,
+            "up_frac_of_fp8_peak": up / (stage_ms["expert_up"] * 1e-3) / 1e12 / peak,
+            "grouped_gemm_pct_of_fp8_peak": 100.0 * (up + down) / ((stage_ms["expert_up"] + stage_ms["expert_down"])
+                                                                   * 1e-3) / 1e12 / peak,
+            "weights": "E4M3 codes with power-of-two row scales, quantised on the device from the bf16 weights",
+        }
 
 
 if __name__ == "__main__":

@@ -666,7 +666,7 @@ moe_status moe_quantize_fp8(const void* src, int32_t src_dtype, int64_t rows, in
         return fail(MOE_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
     if (K < 64 || K > kMaxDim || K % 64)
         return fail(MOE_ERR_UNSUPPORTED, "K=%d must be a multiple of 64 in [64, %d]", K, kMaxDim);
-    if (rows > ((long long)1 << 40) / K)
+    if (rows > ((long long)1 << 40) / K || rows > INT32_MAX)
         return fail(MOE_ERR_UNSUPPORTED, "too many rows");
     if (rows == 0)
         return ok();

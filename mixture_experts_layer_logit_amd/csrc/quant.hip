@@ -9,8 +9,9 @@
 // exactly: the rounding below is done on the exact value, in integer-exact
 // fp32 steps.
 //
-// One wavefront per row: pass 1 finds max|v| (16-byte loads), pass 2 re-reads
-// the row and writes the codes (8 bytes per 8 values).
+// bf16 rows up to 16384 values: one block per row, read once into registers.
+// Longer rows and fp32 rows: one wavefront per row, two passes (max|v|, then
+// codes).  Codes are written 8 bytes per 8 values.
 #include "common.h"
 
 namespace moe {
@@ -86,6 +87,60 @@ __global__ __launch_bounds__(256) void moe_quantize_fp8_kernel(const typename ET
         scales[r] = ldexpf(1.0f, e);
 }
 
+// bf16 rows of at most 256 * 8 * V values, one block of 256 threads per
+// row: the row is read once into registers (V 16-byte vectors per thread),
+// the block finds max|v| (wavefront shuffles, then the 4 wavefronts through
+// LDS) and writes the codes from the registers, so the row crosses HBM once.
+template <int V>
+__global__ __launch_bounds__(256) void moe_quantize_fp8_bf16_kernel(const uint16_t* __restrict__ src, int K,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    float* __restrict__ scales)
+{
+    __shared__ float s_max[4];
+    const long long r = blockIdx.x;
+    const uint4* row = reinterpret_cast<const uint4*>(src + (size_t)r * K);
+    const int nvec = K / 8;
+    uint4 buf[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        buf[i] = c < nvec ? row[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        float f[8];
+        unpack8(buf[i], f, bf16_t{});
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            amax = fmaxf(amax, fabsf(f[q]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (lane_id() == 0)
+        s_max[threadIdx.x / kWave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    const int e = fp8_scale_exp(amax);
+    uint8_t* out = codes + (size_t)r * K;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < nvec) {
+            float f[8];
+            unpack8(buf[i], f, bf16_t{});
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                w[q / 4] |= e4m3_encode(ldexpf(f[q], -e)) << (8 * (q % 4));
+            *reinterpret_cast<uint2*>(out + (size_t)c * 8) = make_uint2(w[0], w[1]);
+        }
+    }
+    if (threadIdx.x == 0)
+        scales[r] = ldexpf(1.0f, e);
+}
+
 }  // namespace moe
 
 // src: R rows of K values (dtype 0 fp32, 1 bf16), K a multiple of 8.
@@ -96,9 +151,18 @@ extern "C" hipError_t moe_launch_quantize_fp8(int dtype, const void* src, long l
     if (R <= 0)
         return hipSuccess;
     const dim3 grid((unsigned)((R + 3) / 4)), block(256);
+    const int per_thread = (K / 8 + 255) / 256;  // 16-byte bf16 vectors per thread, one block per row
+    const uint16_t* sb = (const uint16_t*)src;
+    const dim3 rows((unsigned)R);
     if (dtype == 0)
         moe_quantize_fp8_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)src, R, K, codes, scales);
+    else if (per_thread <= 2)
+        moe_quantize_fp8_bf16_kernel<2><<<rows, block, 0, stream>>>(sb, K, codes, scales);
+    else if (per_thread <= 4)
+        moe_quantize_fp8_bf16_kernel<4><<<rows, block, 0, stream>>>(sb, K, codes, scales);
+    else if (per_thread <= 8)
+        moe_quantize_fp8_bf16_kernel<8><<<rows, block, 0, stream>>>(sb, K, codes, scales);
     else
-        moe_quantize_fp8_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)src, R, K, codes, scales);
+        moe_quantize_fp8_kernel<bf16_t><<<grid, block, 0, stream>>>(sb, R, K, codes, scales);
     return hipGetLastError();
 }

@@ -87,10 +87,13 @@ def routing(case, inp):
 
 
 # ------------------------------------------------------------------ quantisation
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_quantize_fp8_bit_exact(dtype):
-    print(f"[fp8-quant] {dtype}", flush=True)
-    R, K = 517, 384
+@pytest.mark.parametrize("dtype,K", [("bf16", 384), ("f32", 384), ("bf16", 4096), ("bf16", 14336),
+                                     ("bf16", 16384), ("bf16", 20480), ("f32", 14336)])
+def test_quantize_fp8_bit_exact(dtype, K):
+    # bf16 rows up to 16384 values take the register-resident kernel, longer
+    # rows and fp32 rows the two-pass one
+    print(f"[fp8-quant] {dtype} K={K}", flush=True)
+    R = 517 if K <= 4096 else 67
     v = (RNG.standard_normal((R, K)) * np.exp(RNG.uniform(-20, 20, (R, 1)))).astype(np.float32)
     v[0] = 0.0                                    # zero row: scale 1, codes 0
     v[1] = 448.0 * 2.0 ** -3                      # exactly at a scale boundary
