@@ -50,6 +50,13 @@
  *                 max|row| <= 448 s, and its codes are the E4M3 values
  *                 nearest to v / s (ties to even, saturating at 448).  The
  *                 products are of the dequantised values code * s.
+ *   - backward:   the gradient of the layer (all throughput figures on the
+ *                 pages are for training: Skywork news "训练Infra", FastMoE
+ *                 page "特色三", Megatron-Core page "训练效果与性能实测").  The
+ *                 chain rule through the combine, both expert layers, the
+ *                 softmax, the normalisation and the gate; the top-k choice
+ *                 and the capacity drops are piecewise constant and pass no
+ *                 gradient (a dropped choice does not touch y at all).
  *   - router by-products: the quantities the load-balancing auxiliary loss,
  *                 its adaptive coefficient and the Z-loss are built from
  *                 (Megatron-Core page, "MoE负载均衡的挑战与应对": an auxiliary
@@ -629,4 +636,161 @@ void orc_forward_tokens_fp8(int d, int k, int F, int act, int dtype, const void*
         free(o);
         free(xq);
     }
+}
+
+/* ---------------------------------------------------------------- backward */
+
+/* Gradient of the layer output y with respect to its inputs and weights,
+ * given dy = dL/dy [T][d] (dtype) and the forward's routing: z32 [T][E] the
+ * fp32 logits the routing used, idx [T][k], slot [T][k] (-1 = dropped).
+ * Per token t and kept choice j (expert e, weight w = p[t,e]):
+ *   u = W1[e] x_t, h = act(u), o = W2[e] h, y_t += w o
+ *   dw_j = <dy_t, o>;  do = w dy_t
+ *   dW2[e] += do h^T;  dh = W2[e]^T do
+ *   ReLU: du = dh [u > 0];  SwiGLU (g = u[:F], v = u[F:], h = silu(g) v):
+ *     dg = dh v silu'(g), dv = dh silu(g), silu'(g) = s (1 + g (1 - s)), s = 1/(1+e^-g)
+ *   dW1[e] += du x_t^T;  dx_t += W1[e]^T du
+ * Router: dp[e] = dw_j for the kept choice j on expert e (0 otherwise);
+ *   ds = p (dp - <p, dp>)   (softmax);
+ *   dz = ds, or with the normalisation s = lambda zh, zh = (z - mu)/sigma:
+ *   dz = (lambda/sigma) (ds - mean(ds) - zh mean(ds zh)); sigma == 0 gives 0.
+ * Gate: dWg[e] += dz[e] x_t, dbg[e] += dz[e], dx_t += sum_e dz[e] Wg[e].
+ * Outputs (double): dx [T][d], dWg [E][d], dbg [E], dW1 [E][n1][d], dW2 [E][d][F];
+ * Wg == NULL means the logits were given (no gate): dWg, dbg and the gate term
+ * of dx are skipped.  dz (nullable) [T][E] receives the logit gradient. */
+void orc_backward(int T, int d, int E, int k, int F, int act, int dtype, int normalize, double lambda,
+                  const void* x, const void* Wg, const void* W1, const void* W2, const float* z32,
+                  const int32_t* idx, const int32_t* slot, const void* dy, double* dx, double* dWg, double* dbg,
+                  double* dW1, double* dW2, double* dz_out)
+{
+    const size_t n1 = (act == ORC_SWIGLU) ? 2 * (size_t)F : (size_t)F;
+    memset(dWg, 0, sizeof(double) * (size_t)E * d);
+    memset(dbg, 0, sizeof(double) * (size_t)E);
+    memset(dW1, 0, sizeof(double) * (size_t)E * n1 * d);
+    memset(dW2, 0, sizeof(double) * (size_t)E * d * F);
+    double* xt = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dyt = (double*)malloc(sizeof(double) * (size_t)d);
+    double* u = (double*)malloc(sizeof(double) * n1);
+    double* h = (double*)malloc(sizeof(double) * (size_t)F);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dh = (double*)malloc(sizeof(double) * (size_t)F);
+    double* du = (double*)malloc(sizeof(double) * n1);
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)E);
+    double* dzt = (double*)malloc(sizeof(double) * (size_t)E);
+    for (int t = 0; t < T; ++t) {
+        double* dxt = dx + (size_t)t * d;
+        for (int i = 0; i < d; ++i) {
+            xt[i] = elem(dtype, x, (size_t)t * d + i);
+            dyt[i] = elem(dtype, dy, (size_t)t * d + i);
+            dxt[i] = 0.0;
+        }
+        orc_gate_probs(E, z32 + (size_t)t * E, normalize, lambda, p);
+        for (int e = 0; e < E; ++e)
+            dp[e] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            const size_t a = (size_t)t * k + j;
+            if (slot[a] < 0)
+                continue;
+            const int e = idx[a];
+            const double w = p[e];
+            const size_t w1e = (size_t)e * n1 * d, w2e = (size_t)e * d * F;
+            for (size_t n = 0; n < n1; ++n) {
+                double s = 0.0;
+                for (int i = 0; i < d; ++i)
+                    s += elem(dtype, W1, w1e + n * d + i) * xt[i];
+                u[n] = s;
+            }
+            for (int f = 0; f < F; ++f) {
+                if (act == ORC_RELU) {
+                    h[f] = u[f] > 0.0 ? u[f] : 0.0;
+                } else {
+                    const double g = u[f], v = u[F + f];
+                    h[f] = g / (1.0 + exp(-g)) * v;
+                }
+            }
+            double dw = 0.0;
+            for (int i = 0; i < d; ++i) {
+                double s = 0.0;
+                for (int f = 0; f < F; ++f)
+                    s += elem(dtype, W2, w2e + (size_t)i * F + f) * h[f];
+                o[i] = s;
+                dw += dyt[i] * s;
+            }
+            dp[e] += dw;
+            /* do = w dy: dW2 and dh */
+            for (int f = 0; f < F; ++f)
+                dh[f] = 0.0;
+            for (int i = 0; i < d; ++i) {
+                const double doi = w * dyt[i];
+                for (int f = 0; f < F; ++f) {
+                    dW2[w2e + (size_t)i * F + f] += doi * h[f];
+                    dh[f] += elem(dtype, W2, w2e + (size_t)i * F + f) * doi;
+                }
+            }
+            for (int f = 0; f < F; ++f) {
+                if (act == ORC_RELU) {
+                    du[f] = u[f] > 0.0 ? dh[f] : 0.0;
+                } else {
+                    const double g = u[f], v = u[F + f];
+                    const double sg = 1.0 / (1.0 + exp(-g));
+                    const double silu = g * sg;
+                    du[f] = dh[f] * v * sg * (1.0 + g * (1.0 - sg));
+                    du[F + f] = dh[f] * silu;
+                }
+            }
+            for (size_t n = 0; n < n1; ++n)
+                for (int i = 0; i < d; ++i) {
+                    dW1[w1e + n * d + i] += du[n] * xt[i];
+                    dxt[i] += elem(dtype, W1, w1e + n * d + i) * du[n];
+                }
+        }
+        /* softmax, then the normalisation */
+        double pdp = 0.0;
+        for (int e = 0; e < E; ++e)
+            pdp += p[e] * dp[e];
+        for (int e = 0; e < E; ++e)
+            dzt[e] = p[e] * (dp[e] - pdp);
+        if (normalize) {
+            const float* zt = z32 + (size_t)t * E;
+            double mu = 0.0;
+            for (int e = 0; e < E; ++e)
+                mu += (double)zt[e];
+            mu /= E;
+            double var = 0.0;
+            for (int e = 0; e < E; ++e)
+                var += ((double)zt[e] - mu) * ((double)zt[e] - mu);
+            const double sigma = sqrt(var / E);
+            if (sigma == 0.0) {
+                for (int e = 0; e < E; ++e)
+                    dzt[e] = 0.0;
+            } else {
+                double m1 = 0.0, m2 = 0.0;
+                for (int e = 0; e < E; ++e) {
+                    const double zh = ((double)zt[e] - mu) / sigma;
+                    m1 += dzt[e];
+                    m2 += dzt[e] * zh;
+                }
+                m1 /= E;
+                m2 /= E;
+                for (int e = 0; e < E; ++e) {
+                    const double zh = ((double)zt[e] - mu) / sigma;
+                    dzt[e] = lambda / sigma * (dzt[e] - m1 - zh * m2);
+                }
+            }
+        }
+        if (dz_out)
+            for (int e = 0; e < E; ++e)
+                dz_out[(size_t)t * E + e] = dzt[e];
+        if (Wg) {
+            for (int e = 0; e < E; ++e) {
+                dbg[e] += dzt[e];
+                for (int i = 0; i < d; ++i) {
+                    dWg[(size_t)e * d + i] += dzt[e] * xt[i];
+                    dxt[i] += dzt[e] * elem(dtype, Wg, (size_t)e * d + i);
+                }
+            }
+        }
+    }
+    free(xt); free(dyt); free(u); free(h); free(o); free(dh); free(du); free(p); free(dp); free(dzt);
 }

@@ -667,3 +667,145 @@ def test_fp8_forward_tokens_recomposes_rows_and_combine():
                 ref[t] += w[t, j] * yp[disp["slot"][t, j]]
     assert np.allclose(y, ref, rtol=1e-13, atol=1e-15)
     assert not y[np.all(disp["slot"] < 0, axis=1)].any()
+
+
+# ---------------------------------------------------------------- backward
+# The layer's gradient (training is what the pages measure: Skywork news "训练
+# Infra", FastMoE page "特色三", Megatron-Core page "训练效果与性能实测").  Pinned
+# against torch autograd in float64 on an independent forward written here, and
+# against central differences of the forward oracle.
+
+def torch_layer_grads(x, Wg, bg, W1, W2, z32, idx, slot, dy, act, F, normalize, lam):
+    """Independent float64 forward with autograd.  The logits take the fp32
+    values the routing used (straight-through: value z32, gradient of z)."""
+    f64 = lambda a: torch.tensor(oracle.to_f64(np.asarray(a)), dtype=torch.float64, requires_grad=True)
+    xt, W1t, W2t = f64(x), f64(W1), f64(W2)
+    Wgt = f64(Wg) if Wg is not None else None
+    bgt = torch.tensor(np.asarray(bg, np.float64), requires_grad=True) if bg is not None else None
+    zv = torch.tensor(np.asarray(z32, np.float64))
+    if Wgt is not None:
+        z = xt @ Wgt.T + (bgt if bgt is not None else 0.0)
+        z = z + (zv - z).detach()
+    else:
+        z = zv
+    if normalize:
+        mu = z.mean(dim=1, keepdim=True)
+        sd = ((z - mu) ** 2).mean(dim=1, keepdim=True).sqrt()
+        s = torch.where(sd > 0, lam * (z - mu) / torch.where(sd > 0, sd, torch.ones_like(sd)), torch.zeros_like(z))
+    else:
+        s = z
+    p = torch.softmax(s, dim=1)
+    T, k = idx.shape
+    ys = []
+    for t in range(T):
+        yt = torch.zeros(xt.shape[1], dtype=torch.float64)
+        for j in range(k):
+            if slot[t, j] < 0:
+                continue
+            e = int(idx[t, j])
+            u = W1t[e] @ xt[t]
+            if act == oracle.RELU:
+                hh = torch.relu(u)
+            else:
+                hh = torch.nn.functional.silu(u[:F]) * u[F:]
+            yt = yt + p[t, e] * (W2t[e] @ hh)
+        ys.append(yt)
+    y = torch.stack(ys)
+    (y * torch.tensor(oracle.to_f64(np.asarray(dy)))).sum().backward()
+    g = {"dx": xt.grad.numpy(), "dW1": W1t.grad.numpy(), "dW2": W2t.grad.numpy()}
+    if Wgt is not None:
+        g["dWg"] = Wgt.grad.numpy()
+        g["dbg"] = bgt.grad.numpy() if bgt is not None else None
+    return g
+
+
+@pytest.mark.parametrize("act,normalize,cf,dtype,gate", [
+    (oracle.SWIGLU, False, 0.0, "bf16", True),
+    (oracle.RELU, False, 0.7, "f32", True),
+    (oracle.SWIGLU, True, 1.0, "f32", True),
+    (oracle.RELU, True, 0.0, "bf16", False),
+])
+def test_backward_matches_torch_autograd(act, normalize, cf, dtype, gate):
+    T, d, E, k, F = 23, 64, 5, 2, 64
+    n1 = 2 * F if act == oracle.SWIGLU else F
+    cast = (lambda a: moe_inputs.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    x = cast(RNG.standard_normal((T, d)).astype(np.float32))
+    W1 = cast((RNG.standard_normal((E, n1, d)) * 0.1).astype(np.float32))
+    W2 = cast((RNG.standard_normal((E, d, F)) * 0.1).astype(np.float32))
+    dy = cast(RNG.standard_normal((T, d)).astype(np.float32))
+    if gate:
+        Wg = cast((RNG.standard_normal((E, d)) * 0.2).astype(np.float32))
+        bg = RNG.standard_normal(E).astype(np.float32)
+        _ze, z32 = oracle.gate_logits(x, Wg, bg)
+    else:
+        Wg = bg = None
+        z32 = RNG.standard_normal((T, E)).astype(np.float32)
+    idx, _w = oracle.route(z32, k, normalize, 1.5)
+    disp = oracle.dispatch(idx, E, oracle.capacity(T, E, k, cf))
+    g = oracle.backward(x, Wg, W1, W2, z32, idx, disp["slot"], dy, act, F, normalize, 1.5)
+    ref = torch_layer_grads(x, Wg, bg, W1, W2, z32, idx, disp["slot"], dy, act, F, normalize, 1.5)
+    for name in ("dx", "dW1", "dW2") + (("dWg", "dbg") if gate else ()):
+        a, b = g[name], ref[name]
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-12 * max(1.0, np.abs(b).max())), name
+    if not gate:
+        assert not g["dWg"].any() and not g["dbg"].any()
+
+
+def test_backward_central_differences():
+    """d(sum y*dy)/d(param) by central differences of the forward oracle."""
+    T, d, E, k, F = 7, 64, 4, 2, 64
+    act = oracle.SWIGLU
+    x = RNG.standard_normal((T, d)).astype(np.float32)
+    Wg = (RNG.standard_normal((E, d)) * 0.3).astype(np.float32)
+    bg = (np.arange(E) * 0.5).astype(np.float32)
+    W1 = (RNG.standard_normal((E, 2 * F, d)) * 0.1).astype(np.float32)
+    W2 = (RNG.standard_normal((E, d, F)) * 0.1).astype(np.float32)
+    dy = RNG.standard_normal((T, d)).astype(np.float32)
+
+    def loss(x, Wg, bg, W1, W2):
+        out = oracle.moe_forward(x, Wg, bg, W1, W2, k=k, F=F, act=act, normalize_flag=True, lam=0.8)
+        return float((out["y"] * dy.astype(np.float64)).sum()), out
+
+    _l0, out0 = loss(x, Wg, bg, W1, W2)
+    g = oracle.backward(x, Wg, W1, W2, out0["z32"], out0["topk_idx"], out0["slot"], dy, act, F, True, 0.8)
+    checks = [("x", (2, 5), "dx"), ("x", (6, 63), "dx"), ("Wg", (1, 10), "dWg"), ("bg", (3,), "dbg"),
+              ("W1", (out0["topk_idx"][0, 0], 3, 7), "dW1"), ("W1", (out0["topk_idx"][1, 1], F + 9, 2), "dW1"),
+              ("W2", (out0["topk_idx"][4, 0], 11, 13), "dW2")]
+    params = {"x": x, "Wg": Wg, "bg": bg, "W1": W1, "W2": W2}
+    for pname, at, gname in checks:
+        base = params[pname]
+        h = np.float32(2.0 ** -9) * max(1.0, abs(float(base[at])))
+        vals = []
+        for sgn in (1, -1):
+            q = {n: v.copy() for n, v in params.items()}
+            q[pname][at] = base[at] + sgn * h
+            l, out = loss(**q)
+            assert np.array_equal(out["topk_idx"], out0["topk_idx"])  # routing unchanged by the step
+            vals.append(l)
+        step = float(np.float32(base[at] + h)) - float(np.float32(base[at] - h))
+        fd = (vals[0] - vals[1]) / step
+        an = g[gname][at]
+        assert abs(fd - an) <= 2e-3 * max(1.0, abs(an)), (pname, at, fd, an)
+
+
+def test_backward_degenerate_cases():
+    T, d, E, k, F = 9, 64, 3, 1, 64
+    x = RNG.standard_normal((T, d)).astype(np.float32)
+    W1 = (RNG.standard_normal((E, F, d)) * 0.1).astype(np.float32)
+    W2 = (RNG.standard_normal((E, d, F)) * 0.1).astype(np.float32)
+    Wg = (RNG.standard_normal((E, d)) * 0.1).astype(np.float32)
+    dy = RNG.standard_normal((T, d)).astype(np.float32)
+    _ze, z32 = oracle.gate_logits(x, Wg, None)
+    idx, _ = oracle.route(z32, k)
+    # every choice dropped: y == 0 whatever the inputs, so every gradient is 0
+    gone = np.full((T, k), -1, np.int32)
+    g = oracle.backward(x, Wg, W1, W2, z32, idx, gone, dy, oracle.RELU, F)
+    assert not any(g[n].any() for n in ("dx", "dWg", "dbg", "dW1", "dW2"))
+    # constant logits under the normalisation: the scores are 0 whatever z, so dz == 0
+    zc = np.full((T, E), 0.25, np.float32)
+    slot = np.arange(T, dtype=np.int32)[:, None]
+    g = oracle.backward(x, None, W1, W2, zc, np.zeros((T, 1), np.int32), slot, dy, oracle.RELU, F, True, 1.0)
+    assert not g["dz"].any()
+    # a dz row sums to zero: softmax (and the standardisation) are shift invariant
+    g = oracle.backward(x, Wg, W1, W2, z32, idx, slot, dy, oracle.RELU, F, True, 2.0)
+    assert np.allclose(g["dz"].sum(axis=1), 0.0, atol=1e-12)
