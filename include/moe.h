@@ -23,6 +23,9 @@
  *                    combine
  *   moe_quantize_fp8, moe_expert_up_fp8, moe_expert_down_fp8, moe_forward_fp8
  *                    the layer with FP8 (E4M3) expert weights and activations
+ *   moe_forward_train, moe_backward
+ *                    training: the forward keeping its intermediates, and the
+ *                    gradients of every input and weight
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -236,6 +239,51 @@ moe_status moe_shared_expert(const moe_problem* p, int32_t Fs, const void* x, co
  * choices were all dropped gets y_shared[t]. */
 moe_status moe_combine_shared(const moe_problem* p, const void* y_perm, const int32_t* slot, const float* topk_w,
                               const void* y_shared, void* y, void* stream);
+
+/* ---------------------------------------------------------------- training
+ * Backward of the layer (every throughput figure on the pages is for
+ * training: Skywork news item "训练Infra", FastMoE page "特色三", Megatron-Core
+ * page "训练效果与性能实测").  The chain rule through the combine, both expert
+ * layers, the softmax, the normalisation and the gate; the top-k choice and
+ * the capacity drops pass no gradient (a dropped choice does not touch y).
+ * moe_forward_train is moe_forward keeping what the backward needs: logits,
+ * every info field, and the saved tensors below ([T*k] rows each, dtype). */
+typedef struct {
+    void* u;      /* [T*k][n1] pre-activation x W1[e]^T (gate then up columns for SwiGLU) */
+    void* h;      /* [T*k][F] activation output */
+    void* y_perm; /* [T*k][d] expert outputs */
+} moe_saved;
+
+/* The forward with logits (required, written or given as in moe_forward),
+ * info (required, every field) and saved filled in.  Needs ws_bytes >=
+ * moe_workspace_size. */
+moe_status moe_forward_train(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                             const void* W2, void* y, float* logits, const moe_route_info* info,
+                             const moe_saved* saved, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace for moe_backward (gradients of the permuted rows,
+ * transposed weights, transposed row operands of the weight gradients).  Host
+ * only.  MOE_ERR_UNSUPPORTED when an operand [max(d,F,n1)][T*k + 64E] exceeds
+ * 32-bit offsets. */
+moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* Gradients given dy = dL/dy [T][d] (dtype) and the forward's logits, info and
+ * saved tensors (from moe_forward_train on the same inputs):
+ *   dx [T][d] dtype; dW1 [E][n1][d], dW2 [E][d][F] fp32;
+ *   dWg [E][d], dbg [E] fp32 (required when Wg != NULL; Wg == NULL means the
+ *   logits were given and there is no gate gradient).
+ * Per kept choice (t, j, e, w): d_w = <dy_t, y_perm row>, do = w dy_t;
+ * dW2[e] += do h^T; dh = W2[e]^T do; du = act'(u) dh (ReLU: [u > 0]; SwiGLU:
+ * dg = dh v silu'(g), dv = dh silu(g)); dW1[e] += du x_t^T; dx_t += W1[e]^T du.
+ * Router: dp[e] = d_w of the kept choice on e; ds = p (dp - <p,dp>); with the
+ * normalisation dz = (lambda/sigma)(ds - mean ds - zh mean(ds zh)) (0 when
+ * sigma == 0), else dz = ds.  Gate: dWg = dz^T x, dbg = sum_t dz,
+ * dx += dz Wg.  fp32 accumulation; sums in fixed orders (the same bits on
+ * every run).  Needs ws_bytes >= moe_backward_workspace_size. */
+moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, const void* Wg, const void* W1,
+                        const void* W2, const float* logits, const moe_route_info* info, const moe_saved* saved,
+                        void* dx, float* dWg, float* dbg, float* dW1, float* dW2, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* ---------------------------------------------------------------- FP8 experts
  * Expert weights as OCP FP8 E4M3 codes (Skywork-MoE model card: an FP8

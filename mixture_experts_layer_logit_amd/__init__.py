@@ -9,7 +9,8 @@ Entry points (same names as the C ABI): moe_capacity, moe_workspace_size,
 moe_route, moe_permute, moe_expert_up, moe_expert_down, moe_grouped_ffn,
 moe_combine, moe_forward, moe_router_stats, moe_shared_workspace_size,
 moe_shared_expert, moe_combine_shared, moe_quantize_fp8, moe_fp8_workspace_size,
-moe_expert_up_fp8, moe_expert_down_fp8, moe_forward_fp8.
+moe_expert_up_fp8, moe_expert_down_fp8, moe_forward_fp8, moe_forward_train,
+moe_backward_workspace_size, moe_backward.
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_capacity", "moe_workspace
            "moe_permute", "moe_expert_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_forward",
            "moe_router_stats", "moe_shared_workspace_size", "moe_shared_expert", "moe_combine_shared",
            "moe_quantize_fp8", "moe_fp8_workspace_size", "moe_expert_up_fp8", "moe_expert_down_fp8",
-           "moe_forward_fp8")
+           "moe_forward_fp8", "moe_forward_train", "moe_backward_workspace_size", "moe_backward")
 
 
 class MoeError(RuntimeError):
@@ -45,6 +46,10 @@ class Problem(ctypes.Structure):
 class RouteInfo(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("slot", ctypes.c_void_p), ("src_token", ctypes.c_void_p)]
+
+
+class Saved(ctypes.Structure):
+    _fields_ = [("u", ctypes.c_void_p), ("h", ctypes.c_void_p), ("y_perm", ctypes.c_void_p)]
 
 
 _lib = None
@@ -84,6 +89,11 @@ def load() -> ctypes.CDLL:
     lib.moe_expert_down_fp8.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_forward_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), P, ctypes.c_size_t,
                                     P]
+    lib.moe_forward_train.argtypes = [PP, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), ctypes.POINTER(Saved), P,
+                                      ctypes.c_size_t, P]
+    lib.moe_backward_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_backward.argtypes = [PP, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), ctypes.POINTER(Saved), P, P, P,
+                                 P, P, P, ctypes.c_size_t, P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = st
     _lib = lib
@@ -242,3 +252,34 @@ def moe_forward_fp8(p, x, Wg, bg, W1q, w1s, W2q, w2s, y, logits=None, info=None,
     _check(load().moe_forward_fp8(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1q), _ptr(w1s), _ptr(W2q),
                                   _ptr(w2s), _ptr(y), _ptr(logits), ctypes.byref(ri) if ri is not None else None,
                                   _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def _route_info(info):
+    return RouteInfo(*[_ptr(info.get(f)) for f, _ in RouteInfo._fields_])
+
+
+def _saved(saved):
+    return Saved(*[_ptr(saved.get(f)) for f, _ in Saved._fields_])
+
+
+def moe_forward_train(p, x, Wg, bg, W1, W2, y, logits, info, saved, ws=None, stream=None):
+    """info: dict of every route-info tensor; saved: dict of u, h, y_perm tensors."""
+    ri, sv = _route_info(info), _saved(saved)
+    _check(load().moe_forward_train(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(y),
+                                    _ptr(logits), ctypes.byref(ri), ctypes.byref(sv), _ptr(ws), _nbytes(ws),
+                                    _stream(stream)))
+
+
+def moe_backward_workspace_size(p) -> int:
+    n = ctypes.c_size_t()
+    _check(load().moe_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def moe_backward(p, dy, x, Wg, W1, W2, logits, info, saved, dx, dWg, dbg, dW1, dW2, ws=None, stream=None):
+    ri = _route_info(info) if info is not None else None
+    sv = _saved(saved) if saved is not None else None
+    _check(load().moe_backward(ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(Wg), _ptr(W1), _ptr(W2), _ptr(logits),
+                               ctypes.byref(ri) if ri is not None else None,
+                               ctypes.byref(sv) if sv is not None else None, _ptr(dx), _ptr(dWg), _ptr(dbg),
+                               _ptr(dW1), _ptr(dW2), _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "quant.hip", "api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "quant.hip", "backward.hip", "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -22,11 +22,30 @@ hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, const void* x,
                               void* x_perm, int32_t* chunk_cnt, hipStream_t stream);
 hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const int32_t* gather, int gather_rows,
                                    const void* W, void* C, const int32_t* offsets, int E, int K, int Nw, int Nout,
-                                   int F, int max_rows, int mean_rows, int ncu, float* partial, hipStream_t stream);
+                                   int F, int max_rows, int mean_rows, int ncu, float* partial, const void* aux_in,
+                                   void* aux_out, int aux_ld, hipStream_t stream);
 size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows);
 hipError_t moe_launch_combine(int dtype, const void* y_perm, const int32_t* slot, const float* topk_w,
                               const void* y_add, int T, int d, int k, int max_rows, void* y, hipStream_t stream);
 size_t moe_router_stats_partial_bytes(int T, int E);
+hipError_t moe_launch_combine_bwd(int dtype, const void* dy, const void* y_perm, const int32_t* slot,
+                                  const float* topk_w, int T, int d, int k, int max_rows, void* d_yp, float* d_w,
+                                  hipStream_t stream);
+hipError_t moe_launch_router_bwd(const float* logits, const int32_t* topk_idx, const int32_t* slot, const float* d_w,
+                                 int T, int E, int k, int normalize, float lambda, float* dz, hipStream_t stream);
+hipError_t moe_launch_kofs(const int32_t* offsets, int E, int max_rows, int align, int32_t* kofs, hipStream_t stream);
+hipError_t moe_launch_transpose(int dtype, const void* src, int B, int R, int C, void* dst, hipStream_t stream);
+hipError_t moe_launch_seg_transpose(int dtype, const void* src, const int32_t* gather, int gather_rows,
+                                    const int32_t* offsets, const int32_t* kofs, int E, int max_rows, int C, int ld,
+                                    void* dst, hipStream_t stream);
+hipError_t moe_launch_unpermute_bwd(int dtype, const void* dx_perm, const int32_t* slot, int T, int d, int k,
+                                    int max_rows, const float* dz, const void* Wg, int E, void* dx, hipStream_t stream);
+size_t moe_gate_wgrad_partial_bytes(int T, int d, int E);
+hipError_t moe_launch_zero(float* p, size_t n, hipStream_t stream);
+hipError_t moe_launch_gate_wgrad(int dtype, const float* dz, const void* x, int T, int d, int E, float* partial,
+                                 float* dWg, float* dbg, hipStream_t stream);
+hipError_t moe_launch_grouped_gemm_kgrp(int dtype, const void* A, const void* W, float* C, const int32_t* kofs, int E,
+                                        int lda, int M, int N, int ncu, hipStream_t stream);
 hipError_t moe_launch_quantize_fp8(int dtype, const void* src, long long R, int K, uint8_t* codes, float* scales,
                                    hipStream_t stream);
 hipError_t moe_launch_grouped_gemm_fp8(int epi, const void* A, const int32_t* gather, int gather_rows, const void* W,
@@ -248,11 +267,12 @@ int mean_rows_of(const moe_problem* p)
 // partial: the tail-split workspace (nullable: no split).  gather
 // (nullable): A is x itself and permuted row r reads row gather[r] of x.
 moe_status do_up(const moe_problem* p, const void* A, const int32_t* gather, const int32_t* offsets, const void* W1,
-                 void* h, float* partial, hipStream_t s)
+                 void* h, float* partial, hipStream_t s, void* u_out = nullptr)
 {
     const int epi = p->act == MOE_ACT_SWIGLU ? 2 : 1;
     return hip_status(moe_launch_grouped_gemm(p->dtype, epi, A, gather, p->T, W1, h, offsets, p->E, p->d, n1_of(p),
-                                              p->F, p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, s),
+                                              p->F, p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, nullptr,
+                                              u_out, n1_of(p), s),
                       "expert up launch");
 }
 
@@ -260,7 +280,8 @@ moe_status do_down(const moe_problem* p, const void* h, const int32_t* offsets, 
                    float* partial, hipStream_t s)
 {
     return hip_status(moe_launch_grouped_gemm(p->dtype, 0, h, nullptr, 0, W2, y_perm, offsets, p->E, p->F, p->d,
-                                              p->d, p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, s),
+                                              p->d, p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, nullptr,
+                                              nullptr, 0, s),
                       "expert down launch");
 }
 
@@ -361,6 +382,56 @@ moe_status do_down_fp8(const moe_problem* p, const void* hq, const float* hs, co
                                                   p->F, p->T * p->k, mean_rows_of(p), cu_count(), partial, hs, w2s,
                                                   s),
                       "FP8 expert down launch");
+}
+
+// ---- backward
+constexpr int kSegAlign = 64;  // padded expert segments of the weight-gradient GEMMs' K
+
+struct LayoutBwd {
+    size_t d_yp, d_w, dz, du, dx_perm, W1T, W2T, kofs, d_ypT, hT, duT, xpT, gate, partial, total;
+    int ld;
+};
+
+LayoutBwd layout_bwd_of(const moe_problem* p)
+{
+    LayoutBwd L;
+    const size_t T = (size_t)p->T, k = (size_t)p->k, E = (size_t)p->E, d = (size_t)p->d, F = (size_t)p->F;
+    const size_t n1 = (size_t)n1_of(p), b = elem_bytes(p);
+    L.ld = (int)(((T * k + kSegAlign * E) + 63) / 64 * 64);
+    const size_t ld = (size_t)L.ld;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round_up(bytes);
+        return at;
+    };
+    L.d_yp = take(T * k * d * b);
+    L.d_w = take(T * k * 4);
+    L.dz = take(T * E * 4);
+    L.du = take(T * k * n1 * b);
+    L.dx_perm = take(T * k * d * b);
+    L.W1T = take(E * n1 * d * b);
+    L.W2T = take(E * d * F * b);
+    L.kofs = take((E + 1) * 4);
+    L.d_ypT = take(d * ld * b);
+    L.hT = take(F * ld * b);
+    L.duT = take(n1 * ld * b);
+    L.xpT = take(d * ld * b);
+    L.gate = take(moe_gate_wgrad_partial_bytes(p->T, p->d, p->E));
+    L.partial = take(moe_grouped_gemm_partial_bytes(p->dtype, mean_rows_of(p)));
+    L.total = off;
+    return L;
+}
+
+moe_status check_bwd(const moe_problem* p)
+{
+    CHECK(check_problem(p));
+    // the weight-gradient GEMMs address [rows][ld] operands with 32-bit offsets
+    const LayoutBwd L = layout_bwd_of(p);
+    const long long widest = std::max<long long>(std::max(p->d, p->F), n1_of(p));
+    if (widest * L.ld * (long long)elem_bytes(p) >= 0xF0000000LL)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward's transposed operands exceed 32-bit offsets");
+    return MOE_OK;
 }
 
 }  // namespace
@@ -625,10 +696,10 @@ moe_status moe_shared_expert(const moe_problem* p, int32_t Fs, const void* x, co
     const int n1s = p->act == MOE_ACT_SWIGLU ? 2 * Fs : Fs;
     hipStream_t s = (hipStream_t)stream;
     CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, epi, x, nullptr, 0, Ws1, h, nullptr, 1, p->d, n1s, Fs, Fs,
-                                             p->T, p->T, cu_count(), partial, s),
+                                             p->T, p->T, cu_count(), partial, nullptr, nullptr, 0, s),
                      "shared expert up launch"));
     CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, 0, h, nullptr, 0, Ws2, y_shared, nullptr, 1, Fs, p->d, p->d,
-                                             Fs, p->T, p->T, cu_count(), partial, s),
+                                             Fs, p->T, p->T, cu_count(), partial, nullptr, nullptr, 0, s),
                      "shared expert down launch"));
     return ok();
 }
@@ -782,6 +853,159 @@ moe_status moe_forward_fp8(const moe_problem* p, const void* x, const void* Wg, 
                      "FP8 quantisation launch"));
     CHECK(do_down_fp8(p, hq, hs, offsets, W2q, w2s, y_perm, partial, s));
     CHECK(do_combine(p, y_perm, slot, topk_w, nullptr, y, s));
+    return ok();
+}
+
+moe_status moe_forward_train(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                             const void* W2, void* y, float* logits, const moe_route_info* info,
+                             const moe_saved* saved, void* ws, size_t ws_bytes, void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    if (!info || !saved)
+        return fail(MOE_ERR_INVALID_ARG, "info and saved are required");
+    CHECK(check_ptr(x, "x", 16));
+    CHECK(check_ptr(W1, "W1", 16));
+    CHECK(check_ptr(W2, "W2", 16));
+    CHECK(check_ptr(y, "y", 16));
+    CHECK(check_ptr(logits, "logits", 4));
+    if (Wg) {
+        CHECK(check_ptr(Wg, "Wg", 16));
+        if (bg)
+            CHECK(check_ptr(bg, "bg", 4));
+    }
+    const void* rp[] = {info->topk_idx, info->topk_w, info->counts, info->offsets, info->slot, info->src_token};
+    for (const void* q : rp)
+        CHECK(check_ptr(q, "route info field", 4));
+    CHECK(check_ptr(saved->u, "saved u", 16));
+    CHECK(check_ptr(saved->h, "saved h", 16));
+    CHECK(check_ptr(saved->y_perm, "saved y_perm", 16));
+    CHECK(check_ws(p, ws, ws_bytes));
+    const Layout L = layout_of(p);
+    float* partial = at<float>(ws, L.partial);
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(do_route(p, Wg ? x : nullptr, Wg, bg, logits, info->topk_idx, info->topk_w, s));
+    if (gather_ok(p)) {
+        CHECK(do_permute(p, info->topk_idx, x, info->counts, info->offsets, info->slot, info->src_token, nullptr, ws,
+                         s));
+        CHECK(do_up(p, x, info->src_token, info->offsets, W1, saved->h, partial, s, saved->u));
+    } else {
+        void* x_perm = at<char>(ws, L.x_perm);
+        CHECK(do_permute(p, info->topk_idx, x, info->counts, info->offsets, info->slot, info->src_token, x_perm, ws,
+                         s));
+        CHECK(do_up(p, x_perm, nullptr, info->offsets, W1, saved->h, partial, s, saved->u));
+    }
+    CHECK(do_down(p, saved->h, info->offsets, W2, saved->y_perm, partial, s));
+    CHECK(do_combine(p, saved->y_perm, info->slot, info->topk_w, nullptr, y, s));
+    return ok();
+}
+
+moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes)
+{
+    CHECK(check_bwd(p));
+    if (!bytes)
+        return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = layout_bwd_of(p).total;
+    return ok();
+}
+
+moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, const void* Wg, const void* W1,
+                        const void* W2, const float* logits, const moe_route_info* info, const moe_saved* saved,
+                        void* dx, float* dWg, float* dbg, float* dW1, float* dW2, void* ws, size_t ws_bytes,
+                        void* stream)
+{
+    CHECK(check_bwd(p));
+    hipStream_t s = (hipStream_t)stream;
+    const int T = p->T, d = p->d, E = p->E, k = p->k, F = p->F, n1 = n1_of(p), rows = T * k;
+    if (T == 0) {  // no tokens: every weight gradient is zero
+        CHECK(check_ptr(dW1, "dW1", 16));
+        CHECK(check_ptr(dW2, "dW2", 16));
+        CHECK(hip_status(moe_launch_zero(dW1, (size_t)E * n1 * d, s), "zero fill launch"));
+        CHECK(hip_status(moe_launch_zero(dW2, (size_t)E * d * F, s), "zero fill launch"));
+        if (Wg) {
+            CHECK(check_ptr(dWg, "dWg", 4));
+            CHECK(check_ptr(dbg, "dbg", 4));
+            CHECK(hip_status(moe_launch_zero(dWg, (size_t)E * d, s), "zero fill launch"));
+            CHECK(hip_status(moe_launch_zero(dbg, (size_t)E, s), "zero fill launch"));
+        }
+        return ok();
+    }
+    if (!info || !saved)
+        return fail(MOE_ERR_INVALID_ARG, "info and saved are required");
+    CHECK(check_ptr(dy, "dy", 16));
+    CHECK(check_ptr(x, "x", 16));
+    CHECK(check_ptr(W1, "W1", 16));
+    CHECK(check_ptr(W2, "W2", 16));
+    CHECK(check_ptr(logits, "logits", 4));
+    const void* rp[] = {info->topk_idx, info->topk_w, info->offsets, info->slot, info->src_token};
+    for (const void* q : rp)
+        CHECK(check_ptr(q, "route info field", 4));
+    CHECK(check_ptr(saved->u, "saved u", 16));
+    CHECK(check_ptr(saved->h, "saved h", 16));
+    CHECK(check_ptr(saved->y_perm, "saved y_perm", 16));
+    CHECK(check_ptr(dx, "dx", 16));
+    CHECK(check_ptr(dW1, "dW1", 16));
+    CHECK(check_ptr(dW2, "dW2", 16));
+    if (Wg) {
+        CHECK(check_ptr(Wg, "Wg", 16));
+        CHECK(check_ptr(dWg, "dWg", 4));
+        CHECK(check_ptr(dbg, "dbg", 4));
+    }
+    const LayoutBwd L = layout_bwd_of(p);
+    if (ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, L.total);
+    CHECK(check_ptr(ws, "ws", 16));
+    const int dt = p->dtype == MOE_F32 ? 0 : 1;
+    void* d_yp = at<char>(ws, L.d_yp);
+    float* d_w = at<float>(ws, L.d_w);
+    float* dz = at<float>(ws, L.dz);
+    void* du = at<char>(ws, L.du);
+    void* dx_perm = at<char>(ws, L.dx_perm);
+    void* W1T = at<char>(ws, L.W1T);
+    void* W2T = at<char>(ws, L.W2T);
+    int32_t* kofs = at<int32_t>(ws, L.kofs);
+    float* partial = at<float>(ws, L.partial);
+    const int32_t* offsets = info->offsets;
+    // combine and router
+    CHECK(hip_status(moe_launch_combine_bwd(dt, dy, saved->y_perm, info->slot, info->topk_w, T, d, k, rows, d_yp, d_w,
+                                            s), "combine backward launch"));
+    CHECK(hip_status(moe_launch_router_bwd(logits, info->topk_idx, info->slot, d_w, T, E, k, p->normalize, p->lambda,
+                                           dz, s), "router backward launch"));
+    // input gradients of the expert layers: dh = d_yp W2[e] (+ activation backward), dx_perm = du W1[e]
+    CHECK(hip_status(moe_launch_transpose(dt, W2, E, d, F, W2T, s), "transpose launch"));
+    CHECK(hip_status(moe_launch_transpose(dt, W1, E, n1, d, W1T, s), "transpose launch"));
+    const int depi = p->act == MOE_ACT_SWIGLU ? 4 : 3;
+    CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, depi, d_yp, nullptr, 0, W2T, du, offsets, E, d, F, n1, F, rows,
+                                             mean_rows_of(p), cu_count(), partial, saved->u, nullptr, n1, s),
+                     "expert down backward launch"));
+    CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, 0, du, nullptr, 0, W1T, dx_perm, offsets, E, n1, d, d, d, rows,
+                                             mean_rows_of(p), cu_count(), partial, nullptr, nullptr, 0, s),
+                     "expert up backward launch"));
+    // weight gradients: per expert, reductions over its rows
+    CHECK(hip_status(moe_launch_kofs(offsets, E, rows, kSegAlign, kofs, s), "segment offsets launch"));
+    void* d_ypT = at<char>(ws, L.d_ypT);
+    void* hT = at<char>(ws, L.hT);
+    void* duT = at<char>(ws, L.duT);
+    void* xpT = at<char>(ws, L.xpT);
+    CHECK(hip_status(moe_launch_seg_transpose(dt, d_yp, nullptr, 0, offsets, kofs, E, rows, d, L.ld, d_ypT, s),
+                     "segment transpose launch"));
+    CHECK(hip_status(moe_launch_seg_transpose(dt, saved->h, nullptr, 0, offsets, kofs, E, rows, F, L.ld, hT, s),
+                     "segment transpose launch"));
+    CHECK(hip_status(moe_launch_seg_transpose(dt, du, nullptr, 0, offsets, kofs, E, rows, n1, L.ld, duT, s),
+                     "segment transpose launch"));
+    CHECK(hip_status(moe_launch_seg_transpose(dt, x, info->src_token, T, offsets, kofs, E, rows, d, L.ld, xpT, s),
+                     "segment transpose launch"));
+    CHECK(hip_status(moe_launch_grouped_gemm_kgrp(dt, d_ypT, hT, dW2, kofs, E, L.ld, d, F, cu_count(), s),
+                     "weight gradient launch"));
+    CHECK(hip_status(moe_launch_grouped_gemm_kgrp(dt, duT, xpT, dW1, kofs, E, L.ld, n1, d, cu_count(), s),
+                     "weight gradient launch"));
+    // input gradient, and the gate's
+    CHECK(hip_status(moe_launch_unpermute_bwd(dt, dx_perm, info->slot, T, d, k, rows, dz, Wg, E, dx, s),
+                     "un-permute backward launch"));
+    if (Wg)
+        CHECK(hip_status(moe_launch_gate_wgrad(dt, dz, x, T, d, E, at<float>(ws, L.gate), dWg, dbg, s),
+                         "gate gradient launch"));
     return ok();
 }
 

@@ -1,0 +1,462 @@
+// Backward of the MoE layer: the memory-bound pieces (gfx950).
+//
+// The layer's gradient (all throughput figures on the pages are for training:
+// Skywork news item "训练Infra", FastMoE page "特色三", Megatron-Core page
+// "训练效果与性能实测").  The expert GEMMs of the backward run on the grouped
+// GEMM kernel; this file holds what surrounds them:
+//   combine backward   d_yp[slot[t,j]] = w[t,j] dy[t];  d_w[t,j] = <dy[t], y_perm[slot[t,j]]>
+//   segment offsets    each expert's rows padded to a multiple of 64, for the
+//                      weight gradients' K ranges
+//   transposes         the weights (so the input-gradient GEMMs keep K
+//                      contiguous), and the permuted rows of d_yp, h, du, x
+//                      into [columns][padded rows] (so the weight-gradient
+//                      GEMMs reduce over rows with K contiguous)
+//   un-permute         dx[t] = sum_j dx_perm[slot[t,j]] + sum_e dz[t,e] Wg[e]
+//   gate gradients     dWg[e] = sum_t dz[t,e] x[t],  dbg[e] = sum_t dz[t,e]
+// Every sum runs in a fixed order (no atomics), so results are the same on
+// every run.
+#include "common.h"
+
+namespace moe {
+
+__device__ __forceinline__ float wave_sum_f(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+template <typename ET>
+__device__ __forceinline__ void load_vec(const typename ET::storage* p, float* f)  // 16 bytes
+{
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    if constexpr (ET::kBytes == 2) {
+        unpack8(raw, f, bf16_t{});
+    } else {
+        f[0] = __uint_as_float(raw.x);
+        f[1] = __uint_as_float(raw.y);
+        f[2] = __uint_as_float(raw.z);
+        f[3] = __uint_as_float(raw.w);
+    }
+}
+
+template <typename ET>
+__device__ __forceinline__ void store_vec(typename ET::storage* p, const float* f)  // 16 bytes
+{
+    uint4 o;
+    if constexpr (ET::kBytes == 2) {
+        o.x = f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16);
+        o.y = f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16);
+        o.z = f32_to_bf16_bits(f[4]) | (f32_to_bf16_bits(f[5]) << 16);
+        o.w = f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16);
+    } else {
+        o.x = __float_as_uint(f[0]);
+        o.y = __float_as_uint(f[1]);
+        o.z = __float_as_uint(f[2]);
+        o.w = __float_as_uint(f[3]);
+    }
+    *reinterpret_cast<uint4*>(p) = o;
+}
+
+// One wavefront per token.  Lane l owns 16-byte vectors l, l+64, ... of the
+// row; a dot product is the lanes' partial sums (each in vector order) added
+// by a fixed shuffle tree.  Slots at or past max_rows count as dropped.
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_combine_bwd_kernel(const typename ET::storage* __restrict__ dy,
+                                                              const typename ET::storage* __restrict__ y_perm,
+                                                              const int32_t* __restrict__ slot,
+                                                              const float* __restrict__ topk_w, int T, int d, int k,
+                                                              int max_rows, typename ET::storage* __restrict__ d_yp,
+                                                              float* __restrict__ d_w)
+{
+    constexpr int kPer = 16 / ET::kBytes;
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T)
+        return;
+    const int nvec = d / kPer;
+    int rows[8];
+    float w[8], dot[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
+        if (rows[j] >= max_rows)
+            rows[j] = -1;
+        w[j] = (j < k) ? topk_w[(size_t)t * k + j] : 0.0f;
+        dot[j] = 0.0f;
+    }
+    for (int v = lane; v < nvec; v += kWave) {
+        float g[kPer];
+        load_vec<ET>(dy + (size_t)t * d + (size_t)v * kPer, g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] < 0)
+                continue;
+            float yv[kPer], o[kPer];
+            load_vec<ET>(y_perm + (size_t)rows[j] * d + (size_t)v * kPer, yv);
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                dot[j] = fmaf(g[q], yv[q], dot[j]);
+                o[q] = w[j] * g[q];
+            }
+            store_vec<ET>(d_yp + (size_t)rows[j] * d + (size_t)v * kPer, o);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j >= k)
+            break;
+        const float s = wave_sum_f(dot[j]);
+        if (lane == 0)
+            d_w[(size_t)t * k + j] = rows[j] >= 0 ? s : 0.0f;
+    }
+}
+
+// Padded segment starts: kofs[e] = sum over e' < e of round_up(rows_e', align),
+// rows_e from offsets clamped into [0, max_rows] and made non-decreasing.  One
+// block of 1024 threads (E <= 1024).
+__global__ __launch_bounds__(1024) void moe_kofs_kernel(const int32_t* __restrict__ offsets, int E, int max_rows,
+                                                        int align, int32_t* __restrict__ kofs)
+{
+    __shared__ int32_t wsum[1024 / kWave];
+    const int e = threadIdx.x;
+    int padded = 0;
+    if (e < E) {
+        const int lo = min(max(offsets[e], 0), max_rows);
+        const int hi = min(max(offsets[e + 1], lo), max_rows);
+        padded = (hi - lo + align - 1) / align * align;
+    }
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    int incl = padded;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(incl, o);
+        if (lane >= o)
+            incl += n;
+    }
+    if (lane == kWave - 1)
+        wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w)
+        base += wsum[w];
+    if (e < E)
+        kofs[e] = base + incl - padded;
+    if (e == E - 1)
+        kofs[E] = base + incl;
+}
+
+// Batched transpose through LDS: dst[b][c][r] = src[b][r][c] for R x C
+// matrices, R and C multiples of 64.  Block: a 64 x 64 tile, 256 threads.
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_transpose_kernel(const typename ET::storage* __restrict__ src, int R,
+                                                            int C, typename ET::storage* __restrict__ dst)
+{
+    typedef typename ET::storage T;
+    __shared__ T tile[64][65];
+    const size_t b = blockIdx.z;
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+    const T* s = src + b * (size_t)R * C;
+    T* o = dst + b * (size_t)R * C;
+    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = ty + 4 * i;
+        tile[r][tx] = s[(size_t)(r0 + r) * C + c0 + tx];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c = ty + 4 * i;
+        o[(size_t)(c0 + c) * R + r0 + tx] = tile[tx][c];
+    }
+}
+
+// Permuted rows into [columns][padded rows]: dst[c][q] for padded position q
+// of expert e (kofs[e] <= q < kofs[e+1]) is src[row][c] with row =
+// offsets[e] + q - kofs[e] (through gather[row] when given) while that is
+// inside the expert's rows, else 0.  C a multiple of 64; ld (dst row stride)
+// a multiple of 64.  Block: 64 positions (blockIdx.x, the long axis) x 64
+// columns (blockIdx.y).
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_seg_transpose_kernel(const typename ET::storage* __restrict__ src,
+                                                                const int32_t* __restrict__ gather,
+                                                                int gather_rows, const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ kofs, int E,
+                                                                int max_rows, int C, int ld,
+                                                                typename ET::storage* __restrict__ dst)
+{
+    typedef typename ET::storage T;
+    __shared__ T tile[64][65];
+    __shared__ int32_t s_row[64];
+    const int q0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+    if (threadIdx.x < 64) {
+        const int q = q0 + threadIdx.x;
+        int row = -1;
+        if (q < kofs[E]) {
+            int lo = 0, hi = E;  // largest e with kofs[e] <= q
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (kofs[mid] <= q)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const int a = min(max(offsets[lo], 0), max_rows);
+            const int b = min(max(offsets[lo + 1], a), max_rows);
+            const int r = a + (q - kofs[lo]);
+            if (r < b) {
+                row = r;
+                if (gather) {
+                    row = gather[r];
+                    if (row < 0 || row >= gather_rows)
+                        row = -1;
+                }
+            }
+        }
+        s_row[threadIdx.x] = row;
+    }
+    __syncthreads();
+    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int qq = ty + 4 * i;
+        const int row = s_row[qq];
+        tile[qq][tx] = row >= 0 ? src[(size_t)row * C + c0 + tx] : (T)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c = ty + 4 * i;
+        dst[(size_t)(c0 + c) * ld + q0 + tx] = tile[tx][c];
+    }
+}
+
+// dx[t] = sum over kept j (in order) of dx_perm[slot[t,j]], plus, with a
+// gate, sum over e (in order) of dz[t,e] Wg[e].  One wavefront per token.
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_unpermute_bwd_kernel(const typename ET::storage* __restrict__ dx_perm,
+                                                                const int32_t* __restrict__ slot, int T, int d, int k,
+                                                                int max_rows, const float* __restrict__ dz,
+                                                                const typename ET::storage* __restrict__ Wg, int E,
+                                                                typename ET::storage* __restrict__ dx)
+{
+    constexpr int kPer = 16 / ET::kBytes;
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T)
+        return;
+    const int nvec = d / kPer;
+    int rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
+        if (rows[j] >= max_rows)
+            rows[j] = -1;
+    }
+    for (int v = lane; v < nvec; v += kWave) {
+        float acc[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q)
+            acc[q] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (rows[j] < 0)
+                continue;
+            float g[kPer];
+            load_vec<ET>(dx_perm + (size_t)rows[j] * d + (size_t)v * kPer, g);
+#pragma unroll
+            for (int q = 0; q < kPer; ++q)
+                acc[q] += g[q];
+        }
+        if (Wg) {
+            for (int e = 0; e < E; ++e) {
+                const float z = dz[(size_t)t * E + e];
+                float wv[kPer];
+                load_vec<ET>(Wg + (size_t)e * d + (size_t)v * kPer, wv);
+#pragma unroll
+                for (int q = 0; q < kPer; ++q)
+                    acc[q] = fmaf(z, wv[q], acc[q]);
+            }
+        }
+        store_vec<ET>(dx + (size_t)t * d + (size_t)v * kPer, acc);
+    }
+}
+
+// Gate weight gradient, pass 1: block (token chunk of 256, column group of
+// 256, expert group of 16): partial[chunk][e][c] = sum over the chunk's tokens
+// (in order) of dz[t,e] x[t,c].  Pass 2 adds the chunks in order.
+constexpr int kGateChunk = 256;
+
+template <typename ET>
+__global__ __launch_bounds__(256) void moe_gate_wgrad_kernel(const float* __restrict__ dz,
+                                                             const typename ET::storage* __restrict__ x, int T, int d,
+                                                             int E, float* __restrict__ partial)
+{
+    const int t0 = blockIdx.x * kGateChunk, t1 = min(T, t0 + kGateChunk);
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    const int e0 = blockIdx.z * 16;
+    float acc[16];
+#pragma unroll
+    for (int ee = 0; ee < 16; ++ee)
+        acc[ee] = 0.0f;
+    if (c < d) {
+        for (int t = t0; t < t1; ++t) {
+            float xv;
+            if constexpr (ET::kBytes == 2)
+                xv = __uint_as_float((uint32_t)x[(size_t)t * d + c] << 16);
+            else
+                xv = x[(size_t)t * d + c];
+#pragma unroll
+            for (int ee = 0; ee < 16; ++ee)
+                if (e0 + ee < E)
+                    acc[ee] = fmaf(dz[(size_t)t * E + e0 + ee], xv, acc[ee]);
+        }
+#pragma unroll
+        for (int ee = 0; ee < 16; ++ee)
+            if (e0 + ee < E)
+                partial[((size_t)blockIdx.x * E + e0 + ee) * d + c] = acc[ee];
+    }
+}
+
+__global__ __launch_bounds__(256) void moe_gate_wgrad_reduce_kernel(const float* __restrict__ partial, int nchunks,
+                                                                    int E, int d, float* __restrict__ dWg)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)E * d)
+        return;
+    float s = 0.0f;
+    for (int ch = 0; ch < nchunks; ++ch)
+        s += partial[(size_t)ch * E * d + i];
+    dWg[i] = s;
+}
+
+// dbg[e] = sum over t (in order) of dz[t,e].
+__global__ __launch_bounds__(256) void moe_colsum_kernel(const float* __restrict__ dz, int T, int E,
+                                                         float* __restrict__ dbg)
+{
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E)
+        return;
+    float s = 0.0f;
+    for (int t = 0; t < T; ++t)
+        s += dz[(size_t)t * E + e];
+    dbg[e] = s;
+}
+
+// n floats set to 0 (a kernel, so that a captured graph holds no memset node).
+__global__ __launch_bounds__(256) void moe_zero_kernel(float* __restrict__ p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        p[i] = 0.0f;
+}
+
+}  // namespace moe
+
+extern "C" hipError_t moe_launch_zero(float* p, size_t n, hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096)
+        blocks = 4096;
+    moe::moe_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p, n);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_combine_bwd(int dtype, const void* dy, const void* y_perm, const int32_t* slot,
+                                             const float* topk_w, int T, int d, int k, int max_rows, void* d_yp,
+                                             float* d_w, hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid((T + 3) / 4), block(256);
+    if (dtype == 0)
+        moe_combine_bwd_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)dy, (const float*)y_perm, slot, topk_w,
+                                                                  T, d, k, max_rows, (float*)d_yp, d_w);
+    else
+        moe_combine_bwd_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)dy, (const uint16_t*)y_perm, slot,
+                                                                   topk_w, T, d, k, max_rows, (uint16_t*)d_yp, d_w);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_kofs(const int32_t* offsets, int E, int max_rows, int align, int32_t* kofs,
+                                      hipStream_t stream)
+{
+    moe::moe_kofs_kernel<<<1, 1024, 0, stream>>>(offsets, E, max_rows, align, kofs);
+    return hipGetLastError();
+}
+
+// B matrices of R x C (multiples of 64) -> C x R.
+extern "C" hipError_t moe_launch_transpose(int dtype, const void* src, int B, int R, int C, void* dst,
+                                           hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid(C / 64, R / 64, B), block(256);
+    if (dtype == 0)
+        moe_transpose_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)src, R, C, (float*)dst);
+    else
+        moe_transpose_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)src, R, C, (uint16_t*)dst);
+    return hipGetLastError();
+}
+
+// dst [C][ld] from permuted rows of src ([*][C]); ld >= kofs[E], multiple of 64.
+extern "C" hipError_t moe_launch_seg_transpose(int dtype, const void* src, const int32_t* gather, int gather_rows,
+                                               const int32_t* offsets, const int32_t* kofs, int E, int max_rows,
+                                               int C, int ld, void* dst, hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid(ld / 64, C / 64), block(256);
+    if (dtype == 0)
+        moe_seg_transpose_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)src, gather, gather_rows, offsets,
+                                                                    kofs, E, max_rows, C, ld, (float*)dst);
+    else
+        moe_seg_transpose_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)src, gather, gather_rows,
+                                                                     offsets, kofs, E, max_rows, C, ld,
+                                                                     (uint16_t*)dst);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_unpermute_bwd(int dtype, const void* dx_perm, const int32_t* slot, int T, int d,
+                                               int k, int max_rows, const float* dz, const void* Wg, int E, void* dx,
+                                               hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid((T + 3) / 4), block(256);
+    if (dtype == 0)
+        moe_unpermute_bwd_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)dx_perm, slot, T, d, k, max_rows, dz,
+                                                                    (const float*)Wg, E, (float*)dx);
+    else
+        moe_unpermute_bwd_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)dx_perm, slot, T, d, k,
+                                                                     max_rows, dz, (const uint16_t*)Wg, E,
+                                                                     (uint16_t*)dx);
+    return hipGetLastError();
+}
+
+extern "C" size_t moe_gate_wgrad_partial_bytes(int T, int d, int E)
+{
+    const size_t nch = (size_t)(T + moe::kGateChunk - 1) / moe::kGateChunk;
+    return (nch > 0 ? nch : 1) * (size_t)E * d * sizeof(float);
+}
+
+extern "C" hipError_t moe_launch_gate_wgrad(int dtype, const float* dz, const void* x, int T, int d, int E,
+                                            float* partial, float* dWg, float* dbg, hipStream_t stream)
+{
+    using namespace moe;
+    const int nch = (T + kGateChunk - 1) / kGateChunk;
+    const dim3 grid(nch, (d + 255) / 256, (E + 15) / 16), block(256);
+    if (dtype == 0)
+        moe_gate_wgrad_kernel<f32_t><<<grid, block, 0, stream>>>(dz, (const float*)x, T, d, E, partial);
+    else
+        moe_gate_wgrad_kernel<bf16_t><<<grid, block, 0, stream>>>(dz, (const uint16_t*)x, T, d, E, partial);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const size_t n = (size_t)E * d;
+    moe_gate_wgrad_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), block, 0, stream>>>(partial, nch, E, d, dWg);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    moe_colsum_kernel<<<dim3((E + 255) / 256), block, 0, stream>>>(dz, T, E, dbg);
+    return hipGetLastError();
+}

@@ -54,7 +54,10 @@
 
 namespace moe {
 
-enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+// Epilogues: none; forward activations (ReLU, SwiGLU); backward of the
+// activation applied to the incoming gradient dh (the tile computes dh and the
+// epilogue turns it into du with the saved pre-activation u).
+enum { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_DRELU = 3, EPI_DSWIGLU = 4 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -301,21 +304,62 @@ struct Frag {
     typename S::frag_t a[S::kFN], b[S::kFM];
 };
 
-// Epilogue: activation and store of a tile from the wave's accumulators.
-// Lane holds row m = .. + (lane & 31), 4 consecutive columns per group.
-// Per-row scales of an FP8 GEMM (null pointers: no scaling): a[source row
-// of A] and w[e * Nw + weight row].
-struct Scales {
+// Epilogue arguments.  a, w: per-row scales of an FP8 GEMM (null: none),
+// a[source row of A] and w[e * Nw + weight row].  aux_out (nullable): the
+// forward's pre-activation u is stored there as well ([rows][aux_ld], the
+// gate columns then the up columns for SwiGLU).  aux_in: the saved u that
+// the activation-backward epilogues read ([rows][aux_ld]).
+struct EpiArgs {
     const float* a;
     const float* w;
+    const void* aux_in;
+    void* aux_out;
+    int aux_ld;
 };
 
+// 4 consecutive elements of a row as fp32 / from fp32.
+template <typename OT>
+__device__ __forceinline__ void load4(const typename OT::storage* p, float* v)
+{
+    if constexpr (OT::kBytes == 2) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        v[0] = __uint_as_float(w.x << 16);
+        v[1] = __uint_as_float(w.x & 0xffff0000u);
+        v[2] = __uint_as_float(w.y << 16);
+        v[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+        const float4 w = *reinterpret_cast<const float4*>(p);
+        v[0] = w.x;
+        v[1] = w.y;
+        v[2] = w.z;
+        v[3] = w.w;
+    }
+}
+template <typename OT>
+__device__ __forceinline__ void store4(typename OT::storage* p, const float* v)
+{
+    if constexpr (OT::kBytes == 2) {
+        uint2 o;
+        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2*>(p) = o;
+    } else {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// Epilogue: activation and store of a tile from the wave's accumulators.
+// Lane holds row m = .. + (lane & 31), 4 consecutive columns per group.
 // `wave` is the wave slot of the tile whose accumulators these are; OT the
 // stored element type.  With scales, u = acc * a_scale(row) * w_scale(col)
 // enters the epilogue (a_scale of row r is a[gather[r]] with a gather index).
+// Backward epilogues (acc = dh at column f < F, u the saved pre-activation):
+//   EPI_DRELU:   du[f] = u[f] > 0 ? dh : 0
+//   EPI_DSWIGLU: g = u[f], v = u[F+f], s = 1/(1+e^-g):
+//                du[f] = dh v s (1 + g (1 - s)),  du[F+f] = dh g s
 template <typename OT, typename S, int EPI>
 __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::storage* __restrict__ C, const TileDec& t,
-                                           int Nout, int ncols, int wave, Scales sc, const int32_t* gather, int Nw,
+                                           int Nout, int ncols, int wave, EpiArgs ep, const int32_t* gather, int Nw,
                                            int F)
 {
     typedef typename OT::storage T;
@@ -327,10 +371,12 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
         if (m >= t.rows)
             continue;
         T* crow = C + (size_t)(t.row0 + m) * Nout;
+        const T* urow = ep.aux_in ? (const T*)ep.aux_in + (size_t)(t.row0 + m) * ep.aux_ld : nullptr;
+        T* prow = ep.aux_out ? (T*)ep.aux_out + (size_t)(t.row0 + m) * ep.aux_ld : nullptr;
         float as = 1.0f;
-        if (sc.a)
-            as = sc.a[gather ? gather[t.row0 + m] : t.row0 + m];
-        const float* wsc = sc.w ? sc.w + (size_t)t.e * Nw : nullptr;
+        if (ep.a)
+            as = ep.a[gather ? gather[t.row0 + m] : t.row0 + m];
+        const float* wsc = ep.w ? ep.w + (size_t)t.e * Nw : nullptr;
         constexpr int kJ = (EPI == EPI_SWIGLU) ? S::kFN / 2 : S::kFN;
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
@@ -338,31 +384,46 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int nl = j * 32 + 8 * g4 + 4 * (lane >> 5);
                 const int n = t.n0 + ((EPI == EPI_SWIGLU) ? wn * (S::kWaveN / 2) : wn * S::kWaveN) + nl;
-                float v[4];
+                if (n >= ncols)
+                    continue;
+                float v[4], v2[4], pre[4], pre2[4], uin[4], uin2[4];
+                if (EPI == EPI_DRELU || EPI == EPI_DSWIGLU)
+                    load4<OT>(urow + n, uin);
+                if (EPI == EPI_DSWIGLU)
+                    load4<OT>(urow + F + n, uin2);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float u = acc.v[i][j][4 * g4 + q];
                     float up = (EPI == EPI_SWIGLU) ? acc.v[i][j + S::kFN / 2][4 * g4 + q] : 0.0f;
-                    if (wsc && n + q < ncols) {
+                    if (wsc) {
                         u *= as * wsc[n + q];
                         if (EPI == EPI_SWIGLU)
                             up *= as * wsc[F + n + q];
                     }
+                    pre[q] = u;
+                    pre2[q] = up;
+                    v2[q] = 0.0f;
                     if (EPI == EPI_RELU)
                         u = fmaxf(u, 0.0f);
                     if (EPI == EPI_SWIGLU)
                         u = u / (1.0f + __expf(-u)) * up;
+                    if (EPI == EPI_DRELU)
+                        u = uin[q] > 0.0f ? u : 0.0f;
+                    if (EPI == EPI_DSWIGLU) {
+                        const float g = uin[q], gv = uin2[q];
+                        const float sg = 1.0f / (1.0f + __expf(-g));
+                        v2[q] = u * g * sg;
+                        u = u * gv * sg * (1.0f + g * (1.0f - sg));
+                    }
                     v[q] = u;
                 }
-                if (n < ncols) {
-                    if constexpr (OT::kBytes == 2) {
-                        uint2 o;
-                        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(crow + n) = o;
-                    } else {
-                        *reinterpret_cast<float4*>(crow + n) = make_float4(v[0], v[1], v[2], v[3]);
-                    }
+                store4<OT>(crow + n, v);
+                if (EPI == EPI_DSWIGLU)
+                    store4<OT>(crow + F + n, v2);
+                if ((EPI == EPI_RELU || EPI == EPI_SWIGLU) && prow) {
+                    store4<OT>(prow + n, pre);
+                    if (EPI == EPI_SWIGLU)
+                        store4<OT>(prow + F + n, pre2);
                 }
             }
         }
@@ -378,12 +439,17 @@ __device__ __forceinline__ size_t partial_index(int wave, int i, int j, int g, i
     return ((((size_t)(wave * S::kFM + i) * S::kFN + j) * 4 + g) * kWave + lane) * 4;
 }
 
-template <typename ET, typename OT, typename S, int EPI>
+// KG (K-grouped, the weight gradients): one dense output per expert,
+// C[e] = A W^T over expert e's K range [offsets[e], offsets[e+1]) (device
+// array, multiples of the K slice): A [max_rows][K], W [Nw][K] row-major with
+// row stride K, C [E][max_rows][Nout] (Nout == Nw).  No row segments, no
+// gather, no split.
+template <typename ET, typename OT, typename S, int EPI, bool KG = false>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
 void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const int32_t* __restrict__ gather,
                              int gather_rows, const typename ET::storage* __restrict__ W,
                              typename OT::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E,
-                             int K, int Nw, int Nout, int F, int max_rows, float* __restrict__ partial, Scales sc)
+                             int K, int Nw, int Nout, int F, int max_rows, float* __restrict__ partial, EpiArgs sc)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only types; the host pass needs the stub only
     constexpr int kWaves = S::kWaves;
@@ -424,13 +490,19 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
     const uint32_t lane_chunk = (uint32_t)(lchunk << 4);
 
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
-    const int ncols = (EPI == EPI_SWIGLU) ? F : Nout;
+    const int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? F : Nout;
     const int ntn = (ncols + tile_cols - 1) / tile_cols;
-    tile_prefix<S::kThreads>(offsets, E, max_rows, S::BM, ntn, s_pref, s_wsum);
-    const int total = s_pref[E];
+    const int mtk = (max_rows + S::BM - 1) / S::BM;  // K-grouped mode: m-tiles per expert
+    int total;
+    if constexpr (KG) {
+        total = E * mtk * ntn;
+    } else {
+        tile_prefix<S::kThreads>(offsets, E, max_rows, S::BM, ntn, s_pref, s_wsum);
+        total = s_pref[E];
+    }
     const int G = gridDim.x;
     const int nk = K / S::kBK;
-    const int parts = split_parts(total, G, nk, partial != nullptr);
+    const int parts = KG ? 1 : split_parts(total, G, nk, partial != nullptr);
     const int full = total - total % G;
     const int tail = total - full;
     const int items = full + tail * parts;
@@ -449,7 +521,27 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             k1 = (part + 1) * nk / parts;
             slot = (j % tail) * parts + part;
         }
-        const TileDec t = decode_tile<S>(tile, s_pref, offsets, E, max_rows, ntn, tile_cols);
+        TileDec t;
+        typename OT::storage* Cb = C;
+        if constexpr (KG) {
+            // (expert, group of GM m-tiles, n-tile, m-tile) order, as decode_tile
+            t.e = tile / (mtk * ntn);
+            const int local = tile - t.e * mtk * ntn;
+            const int g = local / (S::GM * ntn);
+            const int within = local - g * S::GM * ntn;
+            const int gs = min(S::GM, mtk - g * S::GM);
+            const int mt = g * S::GM + within % gs;
+            t.row0 = mt * S::BM;
+            t.rows = min(S::BM, max_rows - t.row0);
+            t.n0 = (within / gs) * tile_cols;
+            const int ka = min(max(offsets[t.e], 0), K);
+            const int kb = min(max(offsets[t.e + 1], ka), K);
+            k0 = ka / S::kBK;
+            k1 = kb / S::kBK;
+            Cb = C + (size_t)t.e * max_rows * Nout;
+        } else {
+            t = decode_tile<S>(tile, s_pref, offsets, E, max_rows, ntn, tile_cols);
+        }
 
         // activation rows: the tile's rows of A (rows past the segment read
         // 0), or rows gather[row] of A
@@ -469,8 +561,8 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             for (int i = 0; i < S::kBlkA; ++i)
                 voffA[i] = (uint32_t)(S::kRowsPerBlk * (wave + kWaves * i) + lrow) * rowK + lane_chunk;
         }
-        // this expert's weight matrix: rows past Nw read 0
-        const i32x4 rsW = make_rsrc(W + (size_t)t.e * Nw * K, (uint32_t)Nw * rowK);
+        // this expert's weight matrix (K-grouped: the one W): rows past Nw read 0
+        const i32x4 rsW = make_rsrc(KG ? W : W + (size_t)t.e * Nw * K, (uint32_t)Nw * rowK);
         uint32_t voffB[S::kBlkB];
 #pragma unroll
         for (int i = 0; i < S::kBlkB; ++i) {
@@ -682,7 +774,7 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         }
 
         if (slot < 0) {
-            store_tile<OT, S, EPI>(acc, C, t, Nout, ncols, wave, sc, gather, Nw, F);
+            store_tile<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, gather, Nw, F);
         } else {
             float* dst = partial + (size_t)slot * S::kTileFloats;
 #pragma unroll
@@ -705,12 +797,12 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
 template <typename OT, typename S, int EPI>
 __global__ __launch_bounds__(256) void moe_grouped_gemm_tail_kernel(
     typename OT::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E, int K, int Nw, int Nout, int F,
-    int max_rows, int G, const float* __restrict__ partial, Scales sc, const int32_t* __restrict__ gather)
+    int max_rows, int G, const float* __restrict__ partial, EpiArgs sc, const int32_t* __restrict__ gather)
 {
     __shared__ int32_t s_pref[kGemmMaxE + 1];
     __shared__ int32_t s_wsum[256 / kWave];
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
-    const int ncols = (EPI == EPI_SWIGLU) ? F : Nout;
+    const int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? F : Nout;
     const int ntn = (ncols + tile_cols - 1) / tile_cols;
     tile_prefix<256>(offsets, E, max_rows, S::BM, ntn, s_pref, s_wsum);
     const int total = s_pref[E];
@@ -767,7 +859,7 @@ struct GemmArgs {
     const int32_t* offsets;
     int E, K, Nw, Nout, F, max_rows, ncu;
     float* partial;
-    Scales sc;
+    EpiArgs sc;
     hipStream_t stream;
 };
 
@@ -777,7 +869,7 @@ hipError_t launch_one(const GemmArgs& g)
     typedef typename ET::storage T;
     typedef typename OT::storage TO;
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
-    const int ncols = (EPI == EPI_SWIGLU) ? g.F : g.Nout;
+    const int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? g.F : g.Nout;
     const long long ntn = (ncols + tile_cols - 1) / tile_cols;
     // upper bound on m-tiles: floor(P/BM) full tiles plus one partial per expert
     const long long mt_max = g.max_rows / S::BM + (long long)(g.E < g.max_rows ? g.E : g.max_rows);
@@ -808,6 +900,12 @@ hipError_t launch_epi(int epi, const GemmArgs& g)
         return launch_one<ET, OT, S, EPI_RELU>(g);
     if (epi == EPI_SWIGLU)
         return launch_one<ET, OT, S, EPI_SWIGLU>(g);
+    if constexpr (ET::kBytes != 1) {  // the backward epilogues exist for bf16 and fp32
+        if (epi == EPI_DRELU)
+            return launch_one<ET, OT, S, EPI_DRELU>(g);
+        if (epi == EPI_DSWIGLU)
+            return launch_one<ET, OT, S, EPI_DSWIGLU>(g);
+    }
     return launch_one<ET, OT, S, EPI_NONE>(g);
 }
 }  // namespace
@@ -851,19 +949,22 @@ extern "C" size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows)
     return (size_t)kSplitSlots * tile_floats * sizeof(float);
 }
 
-// epi: 0 none, 1 ReLU, 2 SwiGLU.  Nw = weight rows per expert, Nout = output
-// row stride (= output columns).  max_rows bounds offsets[E]; mean_rows is the
-// expected rows per expert (selects the tile configuration).  gather
-// (nullable) maps each permuted row to its row of A (gather_rows rows).
-// partial (nullable) is the tail-split workspace of
-// moe_grouped_gemm_partial_bytes bytes; NULL disables the split.
+// epi: 0 none, 1 ReLU, 2 SwiGLU, 3 ReLU backward, 4 SwiGLU backward.  Nw =
+// weight rows per expert, Nout = output row stride (= output columns).
+// max_rows bounds offsets[E]; mean_rows is the expected rows per expert
+// (selects the tile configuration).  gather (nullable) maps each permuted row
+// to its row of A (gather_rows rows).  partial (nullable) is the tail-split
+// workspace of moe_grouped_gemm_partial_bytes bytes; NULL disables the split.
+// aux_out (nullable; epi 1, 2): the pre-activation u is stored there too;
+// aux_in (epi 3, 4): the saved u; both [rows][aux_ld].
 extern "C" hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A, const int32_t* gather,
                                               int gather_rows, const void* W, void* C, const int32_t* offsets, int E,
                                               int K, int Nw, int Nout, int F, int max_rows, int mean_rows, int ncu,
-                                              float* partial, hipStream_t stream)
+                                              float* partial, const void* aux_in, void* aux_out, int aux_ld,
+                                              hipStream_t stream)
 {
     const GemmArgs g = {A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, partial,
-                        Scales{nullptr, nullptr}, stream};
+                        EpiArgs{nullptr, nullptr, aux_in, aux_out, aux_ld}, stream};
     if (dtype == 0)
         return launch_epi<f32_t, f32_t, GemmShape<f32_t, MOE_F32_TILE>>(epi, g);
     if (mean_rows >= 512)
@@ -884,10 +985,39 @@ extern "C" hipError_t moe_launch_grouped_gemm_fp8(int epi, const void* A, const 
                                                   hipStream_t stream)
 {
     const GemmArgs g = {A, gather, gather_rows, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, partial,
-                        Scales{a_scale, w_scale}, stream};
+                        EpiArgs{a_scale, w_scale, nullptr, nullptr, 0}, stream};
     if (mean_rows >= 512)
         return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_LARGE_TILE>>(epi, g);
     if (mean_rows >= 128)
         return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_MEDIUM_TILE>>(epi, g);
     return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_SMALL_TILE>>(epi, g);
+}
+
+// Weight gradients, K-grouped: C[e] (fp32 [M][N]) = A[:, K_e] W[:, K_e]^T for
+// every expert e, K_e = [kofs[e], kofs[e+1]) columns of A [M][lda] and
+// W [N][lda] (bf16 or fp32 per dtype), kofs multiples of 64 (bf16) or 32
+// (fp32) and <= lda, lda a multiple of 64.  Columns past an expert's rows must
+// hold zeros (padding).
+extern "C" hipError_t moe_launch_grouped_gemm_kgrp(int dtype, const void* A, const void* W, float* C,
+                                                   const int32_t* kofs, int E, int lda, int M, int N, int ncu,
+                                                   hipStream_t stream)
+{
+    auto go = [&](auto et, auto shape) -> hipError_t {
+        typedef decltype(et) ET;
+        typedef decltype(shape) S;
+        typedef typename ET::storage T;
+        const long long total = (long long)E * ((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN);
+        long long grid = (long long)ncu * S::OCC;
+        if (total < grid)
+            grid = (total + 7) / 8 * 8;
+        if (grid < 1)
+            grid = 1;
+        moe_grouped_gemm_kernel<ET, f32_t, S, EPI_NONE, true><<<dim3((unsigned)grid), dim3(S::kThreads), 0, stream>>>(
+            (const T*)A, nullptr, 0, (const T*)W, C, kofs, E, lda, N, N, N, M, nullptr,
+            EpiArgs{nullptr, nullptr, nullptr, nullptr, 0});
+        return hipGetLastError();
+    };
+    if (dtype == 0)
+        return go(f32_t{}, GemmShape<f32_t, MOE_F32_TILE>{});
+    return go(bf16_t{}, GemmShape<bf16_t, MOE_LARGE_TILE>{});
 }

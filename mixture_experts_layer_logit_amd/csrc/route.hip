@@ -250,6 +250,100 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
     }
 }
 
+// ---------------------------------------------------------------- router backward
+// Logit gradient of one token from the gate-weight gradients d_w[t,j] (the
+// combine's <dy, y_perm row>): dp[e] = d_w of the kept choice on e (0 for
+// other experts and dropped choices; top-k passes no gradient),
+// ds = p (dp - <p, dp>) through the softmax, and with the normalisation
+// s = lambda zh, zh = (z - mu) / sigma:
+//   dz = (lambda / sigma) (ds - mean(ds) - zh mean(ds zh)),  0 when sigma == 0.
+// fp64 throughout (the router's arithmetic), stored fp32.  One wavefront per
+// token.
+template <int VPL>
+__global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __restrict__ logits,
+                                                             const int32_t* __restrict__ topk_idx,
+                                                             const int32_t* __restrict__ slot,
+                                                             const float* __restrict__ d_w, int T, int E, int k,
+                                                             int normalize, float lambda, float* __restrict__ dz)
+{
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T)
+        return;
+    const float* zt = logits + (size_t)t * E;
+    float z[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        z[i] = e < E ? zt[e] : 0.0f;
+    }
+    double ex[VPL], denom;
+    token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
+    double p[VPL], dp[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        p[i] = ex[i] / denom;
+        dp[i] = 0.0;
+    }
+    for (int j = 0; j < k; ++j) {
+        const size_t a = (size_t)t * k + j;
+        const int e = topk_idx[a];
+        if (slot[a] < 0 || e < 0 || e >= E)
+            continue;
+        const double g = (double)d_w[a];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (lane + kWave * i == e)
+                dp[i] += g;
+    }
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        part += p[i] * dp[i];
+    const double pdp = wave_sum(part);
+    double ds[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        ds[i] = (lane + kWave * i < E) ? p[i] * (dp[i] - pdp) : 0.0;
+    if (normalize) {
+        part = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            part += (lane + kWave * i < E) ? (double)z[i] : 0.0;
+        const double mu = wave_sum(part) / E;
+        part = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const double c = (double)z[i] - mu;
+            part += (lane + kWave * i < E) ? c * c : 0.0;
+        }
+        const double sigma = sqrt(wave_sum(part) / E);
+        if (sigma == 0.0) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                ds[i] = 0.0;
+        } else {
+            double zh[VPL], p1 = 0.0, p2 = 0.0;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                zh[i] = ((double)z[i] - mu) / sigma;
+                p1 += ds[i];
+                p2 += (lane + kWave * i < E) ? ds[i] * zh[i] : 0.0;
+            }
+            const double m1 = wave_sum(p1) / E, m2 = wave_sum(p2) / E;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                ds[i] = (double)lambda / sigma * (ds[i] - m1 - zh[i] * m2);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E)
+            dz[(size_t)t * E + e] = (float)ds[i];
+    }
+}
+
 // ---------------------------------------------------------------- router by-products
 // Sums over tokens for the balancing statistics (Megatron-Core page, "MoE负载
 // 均衡的挑战与应对" and "关键特性": auxiliary loss, Z-Loss; Skywork news item,
@@ -449,5 +543,26 @@ extern "C" hipError_t moe_launch_router_stats(const float* logits, int T, int E,
     if (err != hipSuccess)
         return err;
     moe_router_stats_final_kernel<<<1, 1024, 0, stream>>>(terms, T, E, k, offsets, scalars);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_router_bwd(const float* logits, const int32_t* topk_idx, const int32_t* slot,
+                                            const float* d_w, int T, int E, int k, int normalize, float lambda,
+                                            float* dz, hipStream_t stream)
+{
+    using namespace moe;
+    const dim3 grid((T + 3) / 4), block(256);
+    const int vpl = (E + kWave - 1) / kWave;
+    if (vpl <= 1)
+        moe_router_bwd_kernel<1><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+    else if (vpl <= 2)
+        moe_router_bwd_kernel<2><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+    else if (vpl <= 4)
+        moe_router_bwd_kernel<4><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+    else if (vpl <= 8)
+        moe_router_bwd_kernel<8><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+    else
+        moe_router_bwd_kernel<16><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda,
+                                                              dz);
     return hipGetLastError();
 }

@@ -29,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 ZIPF_BIAS_FILE = os.path.join(_HERE, "zipf_bias.json")
 
 # tensor ids for the seed sequence
-TID_X, TID_WG, TID_W1, TID_W2, TID_LOGITS, TID_HOT = 1, 2, 3, 4, 5, 6
+TID_X, TID_WG, TID_W1, TID_W2, TID_LOGITS, TID_HOT, TID_DY = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclass(frozen=True)
@@ -209,6 +209,19 @@ def make(case, *, weights: bool = True, threads: int = 8, bias_override=None) ->
         out["W1"] = _expert_stack(case, TID_W1, case.n1, case.d, case.w_std, threads)
         out["W2"] = _expert_stack(case, TID_W2, case.d, case.F, case.w_std, threads)
     return out
+
+
+def make_dy(case, tokens=None, std: float = 1.0) -> np.ndarray:
+    """Incoming gradient dL/dy [T,d] of the backward, N(0, std^2) in the case's
+    dtype; with ``tokens`` (indices), rows outside them are zero."""
+    if isinstance(case, str):
+        case = get(case)
+    dy = _normal(case.seed, TID_DY, 0, (case.T, case.d), std)
+    if tokens is not None:
+        keep = np.zeros(case.T, bool)
+        keep[np.asarray(tokens)] = True
+        dy[~keep] = 0.0
+    return _cast(dy, case.dtype)
 
 
 def zipf_shares(E: int, s: float) -> np.ndarray:

@@ -85,3 +85,40 @@ def exact_sum_certified(x64, wg64, bg, mant_bits, chunk=256):
     with np.errstate(over="ignore"):
         ok = np.log2(np.maximum(S, 1e-300)) - gmin < 53
     return ok | np.isinf(gmin)
+
+
+# ---------------------------------------------------------------- ReLU backward
+# The ReLU backward passes dh where u > 0.  The GPU decides on its stored u:
+# an fp32 accumulation of the d products x_ti W1_efi (bf16 products are exact
+# in fp32; fp32 products carry one rounding each), then rounded to the storage
+# dtype, which keeps the sign.  Any order of fp32 multiply-adds is within
+# gamma_{d+1} S of the exact value, gamma_n = n u / (1 - n u), u = 2^-24,
+# S = sum_i |x_ti W1_efi| (Higham, ch. 3-4); the bound is doubled as a margin
+# for the matrix cores' internal accumulation.  Where |u_exact| is inside that
+# bound the two sides may take different, equally correct decisions.
+U24 = 2.0 ** -24
+
+
+def _f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def relu_unpinned(x64, W1, topk_idx, slot, F, d):
+    """Triples (t, e, f) of kept choices whose ReLU decision is not pinned
+    (x64 [T,d] float64; W1 [E,n1,d] as stored: fp32 or bf16 bits)."""
+    n = d + 1
+    gamma = 2.0 * n * U24 / (1.0 - n * U24) + (d + 1) * U53
+    out = []
+    for e in np.unique(topk_idx[slot >= 0]):
+        toks = np.nonzero(np.any((topk_idx == e) & (slot >= 0), axis=1))[0]
+        xs = x64[toks]
+        w = _f64(W1[e, :F])
+        u = xs @ w.T
+        S = np.abs(xs) @ np.abs(w).T
+        bad = np.abs(u) <= gamma * S
+        for r, f in zip(*np.nonzero(bad)):
+            out.append((int(toks[r]), int(e), int(f)))
+    return out

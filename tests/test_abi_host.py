@@ -218,3 +218,70 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert lib.moe_expert_up_fp8(pp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
         moe.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_down_fp8(pp, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def backward_formula(T, d, E, k, F, act, b):
+    r = lambda n: (n + 255) // 256 * 256
+    n1 = 2 * F if act == "swiglu" else F
+    ld = (T * k + 64 * E + 63) // 64 * 64
+    nch = max((T + 255) // 256, 1)
+    tile = 128 * 128 if b == 4 else 256 * 256 if T * k // E >= 512 else 128 * 128 if T * k // E >= 128 else 64 * 256
+    return (r(T * k * d * b) + r(T * k * 4) + r(T * E * 4) + r(T * k * n1 * b) + r(T * k * d * b)
+            + r(E * n1 * d * b) + r(E * d * F * b) + r((E + 1) * 4)
+            + r(d * ld * b) + r(F * ld * b) + r(n1 * ld * b) + r(d * ld * b)
+            + r(nch * E * d * 4) + r(256 * tile * 4))
+
+
+@pytest.mark.parametrize("T,d,E,k,F,act,dt", [(4096, 4096, 8, 2, 14336, "swiglu", "bf16"),
+                                              (256, 64, 4, 2, 128, "relu", "f32"),
+                                              (16384, 1024, 512, 2, 512, "relu", "bf16"),
+                                              (1, 64, 1, 1, 64, "swiglu", "bf16")])
+def test_backward_workspace_size(T, d, E, k, F, act, dt):
+    p = moe.problem(T, d, E, k, F, act=act, dtype=dt)
+    b = 4 if dt == "f32" else 2
+    assert moe.moe_backward_workspace_size(p) == backward_formula(T, d, E, k, F, act, b)
+
+
+def test_backward_entry_points_reject_bad_arguments():
+    lib = moe.load()
+    # transposed row operands beyond 32-bit offsets
+    big = moe.problem(1 << 21, 2048, 64, 2, 1024)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_backward_workspace_size(big)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    p = moe.problem(64, 64, 8, 2, 64)
+    pp = ctypes.byref(p)
+    bws = moe.moe_backward_workspace_size(p)
+    ws = moe.moe_workspace_size(p)
+    info = moe.RouteInfo(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    saved = moe.Saved(FAKE, FAKE, FAKE)
+    ri, sv = ctypes.byref(info), ctypes.byref(saved)
+    # the training forward needs info and saved, and a full workspace
+    assert lib.moe_forward_train(pp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, ri, None, FAKE, ws, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_train(pp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, ri, sv, FAKE, ws - 1, None) == \
+        moe.MOE_ERR_WORKSPACE
+    bad_saved = moe.Saved(FAKE, FAKE + 2, FAKE)
+    assert lib.moe_forward_train(pp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, ri, ctypes.byref(bad_saved), FAKE,
+                                 ws, None) == moe.MOE_ERR_INVALID_ARG
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ri, sv, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bws, None]
+    # short workspace; no route info; a gate without its gradient outputs; null dW2
+    a = list(args)
+    a[-2] = bws - 1
+    assert lib.moe_backward(pp, *a) == moe.MOE_ERR_WORKSPACE
+    a = list(args)
+    a[6] = None
+    assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
+    a = list(args)
+    a[9] = None
+    assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
+    a = list(args)
+    a[12] = None
+    assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
+    # T == 0: the training forward is a no-op; the backward still needs its weight-gradient outputs
+    p0 = moe.problem(0, 64, 8, 2, 64)
+    p0p = ctypes.byref(p0)
+    assert lib.moe_forward_train(p0p, None, None, None, None, None, None, None, None, None, None, 0, None) == \
+        moe.MOE_OK
+    assert lib.moe_backward(p0p, None, None, None, None, None, None, None, None, None, None, None, None, None, None,
+                            0, None) == moe.MOE_ERR_INVALID_ARG
