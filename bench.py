@@ -13,15 +13,21 @@ Prints ONE JSON line: tokens/s of the whole job (value), the roofline of the
 dominant kernel (the expert up-projection grouped GEMM, with its split-K
 reduction) from HIP events on the stream it runs on, and the CPU oracle timed
 on a bounded sample of the same workload on this host's cores.  The same line
-also carries the router statistics and a shared expert (width F) timed on the
-same workload ("next_rows"), and the step timing of the other workloads
+also carries the router statistics, a shared expert (width F), the layer with
+FP8 expert weights and the training step (forward keeping its intermediates,
+then the backward) timed on the same workload ("next_rows"), and the step
+timing of the other workloads
 ("other_configs": routing inputs from the seeded generator, expert weights
 drawn on the device with the same distribution, since their values do not
 change the work).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                   [--no-cpu-baseline] [--no-other-configs] [--no-next-rows]
-                  [--mode copy]
+                  [--mode copy|train]
+
+--mode train times only the training step and prints its own JSON line (for
+profiling the backward); --mode copy times a plain device copy (the HBM
+counter calibration).
 """
 from __future__ import annotations
 
@@ -126,7 +132,7 @@ def main():
     ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--mode", default="layer", choices=["layer", "copy"])
+    ap.add_argument("--mode", default="layer", choices=["layer", "copy", "train"])
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -154,6 +160,12 @@ def main():
     with torch.cuda.stream(stream):
         dev_w = {"W1": to_dev(inp["W1"]), "W2": to_dev(inp["W2"])}
     lay = Layer(moe, case, inp, dev_w, stream)
+    if args.mode == "train":  # the training step alone (forward keeping intermediates, backward)
+        log("[bench] training step")
+        r = lay.time_train(args.steps)
+        r.update(workload=workload_name(case), steps=args.steps)
+        print(json.dumps(r), flush=True)
+        return
     log(f"[bench] warmup {args.warmup}")
     res = lay.time(args.steps, args.warmup)
     T, d, E, k, F = case.T, case.d, case.E, case.k, case.F
@@ -382,7 +394,73 @@ class Layer:
         del Ws1, Ws2, ysh, sws
         if c.dtype == "bf16" and d % 128 == 0 and F % 128 == 0:
             out["fp8_layer"] = self.time_fp8(steps)
+        out["backward"] = self.time_train(steps)
         return out
+
+    def time_train(self, steps):
+        """Training step: moe_forward_train (the forward keeping u, h and
+        y_perm), then moe_backward on a seeded incoming gradient dy; each call
+        timed with events on the layer's stream."""
+        import numpy as np
+        import torch
+        import moe_inputs
+        moe, p, c, s = self.moe, self.p, self.case, self.stream.cuda_stream
+        T, d, E, k, F = c.T, c.d, c.E, c.k, c.F
+        n1, dt = self.n1, self.dt
+        with torch.cuda.stream(self.stream):
+            dy = to_dev(moe_inputs.make_dy(c))
+            saved = {"u": torch.empty(T * k, n1, dtype=dt, device="cuda"), "h": self.h, "y_perm": self.y_perm}
+            info = {"topk_idx": self.idx, "topk_w": self.w, "counts": self.counts, "offsets": self.offsets,
+                    "slot": self.slot, "src_token": self.src}
+            bws = torch.empty(moe.moe_backward_workspace_size(p), dtype=torch.uint8, device="cuda")
+            dx = torch.empty(T, d, dtype=dt, device="cuda")
+            dW1 = torch.empty(E, n1, d, dtype=torch.float32, device="cuda")
+            dW2 = torch.empty(E, d, F, dtype=torch.float32, device="cuda")
+            gate = self.Wg is not None
+            dWg = torch.empty(E, d, dtype=torch.float32, device="cuda") if gate else None
+            dbg = torch.empty(E, dtype=torch.float32, device="cuda") if gate else None
+        torch.cuda.synchronize()
+
+        def fwd():
+            moe.moe_forward_train(p, self.x, self.Wg, self.bg, self.W1, self.W2, self.y, self.logits, info, saved,
+                                  self.ws, stream=s)
+
+        def bwd():
+            moe.moe_backward(p, dy, self.x, self.Wg, self.W1, self.W2, self.logits, info, saved, dx, dWg, dbg, dW1,
+                             dW2, bws, stream=s)
+
+        for _ in range(2):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(self.stream)
+            fwd()
+            ev[i][1].record(self.stream)
+            bwd()
+            ev[i][2].record(self.stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        P = int(self.offsets[-1].item())
+        # algorithmic FLOPs: input and weight gradients of both expert layers
+        # over the kept rows (the zero padding of the weight-gradient GEMMs' K
+        # is not counted), and the gate's two [T,E]x[E,d]-sized products
+        bwd_gemm = 2.0 * (2.0 * P * d * (n1 + F))
+        gate_f = 4.0 * T * E * d if gate else 0.0
+        peak = PEAK_TFLOPS[c.dtype]
+        return {
+            "tokens_per_s": T * steps / elapsed,
+            "ms_per_step": elapsed * 1e3 / steps,
+            "forward_train_ms": f_ms,
+            "backward_ms": b_ms,
+            "backward_tflops": (bwd_gemm + gate_f) / (b_ms * 1e-3) / 1e12,
+            "backward_frac_of_peak": (bwd_gemm + gate_f) / (b_ms * 1e-3) / 1e12 / peak,
+            "flops_note": "backward: 2 x the forward expert FLOPs (input and weight gradients) + 4 T E d for the gate",
+        }
 
     def time_fp8(self, steps):
         """The same layer with FP8 (E4M3) expert weights and activations: the
