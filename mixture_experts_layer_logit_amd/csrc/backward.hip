@@ -147,8 +147,48 @@ __global__ __launch_bounds__(1024) void moe_kofs_kernel(const int32_t* __restric
         kofs[E] = base + incl;
 }
 
-// Batched transpose through LDS: dst[b][c][r] = src[b][r][c] for R x C
-// matrices, R and C multiples of 64.  Block: a 64 x 64 tile, 256 threads.
+// 64 x 64 tile transpose through LDS with 16-byte global accesses: row r of
+// the tile is read from src_row(r) (nullptr: zeros), and row c of the
+// transposed tile (column c of the input) is written to dst_row(c); both are
+// 16-byte aligned pointers to 64 consecutive elements.  256 threads.  The
+// tile pitch of 65 elements spreads both the row-wise LDS writes and the
+// column-wise LDS reads over the banks.
+template <typename ET, typename SrcRow, typename DstRow>
+__device__ __forceinline__ void transpose_tile64(typename ET::storage (*tile)[65], SrcRow src_row, DstRow dst_row)
+{
+    typedef typename ET::storage T;
+    constexpr int kPer = 16 / ET::kBytes;      // elements per 16-byte vector
+    constexpr int kVecs = 64 / kPer;            // vectors per 64-element row
+    constexpr int kRows = 256 / kVecs;          // rows per pass
+    const int v = threadIdx.x % kVecs, r0 = threadIdx.x / kVecs;
+#pragma unroll
+    for (int p = 0; p < 64 / kRows; ++p) {
+        const int r = r0 + p * kRows;
+        const T* row = src_row(r);
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        if (row)
+            raw = *reinterpret_cast<const uint4*>(row + v * kPer);
+        const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            tile[r][v * kPer + j] = e[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 64 / kRows; ++p) {
+        const int c = r0 + p * kRows;
+        uint4 raw;
+        T* e = reinterpret_cast<T*>(&raw);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            e[j] = tile[v * kPer + j][c];
+        *reinterpret_cast<uint4*>(dst_row(c) + v * kPer) = raw;
+    }
+}
+
+// Batched transpose: dst[b][c][r] = src[b][r][c] for R x C matrices, R and C
+// multiples of 64.  Block: one 64 x 64 tile (blockIdx.x: column tile,
+// blockIdx.y: row tile, blockIdx.z: matrix).
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_transpose_kernel(const typename ET::storage* __restrict__ src, int R,
                                                             int C, typename ET::storage* __restrict__ dst)
@@ -157,20 +197,10 @@ __global__ __launch_bounds__(256) void moe_transpose_kernel(const typename ET::s
     __shared__ T tile[64][65];
     const size_t b = blockIdx.z;
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-    const T* s = src + b * (size_t)R * C;
-    T* o = dst + b * (size_t)R * C;
-    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = ty + 4 * i;
-        tile[r][tx] = s[(size_t)(r0 + r) * C + c0 + tx];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int c = ty + 4 * i;
-        o[(size_t)(c0 + c) * R + r0 + tx] = tile[tx][c];
-    }
+    const T* s = src + b * (size_t)R * C + (size_t)r0 * C + c0;
+    T* o = dst + b * (size_t)R * C + (size_t)c0 * R + r0;
+    transpose_tile64<ET>(
+        tile, [&](int r) -> const T* { return s + (size_t)r * C; }, [&](int c) -> T* { return o + (size_t)c * R; });
 }
 
 // Permuted rows into [columns][padded rows]: dst[c][q] for padded position q
@@ -218,19 +248,13 @@ __global__ __launch_bounds__(256) void moe_seg_transpose_kernel(const typename E
         s_row[threadIdx.x] = row;
     }
     __syncthreads();
-    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int qq = ty + 4 * i;
-        const int row = s_row[qq];
-        tile[qq][tx] = row >= 0 ? src[(size_t)row * C + c0 + tx] : (T)0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int c = ty + 4 * i;
-        dst[(size_t)(c0 + c) * ld + q0 + tx] = tile[tx][c];
-    }
+    transpose_tile64<ET>(
+        tile,
+        [&](int r) -> const T* {
+            const int row = s_row[r];
+            return row >= 0 ? src + (size_t)row * C + c0 : nullptr;
+        },
+        [&](int c) -> T* { return dst + (size_t)(c0 + c) * ld + q0; });
 }
 
 // dx[t] = sum over kept j (in order) of dx_perm[slot[t,j]], plus, with a
@@ -284,24 +308,27 @@ __global__ __launch_bounds__(256) void moe_unpermute_bwd_kernel(const typename E
     }
 }
 
-// Gate weight gradient, pass 1: block (token chunk of 256, column group of
-// 256, expert group of 16): partial[chunk][e][c] = sum over the chunk's tokens
-// (in order) of dz[t,e] x[t,c].  Pass 2 adds the chunks in order.
-constexpr int kGateChunk = 256;
+// Gate gradients, pass 1: block (token chunk of 64, column group of 256,
+// expert group of 16): partial[chunk][e][c] = sum over the chunk's tokens (in
+// order) of dz[t,e] x[t,c]; the column-group-0 blocks also write
+// partial_b[chunk][e] = sum over the chunk's tokens of dz[t,e].  Pass 2 adds
+// the chunks in order.
+constexpr int kGateChunk = 64;
 
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_gate_wgrad_kernel(const float* __restrict__ dz,
                                                              const typename ET::storage* __restrict__ x, int T, int d,
-                                                             int E, float* __restrict__ partial)
+                                                             int E, float* __restrict__ partial,
+                                                             float* __restrict__ partial_b)
 {
     const int t0 = blockIdx.x * kGateChunk, t1 = min(T, t0 + kGateChunk);
     const int c = blockIdx.y * 256 + threadIdx.x;
     const int e0 = blockIdx.z * 16;
-    float acc[16];
-#pragma unroll
-    for (int ee = 0; ee < 16; ++ee)
-        acc[ee] = 0.0f;
     if (c < d) {
+        float acc[16];
+#pragma unroll
+        for (int ee = 0; ee < 16; ++ee)
+            acc[ee] = 0.0f;
         for (int t = t0; t < t1; ++t) {
             float xv;
             if constexpr (ET::kBytes == 2)
@@ -318,31 +345,36 @@ __global__ __launch_bounds__(256) void moe_gate_wgrad_kernel(const float* __rest
             if (e0 + ee < E)
                 partial[((size_t)blockIdx.x * E + e0 + ee) * d + c] = acc[ee];
     }
+    if (blockIdx.y == 0 && threadIdx.x < 16 && e0 + (int)threadIdx.x < E) {
+        const int e = e0 + threadIdx.x;
+        float sb = 0.0f;
+        for (int t = t0; t < t1; ++t)
+            sb += dz[(size_t)t * E + e];
+        partial_b[(size_t)blockIdx.x * E + e] = sb;
+    }
 }
 
-__global__ __launch_bounds__(256) void moe_gate_wgrad_reduce_kernel(const float* __restrict__ partial, int nchunks,
-                                                                    int E, int d, float* __restrict__ dWg)
+// Pass 2: element i < E*d of dWg, then the E entries of dbg, each the sum of
+// its nchunks partials in chunk order.
+__global__ __launch_bounds__(256) void moe_gate_wgrad_reduce_kernel(const float* __restrict__ partial,
+                                                                    const float* __restrict__ partial_b, int nchunks,
+                                                                    int E, int d, float* __restrict__ dWg,
+                                                                    float* __restrict__ dbg)
 {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (size_t)E * d)
-        return;
-    float s = 0.0f;
-    for (int ch = 0; ch < nchunks; ++ch)
-        s += partial[(size_t)ch * E * d + i];
-    dWg[i] = s;
-}
-
-// dbg[e] = sum over t (in order) of dz[t,e].
-__global__ __launch_bounds__(256) void moe_colsum_kernel(const float* __restrict__ dz, int T, int E,
-                                                         float* __restrict__ dbg)
-{
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= E)
-        return;
-    float s = 0.0f;
-    for (int t = 0; t < T; ++t)
-        s += dz[(size_t)t * E + e];
-    dbg[e] = s;
+    const size_t n = (size_t)E * d;
+    if (i < n) {
+        float s = 0.0f;
+        for (int ch = 0; ch < nchunks; ++ch)
+            s += partial[(size_t)ch * n + i];
+        dWg[i] = s;
+    } else if (i < n + E) {
+        const size_t e = i - n;
+        float s = 0.0f;
+        for (int ch = 0; ch < nchunks; ++ch)
+            s += partial_b[(size_t)ch * E + e];
+        dbg[e] = s;
+    }
 }
 
 // n floats set to 0 (a kernel, so that a captured graph holds no memset node).
@@ -435,8 +467,10 @@ extern "C" hipError_t moe_launch_unpermute_bwd(int dtype, const void* dx_perm, c
 
 extern "C" size_t moe_gate_wgrad_partial_bytes(int T, int d, int E)
 {
-    const size_t nch = (size_t)(T + moe::kGateChunk - 1) / moe::kGateChunk;
-    return (nch > 0 ? nch : 1) * (size_t)E * d * sizeof(float);
+    size_t nch = (size_t)(T + moe::kGateChunk - 1) / moe::kGateChunk;
+    if (nch == 0)
+        nch = 1;
+    return nch * (size_t)E * (d + 1) * sizeof(float);  // [nch][E][d], then [nch][E]
 }
 
 extern "C" hipError_t moe_launch_gate_wgrad(int dtype, const float* dz, const void* x, int T, int d, int E,
@@ -444,19 +478,18 @@ extern "C" hipError_t moe_launch_gate_wgrad(int dtype, const float* dz, const vo
 {
     using namespace moe;
     const int nch = (T + kGateChunk - 1) / kGateChunk;
+    float* partial_b = partial + (size_t)nch * E * d;
     const dim3 grid(nch, (d + 255) / 256, (E + 15) / 16), block(256);
     if (dtype == 0)
-        moe_gate_wgrad_kernel<f32_t><<<grid, block, 0, stream>>>(dz, (const float*)x, T, d, E, partial);
+        moe_gate_wgrad_kernel<f32_t><<<grid, block, 0, stream>>>(dz, (const float*)x, T, d, E, partial, partial_b);
     else
-        moe_gate_wgrad_kernel<bf16_t><<<grid, block, 0, stream>>>(dz, (const uint16_t*)x, T, d, E, partial);
+        moe_gate_wgrad_kernel<bf16_t><<<grid, block, 0, stream>>>(dz, (const uint16_t*)x, T, d, E, partial,
+                                                                  partial_b);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const size_t n = (size_t)E * d;
-    moe_gate_wgrad_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), block, 0, stream>>>(partial, nch, E, d, dWg);
-    err = hipGetLastError();
-    if (err != hipSuccess)
-        return err;
-    moe_colsum_kernel<<<dim3((E + 255) / 256), block, 0, stream>>>(dz, T, E, dbg);
+    const size_t n = (size_t)E * d + E;
+    moe_gate_wgrad_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), block, 0, stream>>>(partial, partial_b, nch,
+                                                                                          E, d, dWg, dbg);
     return hipGetLastError();
 }

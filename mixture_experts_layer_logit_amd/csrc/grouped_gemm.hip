@@ -317,18 +317,24 @@ struct EpiArgs {
     int aux_ld;
 };
 
-// 4 consecutive elements of a row as fp32 / from fp32.
+// 4 consecutive elements of a row: loaded as stored (raw4, unpack4), or
+// stored from fp32 (store4).
 template <typename OT>
-__device__ __forceinline__ void load4(const typename OT::storage* p, float* v)
+using raw4_t = typename std::conditional<OT::kBytes == 2, uint2, float4>::type;
+template <typename OT>
+__device__ __forceinline__ raw4_t<OT> load_raw4(const typename OT::storage* p)
+{
+    return *reinterpret_cast<const raw4_t<OT>*>(p);
+}
+template <typename OT>
+__device__ __forceinline__ void unpack4(const raw4_t<OT>& w, float* v)
 {
     if constexpr (OT::kBytes == 2) {
-        const uint2 w = *reinterpret_cast<const uint2*>(p);
         v[0] = __uint_as_float(w.x << 16);
         v[1] = __uint_as_float(w.x & 0xffff0000u);
         v[2] = __uint_as_float(w.y << 16);
         v[3] = __uint_as_float(w.y & 0xffff0000u);
     } else {
-        const float4 w = *reinterpret_cast<const float4*>(p);
         v[0] = w.x;
         v[1] = w.y;
         v[2] = w.z;
@@ -363,7 +369,9 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
                                            int F)
 {
     typedef typename OT::storage T;
-    const int lane = lane_id();
+    // lane-derived addresses stay here, not hoisted before the tile loop
+    int lane = lane_id();
+    __asm__ volatile("" : "+v"(lane));
     const int wm = wave / S::WN, wn = wave % S::WN;
 #pragma unroll
     for (int i = 0; i < S::kFM; ++i) {
@@ -378,6 +386,27 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
             as = ep.a[gather ? gather[t.row0 + m] : t.row0 + m];
         const float* wsc = ep.w ? ep.w + (size_t)t.e * Nw : nullptr;
         constexpr int kJ = (EPI == EPI_SWIGLU) ? S::kFN / 2 : S::kFN;
+        // Backward epilogues: this row fragment's saved u, all loaded before
+        // any of its stores.  Stores and loads retire in issue order, so a
+        // load issued after a store would wait for that store as well.
+        constexpr bool kBwd = (EPI == EPI_DRELU || EPI == EPI_DSWIGLU);
+        raw4_t<OT> ug[kBwd ? kJ : 1][4], uv[EPI == EPI_DSWIGLU ? kJ : 1][4];
+        if constexpr (kBwd) {
+#pragma unroll
+            for (int j = 0; j < kJ; ++j)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = t.n0 + wn * S::kWaveN + j * 32 + 8 * g4 + 4 * (lane >> 5);
+                    ug[j][g4] = raw4_t<OT>{};
+                    if (n < ncols)
+                        ug[j][g4] = load_raw4<OT>(urow + n);
+                    if constexpr (EPI == EPI_DSWIGLU) {
+                        uv[j][g4] = raw4_t<OT>{};
+                        if (n < ncols)
+                            uv[j][g4] = load_raw4<OT>(urow + F + n);
+                    }
+                }
+        }
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
 #pragma unroll
@@ -387,10 +416,10 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
                 if (n >= ncols)
                     continue;
                 float v[4], v2[4], pre[4], pre2[4], uin[4], uin2[4];
-                if (EPI == EPI_DRELU || EPI == EPI_DSWIGLU)
-                    load4<OT>(urow + n, uin);
-                if (EPI == EPI_DSWIGLU)
-                    load4<OT>(urow + F + n, uin2);
+                if constexpr (kBwd)
+                    unpack4<OT>(ug[j][g4], uin);
+                if constexpr (EPI == EPI_DSWIGLU)
+                    unpack4<OT>(uv[j][g4], uin2);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float u = acc.v[i][j][4 * g4 + q];
@@ -425,6 +454,74 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
                     if (EPI == EPI_SWIGLU)
                         store4<OT>(prow + F + n, pre2);
                 }
+            }
+        }
+    }
+}
+
+// Plain epilogue (no activation, no scales) through LDS.  Direct stores
+// from the accumulators write 4 consecutive values of 32 different rows per
+// instruction, pieces HBM takes at well under half its write bandwidth; so
+// each row fragment i of every wave (tile rows wm*kWaveM + i*32 + 0..31, WM
+// bands of 32 rows) is first written to a stage buffer as [band row][column],
+// 16-byte chunks XOR-swizzled by row (writes of a fragment and reads of a
+// row both take the minimum LDS cycles), then stored by the whole block with
+// one 16-byte chunk per lane, a wavefront covering a contiguous row run.
+// Fragments alternate between the two stage buffers, one barrier each.  The
+// caller's K loop must be finished (the first barrier here also covers its
+// last LDS reads).
+template <typename OT, typename S>
+__device__ __forceinline__ void store_tile_lds(const Acc<S>& acc, typename OT::storage* __restrict__ C,
+                                               const TileDec& t, int Nout, int ncols, int wave, uint8_t* buf0,
+                                               uint8_t* buf1)
+{
+    constexpr int kRowsPass = S::WM * 32;
+    constexpr int kRowBytes = S::BN * OT::kBytes;
+    constexpr int kChunks = kRowBytes / 16;
+    static_assert(kRowsPass * kRowBytes <= S::kStage, "one row fragment of the tile fits a stage buffer");
+    // The addresses below depend on the thread index only; an opaque copy of
+    // it keeps the compiler from computing them once before the tile loop
+    // and holding them in registers through every K loop.
+    int tid = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    const int r = wm * 32 + (lane & 31);  // this lane's row within a pass
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < S::kFM; ++i) {
+        uint8_t* buf = (i & 1) ? buf1 : buf0;
+#pragma unroll
+        for (int j = 0; j < S::kFN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int col = wn * S::kWaveN + j * 32 + 8 * g4 + 4 * (lane >> 5);
+                const int byte = col * OT::kBytes;
+                uint8_t* dst = buf + r * kRowBytes + (((byte >> 4) ^ (r % kChunks)) << 4) + (byte & 15);
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    v[q] = acc.v[i][j][4 * g4 + q];
+                if constexpr (OT::kBytes == 2) {
+                    uint2 o;
+                    o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                    o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(dst) = o;
+                } else {
+                    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        lds_barrier();
+        static_assert(kRowsPass * kChunks % S::kThreads == 0, "whole chunks per thread");
+#pragma unroll
+        for (int it = 0; it < kRowsPass * kChunks / S::kThreads; ++it) {
+            const int c = tid + it * S::kThreads;
+            const int rr = c / kChunks, q = c % kChunks;
+            const int m = (rr / 32) * S::kWaveM + i * 32 + (rr % 32);
+            const int col = q * (16 / OT::kBytes);
+            if (m < t.rows && t.n0 + col < ncols) {
+                const uint4 v = *reinterpret_cast<const uint4*>(buf + rr * kRowBytes + ((q ^ (rr % kChunks)) << 4));
+                *reinterpret_cast<uint4*>(C + (size_t)(t.row0 + m) * Nout + t.n0 + col) = v;
             }
         }
     }
@@ -774,7 +871,10 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         }
 
         if (slot < 0) {
-            store_tile<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, gather, Nw, F);
+            if constexpr (EPI == EPI_NONE && ET::kBytes != 1)  // unscaled plain output
+                store_tile_lds<OT, S>(acc, Cb, t, Nout, ncols, wave, lds0, lds1);
+            else
+                store_tile<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, gather, Nw, F);
         } else {
             float* dst = partial + (size_t)slot * S::kTileFloats;
 #pragma unroll
