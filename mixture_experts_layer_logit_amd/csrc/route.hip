@@ -17,41 +17,47 @@ namespace moe {
 // tiling.  Routing decisions therefore do not depend on how this kernel (or
 // any other correct gate) orders its sums.
 //
-// Work split: a block of 4 wavefronts takes 4 tokens; the model dimension is
-// cut into 8-element chunks and thread j of the block takes chunks j,
-// j + 256, ..., so the x rows and Wg rows are read with 16-byte coalesced
-// loads and every wavefront covers a quarter of the row (T/4 blocks keep
-// enough loads in flight to stream x).  Experts go in groups of 8.  A lane's
-// 4 x 8 partial sums are reduced across its wavefront by recursive halving
-// (each exchange halves the values a lane holds: 32 values need
-// 16+8+4+2+1+1 shuffles), then the 4 wavefronts' sums are added in wave
-// order through LDS.  Wg rows are re-read per block from L2.
-constexpr int kGateTokPerBlock = 4;
+// Work split: a block of 4 wavefronts holds 4 / WPT token groups of 4 tokens,
+// WPT wavefronts per group, and runs over the experts in groups of 8.  Lane l
+// of the group's wavefront w takes the 8-element chunks w*64 + l, w*64 + l +
+// 64*WPT, ... of the model dimension, so x rows and Wg rows are read with
+// 16-byte loads (1 KB per wavefront instruction).  WPT follows d: one
+// wavefront per group when a row has at most 128 chunks (every lane busy, no
+// LDS, no barrier), up to 4 for long rows (enough wavefronts in flight at
+// moderate T).  A lane's 4 x 8 partial sums are reduced across its wavefront
+// by recursive halving (each exchange halves the values a lane holds: 32
+// values need 16+8+4+2+1+1 shuffles), then the group's wavefronts are added
+// in wave order through LDS.  x rows are re-read per expert group from cache.
+constexpr int kGateTokPerGroup = 4;
+constexpr int kGateWaves = 4;
 constexpr int kGateExpGroup = 8;
 
-template <typename ET>
+template <typename ET, int WPT>
 __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET::storage* __restrict__ x,
                                                               const typename ET::storage* __restrict__ Wg,
                                                               const float* __restrict__ bg,
                                                               float* __restrict__ logits, int T, int d, int E)
 {
-    constexpr int kVals = kGateTokPerBlock * kGateExpGroup;  // 32 sums per lane
-    __shared__ double s_part[4][kVals];
+    constexpr int kVals = kGateTokPerGroup * kGateExpGroup;  // 32 sums per lane
+    constexpr int kGroups = kGateWaves / WPT;
+    __shared__ double s_part[WPT > 1 ? kGateWaves : 1][kVals];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    const int t0 = blockIdx.x * kGateTokPerBlock;  // block-uniform
-    if (t0 >= T)
+    const int wig = wave % WPT;
+    const int t0 = (blockIdx.x * kGroups + wave / WPT) * kGateTokPerGroup;  // uniform over the group
+    if (WPT == 1 && t0 >= T)
         return;
+    const bool active = t0 < T;  // WPT > 1: every wavefront stays for the barriers
     const int nchunk = d / 8;
     for (int e0 = 0; e0 < E; e0 += kGateExpGroup) {
         double acc[kVals];
 #pragma unroll
         for (int v = 0; v < kVals; ++v)
             acc[v] = 0.0;
-        for (int c = threadIdx.x; c < nchunk; c += 256) {
-            double xd[kGateTokPerBlock][8];
+        for (int c = wig * kWave + lane; active && c < nchunk; c += WPT * kWave) {
+            double xd[kGateTokPerGroup][8];
 #pragma unroll
-            for (int tt = 0; tt < kGateTokPerBlock; ++tt) {
+            for (int tt = 0; tt < kGateTokPerGroup; ++tt) {
                 float xf[8];
                 const int t = min(t0 + tt, T - 1);  // rows past T are computed but not stored
                 load8(x + (size_t)t * d + (size_t)c * 8, xf);
@@ -68,7 +74,7 @@ __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET:
                 for (int i = 0; i < 8; ++i) {
                     const double wd = (double)wf[i];
 #pragma unroll
-                    for (int tt = 0; tt < kGateTokPerBlock; ++tt)
+                    for (int tt = 0; tt < kGateTokPerGroup; ++tt)
                         acc[tt * kGateExpGroup + ee] = fma(xd[tt][i], wd, acc[tt * kGateExpGroup + ee]);
                 }
             }
@@ -91,23 +97,31 @@ __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET:
             }
             n = half;
         }
-        const double s = v[0] + __shfl_xor(v[0], 1);
+        double sum = v[0] + __shfl_xor(v[0], 1);
         // lane l now holds value index (l >> 1): token (l >> 4), expert ((l >> 1) & 7)
-        if ((lane & 1) == 0)
-            s_part[wave][lane >> 1] = s;
-        __syncthreads();
-        if (threadIdx.x < kVals) {
-            const int t = t0 + threadIdx.x / kGateExpGroup;
-            const int e = e0 + threadIdx.x % kGateExpGroup;
-            double sum = ((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
-                         s_part[3][threadIdx.x];
-            if (t < T && e < E) {
-                if (bg)
-                    sum += (double)bg[e];
-                logits[(size_t)t * E + e] = (float)sum;
+        int idx = lane >> 1;
+        bool writer = (lane & 1) == 0;
+        if constexpr (WPT > 1) {
+            if (writer)
+                s_part[wave][idx] = sum;
+            __syncthreads();
+            writer = wig == 0 && lane < kVals;
+            idx = lane;
+            if (writer) {
+                sum = s_part[wave][idx];
+#pragma unroll
+                for (int w = 1; w < WPT; ++w)
+                    sum += s_part[wave + w][idx];
             }
+            __syncthreads();  // s_part is reused by the next expert group
         }
-        __syncthreads();  // s_part is reused by the next expert group
+        const int t = t0 + idx / kGateExpGroup;
+        const int e = e0 + idx % kGateExpGroup;
+        if (writer && active && t < T && e < E) {
+            if (bg)
+                sum += (double)bg[e];
+            logits[(size_t)t * E + e] = (float)sum;
+        }
     }
 }
 
@@ -478,13 +492,25 @@ extern "C" hipError_t moe_launch_gate(int dtype, const void* x, const void* Wg, 
                                       int T, int d, int E, hipStream_t stream)
 {
     using namespace moe;
-    const dim3 grid((T + kGateTokPerBlock - 1) / kGateTokPerBlock), block(256);
-    if (dtype == 0)
-        moe_gate_logits_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)x, (const float*)Wg, bg, logits,
-                                                                  T, d, E);
-    else
-        moe_gate_logits_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)x, (const uint16_t*)Wg, bg,
-                                                                   logits, T, d, E);
+    const int nchunk = d / 8;
+    const int wpt = nchunk > 256 ? 4 : nchunk > 128 ? 2 : 1;
+    const int tok_per_block = kGateTokPerGroup * (kGateWaves / wpt);
+    const dim3 grid((T + tok_per_block - 1) / tok_per_block), block(kGateWaves * kWave);
+    auto go = [&](auto et, auto wpt_c) {
+        typedef decltype(et) ET;
+        typedef typename ET::storage S;
+        moe_gate_logits_kernel<ET, decltype(wpt_c)::value>
+            <<<grid, block, 0, stream>>>((const S*)x, (const S*)Wg, bg, logits, T, d, E);
+    };
+    if (dtype == 0) {
+        if (wpt == 4) go(f32_t{}, std::integral_constant<int, 4>{});
+        else if (wpt == 2) go(f32_t{}, std::integral_constant<int, 2>{});
+        else go(f32_t{}, std::integral_constant<int, 1>{});
+    } else {
+        if (wpt == 4) go(bf16_t{}, std::integral_constant<int, 4>{});
+        else if (wpt == 2) go(bf16_t{}, std::integral_constant<int, 2>{});
+        else go(bf16_t{}, std::integral_constant<int, 1>{});
+    }
     return hipGetLastError();
 }
 
