@@ -44,6 +44,9 @@ size_t moe_gate_wgrad_partial_bytes(int T, int d, int E);
 hipError_t moe_launch_zero(float* p, size_t n, hipStream_t stream);
 hipError_t moe_launch_gate_wgrad(int dtype, const float* dz, const void* x, int T, int d, int E, float* partial,
                                  float* dWg, float* dbg, hipStream_t stream);
+hipError_t moe_launch_grouped_gemm_wt(int epi, const void* A, const void* W, void* C, const int32_t* offsets, int E,
+                                      int K, int Nw, int Nout, int F, int max_rows, int mean_rows, int ncu,
+                                      float* partial, const void* aux_in, int aux_ld, hipStream_t stream);
 hipError_t moe_launch_grouped_gemm_kgrp(int dtype, const void* A, const void* W, float* C, const int32_t* kofs, int E,
                                         int lda, int M, int N, int ncu, hipStream_t stream);
 hipError_t moe_launch_quantize_fp8(int dtype, const void* src, long long R, int K, uint8_t* codes, float* scales,
@@ -410,8 +413,10 @@ LayoutBwd layout_bwd_of(const moe_problem* p)
     L.dz = take(T * E * 4);
     L.du = take(T * k * n1 * b);
     L.dx_perm = take(T * k * d * b);
-    L.W1T = take(E * n1 * d * b);
-    L.W2T = take(E * d * F * b);
+    // transposed weights: fp32 only (the bf16 GEMMs read W1 and W2 transposed in place)
+    const bool wt = p->dtype == MOE_BF16;
+    L.W1T = take(wt ? 0 : E * n1 * d * b);
+    L.W2T = take(wt ? 0 : E * d * F * b);
     L.kofs = take((E + 1) * 4);
     L.d_ypT = take(d * ld * b);
     L.hT = take(F * ld * b);
@@ -973,15 +978,25 @@ moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, con
     CHECK(hip_status(moe_launch_router_bwd(logits, info->topk_idx, info->slot, d_w, T, E, k, p->normalize, p->lambda,
                                            dz, s), "router backward launch"));
     // input gradients of the expert layers: dh = d_yp W2[e] (+ activation backward), dx_perm = du W1[e]
-    CHECK(hip_status(moe_launch_transpose(dt, W2, E, d, F, W2T, s), "transpose launch"));
-    CHECK(hip_status(moe_launch_transpose(dt, W1, E, n1, d, W1T, s), "transpose launch"));
     const int depi = p->act == MOE_ACT_SWIGLU ? 4 : 3;
-    CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, depi, d_yp, nullptr, 0, W2T, du, offsets, E, d, F, n1, F, rows,
-                                             mean_rows_of(p), cu_count(), partial, saved->u, nullptr, n1, s),
-                     "expert down backward launch"));
-    CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, 0, du, nullptr, 0, W1T, dx_perm, offsets, E, n1, d, d, d, rows,
-                                             mean_rows_of(p), cu_count(), partial, nullptr, nullptr, 0, s),
-                     "expert up backward launch"));
+    if (p->dtype == MOE_BF16) {
+        // W2[e] is [d][F] and W1[e] is [n1][d]: K-major weight operands, read as stored
+        CHECK(hip_status(moe_launch_grouped_gemm_wt(depi, d_yp, W2, du, offsets, E, d, F, n1, F, rows,
+                                                    mean_rows_of(p), cu_count(), partial, saved->u, n1, s),
+                         "expert down backward launch"));
+        CHECK(hip_status(moe_launch_grouped_gemm_wt(0, du, W1, dx_perm, offsets, E, n1, d, d, d, rows,
+                                                    mean_rows_of(p), cu_count(), partial, nullptr, 0, s),
+                         "expert up backward launch"));
+    } else {
+        CHECK(hip_status(moe_launch_transpose(dt, W2, E, d, F, W2T, s), "transpose launch"));
+        CHECK(hip_status(moe_launch_transpose(dt, W1, E, n1, d, W1T, s), "transpose launch"));
+        CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, depi, d_yp, nullptr, 0, W2T, du, offsets, E, d, F, n1, F,
+                                                 rows, mean_rows_of(p), cu_count(), partial, saved->u, nullptr, n1, s),
+                         "expert down backward launch"));
+        CHECK(hip_status(moe_launch_grouped_gemm(p->dtype, 0, du, nullptr, 0, W1T, dx_perm, offsets, E, n1, d, d, d,
+                                                 rows, mean_rows_of(p), cu_count(), partial, nullptr, nullptr, 0, s),
+                         "expert up backward launch"));
+    }
     // weight gradients: per expert, reductions over its rows
     CHECK(hip_status(moe_launch_kofs(offsets, E, rows, kSegAlign, kofs, s), "segment offsets launch"));
     void* d_ypT = at<char>(ws, L.d_ypT);

@@ -112,6 +112,27 @@ struct GemmShape {
 // (row / (256/RB)) mod (chunks per row) gives the rows of any 16-row group
 // that share banks distinct chunk slots, so reading one chunk of 16
 // consecutive rows touches all 64 banks once.
+// Swizzle term of row `row` of a transposed (WT) weight slice: the 32-byte
+// column block b is stored at b ^ wt_f(row).  One transpose read touches
+// rows k0 + {0..3, 8..11} (or + 4) in two adjacent blocks; wt_f takes the 8
+// distinct values 0..7 there, so the 16 row segments fall 2 per 8-bank group
+// (the minimum for 512 bytes on 64 banks).
+__device__ __forceinline__ int wt_f(int row)
+{
+    return ((row & 3) << 1) | ((row >> 3) & 1);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b16 at an LDS location reached through a generic pointer
+// into a __shared__ array.
+__device__ __forceinline__ v4i16 ds_read_tr16(const uint8_t* p)
+{
+    typedef __attribute__((address_space(3))) v4i16* lds_v4_t;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(__attribute__((address_space(3))) void*)p);
+}
+
 template <typename S>
 __device__ __forceinline__ uint32_t swz(int row, int c)
 {
@@ -536,12 +557,22 @@ __device__ __forceinline__ size_t partial_index(int wave, int i, int j, int g, i
     return ((((size_t)(wave * S::kFM + i) * S::kFN + j) * 4 + g) * kWave + lane) * 4;
 }
 
+// WT (weights stored transposed, bf16): W[e] is [K][Nw], Nw contiguous, as the
+// backward's input-gradient GEMMs find W2 [d][F] and W1 [n1][d].  A K slice
+// of the weight tile is then kBK rows of BN consecutive columns; the DMA lays
+// it out [k][n] (16-byte chunks of 32-byte column blocks XOR-swizzled by the
+// row), and each MFMA weight fragment (8 consecutive k of one column) is two
+// ds_read_b64_tr_b16: within a group of 16 lanes that instruction hands lane
+// i value i % 4 of the 64-bit chunk at lane 4j + i / 4's address as its j-th
+// value, so lanes pointing at rows k0..k0+3, columns c0 + 4 (s % 4) give lane
+// i the column c0 + i at k0..k0+3.
+//
 // KG (K-grouped, the weight gradients): one dense output per expert,
 // C[e] = A W^T over expert e's K range [offsets[e], offsets[e+1]) (device
 // array, multiples of the K slice): A [max_rows][K], W [Nw][K] row-major with
 // row stride K, C [E][max_rows][Nout] (Nout == Nw).  No row segments, no
 // gather, no split.
-template <typename ET, typename OT, typename S, int EPI, bool KG = false>
+template <typename ET, typename OT, typename S, int EPI, bool KG = false, bool WT = false>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
 void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const int32_t* __restrict__ gather,
                              int gather_rows, const typename ET::storage* __restrict__ W,
@@ -585,6 +616,24 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
     const int blk_row0 = (S::RB == 128) ? 8 * (wave & 1) : 0;
     const int lchunk = lphys ^ (((blk_row0 + lrow) >> S::kSwzShift) & (S::kNch - 1));
     const uint32_t lane_chunk = (uint32_t)(lchunk << 4);
+    // WT: weight tile rows are k, kWtPitch bytes of columns each.  Lane s of
+    // lane group g (16 lanes) reads rows 16 kk + 8 (g >> 1) + (s >> 2) (+4 for
+    // a fragment's second half), columns wn*kWaveN + 32 j + 16 (g & 1) +
+    // 4 (s & 3).  The swizzle term wt_f(row) depends only on row bits 0, 1
+    // and 3, which are (s >> 2) and (g >> 1) here, so it is one value per lane.
+    static_assert(!WT || (ET::kBytes == 2 && S::kChunks == 1), "WT is a bf16 layout");
+    constexpr uint32_t kWtPitch = S::BN * 2;
+    uint32_t rdBT[S::kFN];
+    if constexpr (WT) {
+        const int g = lane >> 4, sl = lane & 15;
+        const int row = 8 * (g >> 1) + (sl >> 2);
+        const int f = wt_f(row);
+#pragma unroll
+        for (int j = 0; j < S::kFN; ++j) {
+            const int blk = (wn * S::kWaveN + 32 * j) / 16 + (g & 1);
+            rdBT[j] = S::kLdsA + row * kWtPitch + ((blk ^ f) << 5) + 8 * (sl & 3);
+        }
+    }
 
     const int tile_cols = (EPI == EPI_SWIGLU) ? S::BN / 2 : S::BN;
     const int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? F : Nout;
@@ -674,17 +723,28 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 wrow = t.n0 + r;
             }
             voffB[i] = (uint32_t)(wrow + lrow) * rowK + lane_chunk;
+            if constexpr (WT) {
+                // 1 KB block = 1024 / kWtPitch rows of the [k][n] slice; the
+                // lane's physical chunk holds the logical one of wt_f(row)
+                constexpr int kRowsB = 1024 / kWtPitch, kChB = kWtPitch / 16;
+                const int blk = wave + kWaves * i;
+                const int row = kRowsB * blk + lane / kChB, pc = lane % kChB;
+                const int lb = (pc >> 1) ^ wt_f(row);
+                voffB[i] = (uint32_t)row * (uint32_t)Nw * 2u + (uint32_t)(t.n0 + 16 * lb + 8 * (pc & 1)) * 2u;
+            }
         }
 
         auto issue = [&](int kt, int stage) {
             const uint32_t soff = (uint32_t)kt * S::RB;
+            // WT: the slice is kBK rows further down W[e]
+            const uint32_t soffB = WT ? (uint32_t)kt * S::kBK * (uint32_t)Nw * 2u : soff;
             const uint32_t dst = stage_addr[stage] + wave * 1024;
 #pragma unroll
             for (int i = 0; i < S::kBlkA; ++i)
                 dma16(rsA, dst + kWaves * i * 1024, voffA[i], soff);
 #pragma unroll
             for (int i = 0; i < S::kBlkB; ++i)
-                dma16(rsW, dst + S::kLdsA + kWaves * i * 1024, voffB[i], soff);
+                dma16(rsW, dst + S::kLdsA + kWaves * i * 1024, voffB[i], soffB);
         };
 
         Acc<S> acc;
@@ -716,7 +776,12 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             auto rd = [&](uint32_t off) { return *reinterpret_cast<const i32x4*>(buf + off); };
 #pragma unroll
             for (int j = 0; j < S::kFN; ++j) {
-                if constexpr (S::kChunks == 2) {
+                if constexpr (WT) {
+                    const uint8_t* p = buf + rdBT[j] + 16 * kk * kWtPitch;
+                    const i32x2 lo = __builtin_bit_cast(i32x2, ds_read_tr16(p));
+                    const i32x2 hi = __builtin_bit_cast(i32x2, ds_read_tr16(p + 4 * kWtPitch));
+                    f.a[j] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+                } else if constexpr (S::kChunks == 2) {
                     f.a[j].lo = rd(rdB[kk][0] + j * 32 * S::RB);
                     f.a[j].hi = rd(rdB[kk][1] + j * 32 * S::RB);
                 } else {
@@ -963,7 +1028,7 @@ struct GemmArgs {
     hipStream_t stream;
 };
 
-template <typename ET, typename OT, typename S, int EPI>
+template <typename ET, typename OT, typename S, int EPI, bool WT = false>
 hipError_t launch_one(const GemmArgs& g)
 {
     typedef typename ET::storage T;
@@ -981,7 +1046,7 @@ hipError_t launch_one(const GemmArgs& g)
         grid = (tiles_max + 7) / 8 * 8;
     if (grid < 1)
         grid = 1;
-    moe_grouped_gemm_kernel<ET, OT, S, EPI><<<dim3((unsigned)grid), dim3(S::kThreads), 0, g.stream>>>(
+    moe_grouped_gemm_kernel<ET, OT, S, EPI, false, WT><<<dim3((unsigned)grid), dim3(S::kThreads), 0, g.stream>>>(
         (const T*)g.A, g.gather, g.gather_rows, (const T*)g.W, (TO*)g.C, g.offsets, g.E, g.K, g.Nw, g.Nout, g.F,
         g.max_rows, g.partial, g.sc);
     hipError_t err = hipGetLastError();
@@ -1007,6 +1072,18 @@ hipError_t launch_epi(int epi, const GemmArgs& g)
             return launch_one<ET, OT, S, EPI_DSWIGLU>(g);
     }
     return launch_one<ET, OT, S, EPI_NONE>(g);
+}
+
+// Transposed-weight launches (bf16): the plain and activation-backward
+// epilogues of the input-gradient GEMMs.
+template <typename S>
+hipError_t launch_wt(int epi, const GemmArgs& g)
+{
+    if (epi == EPI_DRELU)
+        return launch_one<bf16_t, bf16_t, S, EPI_DRELU, true>(g);
+    if (epi == EPI_DSWIGLU)
+        return launch_one<bf16_t, bf16_t, S, EPI_DSWIGLU, true>(g);
+    return launch_one<bf16_t, bf16_t, S, EPI_NONE, true>(g);
 }
 }  // namespace
 
@@ -1072,6 +1149,24 @@ extern "C" hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A,
     if (mean_rows >= 128)
         return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, g);
     return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_SMALL_TILE>>(epi, g);
+}
+
+// bf16 grouped GEMM with the weights stored transposed: W [E][K][Nw] (Nw
+// contiguous), so C = A W[e] per segment.  epi: 0 none, 3 ReLU backward, 4
+// SwiGLU backward (aux_in / aux_ld as moe_launch_grouped_gemm).  No gather.
+// Nw a multiple of 64; other arguments as moe_launch_grouped_gemm.
+extern "C" hipError_t moe_launch_grouped_gemm_wt(int epi, const void* A, const void* W, void* C,
+                                                 const int32_t* offsets, int E, int K, int Nw, int Nout, int F,
+                                                 int max_rows, int mean_rows, int ncu, float* partial,
+                                                 const void* aux_in, int aux_ld, hipStream_t stream)
+{
+    const GemmArgs g = {A, nullptr, 0, W, C, offsets, E, K, Nw, Nout, F, max_rows, ncu, partial,
+                        EpiArgs{nullptr, nullptr, aux_in, nullptr, aux_ld}, stream};
+    if (mean_rows >= 512)
+        return launch_wt<GemmShape<bf16_t, MOE_LARGE_TILE>>(epi, g);
+    if (mean_rows >= 128)
+        return launch_wt<GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, g);
+    return launch_wt<GemmShape<bf16_t, MOE_SMALL_TILE>>(epi, g);
 }
 
 // FP8 grouped GEMM: A [rows][K] and W [E][Nw][K] hold E4M3 codes, a_scale

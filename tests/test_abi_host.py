@@ -227,7 +227,8 @@ def backward_formula(T, d, E, k, F, act, b):
     nch = max((T + 63) // 64, 1)  # token chunks of the gate gradients' first pass
     tile = 128 * 128 if b == 4 else 256 * 256 if T * k // E >= 512 else 128 * 128 if T * k // E >= 128 else 64 * 256
     return (r(T * k * d * b) + r(T * k * 4) + r(T * E * 4) + r(T * k * n1 * b) + r(T * k * d * b)
-            + r(E * n1 * d * b) + r(E * d * F * b) + r((E + 1) * 4)
+            + (r(E * n1 * d * b) + r(E * d * F * b) if b == 4 else 0)  # transposed weights, fp32 only
+            + r((E + 1) * 4)
             + r(d * ld * b) + r(F * ld * b) + r(n1 * ld * b) + r(d * ld * b)
             + r(nch * E * (d + 1) * 4) + r(256 * tile * 4))
 
