@@ -262,7 +262,8 @@ moe_status moe_forward_train(const moe_problem* p, const void* x, const void* Wg
                              const moe_saved* saved, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace for moe_backward (gradients of the permuted rows,
- * transposed weights, transposed row operands of the weight gradients).  Host
+ * transposed row operands of the weight gradients, and for fp32 layers
+ * transposed copies of W1 and W2; bf16 layers read them as stored).  Host
  * only.  MOE_ERR_UNSUPPORTED when an operand [max(d,F,n1)][T*k + 64E] exceeds
  * 32-bit offsets. */
 moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes);
