@@ -384,7 +384,8 @@ __device__ __forceinline__ void store4(typename OT::storage* p, const float* v)
 //   EPI_DRELU:   du[f] = u[f] > 0 ? dh : 0
 //   EPI_DSWIGLU: g = u[f], v = u[F+f], s = 1/(1+e^-g):
 //                du[f] = dh v s (1 + g (1 - s)),  du[F+f] = dh g s
-template <typename OT, typename S, int EPI>
+// ONLY_I >= 0: store row fragment ONLY_I alone (the others are not read).
+template <typename OT, typename S, int EPI, int ONLY_I = -1>
 __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::storage* __restrict__ C, const TileDec& t,
                                            int Nout, int ncols, int wave, EpiArgs ep, const int32_t* gather, int Nw,
                                            int F)
@@ -396,6 +397,8 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
     const int wm = wave / S::WN, wn = wave % S::WN;
 #pragma unroll
     for (int i = 0; i < S::kFM; ++i) {
+        if (ONLY_I >= 0 && i != ONLY_I)
+            continue;
         const int m = wm * S::kWaveM + i * 32 + (lane & 31);
         if (m >= t.rows)
             continue;
@@ -956,9 +959,37 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
 #endif
 }
 
-// Second pass of the tail split: one wavefront per (split tile, wave slot)
-// adds that slot's K parts in part order and stores its share of the tile
-// through the same epilogue (so every CU takes part, not one block per tile).
+// Second pass of the tail split: one wavefront per (split tile, wave slot,
+// row fragment) adds that fragment's K parts in part order and stores it
+// through the same epilogue (kFM times the work items of one per wave slot,
+// so the reduction is not latency-bound on a few wavefronts per CU).
+template <typename OT, typename S, int EPI, int I>
+__device__ __forceinline__ void tail_fragment(const float* __restrict__ partial, int j, int parts, int wave, int lane,
+                                              typename OT::storage* __restrict__ C, const TileDec& t, int Nout,
+                                              int ncols, EpiArgs sc, const int32_t* gather, int Nw, int F)
+{
+    Acc<S> acc;
+#pragma unroll
+    for (int jj = 0; jj < S::kFN; ++jj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc.v[I][jj][v] = 0.0f;
+    for (int part = 0; part < parts; ++part) {
+        const float* src = partial + (size_t)(j * parts + part) * S::kTileFloats;
+#pragma unroll
+        for (int jj = 0; jj < S::kFN; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 p = *reinterpret_cast<const float4*>(src + partial_index<S>(wave, I, jj, g, lane));
+                acc.v[I][jj][4 * g] += p.x;
+                acc.v[I][jj][4 * g + 1] += p.y;
+                acc.v[I][jj][4 * g + 2] += p.z;
+                acc.v[I][jj][4 * g + 3] += p.w;
+            }
+    }
+    store_tile<OT, S, EPI, I>(acc, C, t, Nout, ncols, wave, sc, gather, Nw, F);
+}
+
 template <typename OT, typename S, int EPI>
 __global__ __launch_bounds__(256) void moe_grouped_gemm_tail_kernel(
     typename OT::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E, int K, int Nw, int Nout, int F,
@@ -978,35 +1009,23 @@ __global__ __launch_bounds__(256) void moe_grouped_gemm_tail_kernel(
     const int full = total - total % G;
     const int tail = total - full;
     const int lane = lane_id();
-    const int nwork = tail * S::kWaves;
+    static_assert(S::kFM <= 4, "row fragments per wave slot");
+    const int nwork = tail * S::kWaves * S::kFM;
     for (int wk = blockIdx.x * 4 + threadIdx.x / kWave; wk < nwork; wk += gridDim.x * 4) {
-        const int j = wk / S::kWaves, wave = wk % S::kWaves;
+        const int fi = wk % S::kFM, ws = wk / S::kFM;
+        const int j = ws / S::kWaves, wave = ws % S::kWaves;
         const TileDec t = decode_tile<S>(full + j, s_pref, offsets, E, max_rows, ntn, tile_cols);
-        Acc<S> acc;
-#pragma unroll
-        for (int i = 0; i < S::kFM; ++i)
-#pragma unroll
-            for (int jj = 0; jj < S::kFN; ++jj)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc.v[i][jj][v] = 0.0f;
-        for (int part = 0; part < parts; ++part) {
-            const float* src = partial + (size_t)(j * parts + part) * S::kTileFloats;
-#pragma unroll
-            for (int i = 0; i < S::kFM; ++i)
-#pragma unroll
-                for (int jj = 0; jj < S::kFN; ++jj)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const float4 p =
-                            *reinterpret_cast<const float4*>(src + partial_index<S>(wave, i, jj, g, lane));
-                        acc.v[i][jj][4 * g] += p.x;
-                        acc.v[i][jj][4 * g + 1] += p.y;
-                        acc.v[i][jj][4 * g + 2] += p.z;
-                        acc.v[i][jj][4 * g + 3] += p.w;
-                    }
-        }
-        store_tile<OT, S, EPI>(acc, C, t, Nout, ncols, wave, sc, gather, Nw, F);
+        if (fi == 0)
+            tail_fragment<OT, S, EPI, 0>(partial, j, parts, wave, lane, C, t, Nout, ncols, sc, gather, Nw, F);
+        else if (fi == 1)
+            tail_fragment<OT, S, EPI, (S::kFM > 1 ? 1 : 0)>(partial, j, parts, wave, lane, C, t, Nout, ncols, sc,
+                                                              gather, Nw, F);
+        else if (fi == 2)
+            tail_fragment<OT, S, EPI, (S::kFM > 2 ? 2 : 0)>(partial, j, parts, wave, lane, C, t, Nout, ncols, sc,
+                                                              gather, Nw, F);
+        else
+            tail_fragment<OT, S, EPI, (S::kFM > 3 ? 3 : 0)>(partial, j, parts, wave, lane, C, t, Nout, ncols, sc,
+                                                              gather, Nw, F);
     }
 }
 
@@ -1052,8 +1071,10 @@ hipError_t launch_one(const GemmArgs& g)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || g.partial == nullptr)
         return err;
-    // at most kSplitSlots / 2 split tiles (each has >= 2 parts) x kWaves wave slots, 4 per block
-    moe_grouped_gemm_tail_kernel<OT, S, EPI><<<dim3(kSplitSlots / 2 * S::kWaves / 4), dim3(256), 0, g.stream>>>(
+    // at most kSplitSlots / 2 split tiles (each has >= 2 parts) x kWaves wave slots x kFM row
+    // fragments, 4 per block
+    moe_grouped_gemm_tail_kernel<OT, S, EPI>
+        <<<dim3(kSplitSlots / 2 * S::kWaves * S::kFM / 4), dim3(256), 0, g.stream>>>(
         (TO*)g.C, g.offsets, g.E, g.K, g.Nw, g.Nout, g.F, g.max_rows, (int)grid, g.partial, g.sc, g.gather);
     return hipGetLastError();
 }
