@@ -27,7 +27,9 @@ namespace moe {
 // moderate T).  A lane's 4 x 8 partial sums are reduced across its wavefront
 // by recursive halving (each exchange halves the values a lane holds: 32
 // values need 16+8+4+2+1+1 shuffles), then the group's wavefronts are added
-// in wave order through LDS.  x rows are re-read per expert group from cache.
+// in wave order through LDS.  Expert groups are spread over blockIdx.y (every
+// group of a block shares its e0, so the barriers stay uniform); x rows are
+// re-read per expert group from cache.
 constexpr int kGateTokPerGroup = 4;
 constexpr int kGateWaves = 4;
 constexpr int kGateExpGroup = 8;
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET:
         return;
     const bool active = t0 < T;  // WPT > 1: every wavefront stays for the barriers
     const int nchunk = d / 8;
-    for (int e0 = 0; e0 < E; e0 += kGateExpGroup) {
+    for (int e0 = blockIdx.y * kGateExpGroup; e0 < E; e0 += gridDim.y * kGateExpGroup) {
         double acc[kVals];
 #pragma unroll
         for (int v = 0; v < kVals; ++v)
@@ -495,7 +497,8 @@ extern "C" hipError_t moe_launch_gate(int dtype, const void* x, const void* Wg, 
     const int nchunk = d / 8;
     const int wpt = nchunk > 256 ? 4 : nchunk > 128 ? 2 : 1;
     const int tok_per_block = kGateTokPerGroup * (kGateWaves / wpt);
-    const dim3 grid((T + tok_per_block - 1) / tok_per_block), block(kGateWaves * kWave);
+    const int egroups = (E + kGateExpGroup - 1) / kGateExpGroup;
+    const dim3 grid((T + tok_per_block - 1) / tok_per_block, egroups), block(kGateWaves * kWave);
     auto go = [&](auto et, auto wpt_c) {
         typedef decltype(et) ET;
         typedef typename ET::storage S;
