@@ -494,7 +494,9 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
 // Fragments alternate between the two stage buffers, one barrier each.  The
 // caller's K loop must be finished (the first barrier here also covers its
 // last LDS reads).
-template <typename OT, typename S>
+// NT: non-temporal global stores (outputs no later kernel here reads soon:
+// the weight gradients).
+template <typename OT, typename S, bool NT = false>
 __device__ __forceinline__ void store_tile_lds(const Acc<S>& acc, typename OT::storage* __restrict__ C,
                                                const TileDec& t, int Nout, int ncols, int wave, uint8_t* buf0,
                                                uint8_t* buf1)
@@ -545,7 +547,13 @@ __device__ __forceinline__ void store_tile_lds(const Acc<S>& acc, typename OT::s
             const int col = q * (16 / OT::kBytes);
             if (m < t.rows && t.n0 + col < ncols) {
                 const uint4 v = *reinterpret_cast<const uint4*>(buf + rr * kRowBytes + ((q ^ (rr % kChunks)) << 4));
-                *reinterpret_cast<uint4*>(C + (size_t)(t.row0 + m) * Nout + t.n0 + col) = v;
+                uint4* dst = reinterpret_cast<uint4*>(C + (size_t)(t.row0 + m) * Nout + t.n0 + col);
+                if constexpr (NT) {
+                    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+                    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(dst));
+                } else {
+                    *dst = v;
+                }
             }
         }
     }
@@ -940,7 +948,7 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
 
         if (slot < 0) {
             if constexpr (EPI == EPI_NONE && ET::kBytes != 1)  // unscaled plain output
-                store_tile_lds<OT, S>(acc, Cb, t, Nout, ncols, wave, lds0, lds1);
+                store_tile_lds<OT, S, KG>(acc, Cb, t, Nout, ncols, wave, lds0, lds1);
             else
                 store_tile<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, gather, Nw, F);
         } else {
