@@ -105,8 +105,20 @@ SMALL = {
     "many_small_s": FULL["many_small"].with_(name="many_small_s", T=2048, d=256, F=128, seed=2005),
 }
 
+# Large token counts at small widths: index arithmetic, grids and chunk loops
+# at about a million routed rows (routing, permutation, combine) and at a
+# quarter million for the backward (long K ranges of the weight gradients,
+# many gate-gradient chunks).
+LARGE = {
+    "large_t_fwd": Case("large_t_fwd", T=(1 << 20) + 13, d=64, E=64, k=2, F=64, act="relu", dtype="bf16",
+                        seed=3001, cf=1.0, logits="given"),
+    "large_t_bwd": Case("large_t_bwd", T=(1 << 18) + 7, d=64, E=16, k=2, F=64, act="swiglu", dtype="bf16",
+                        seed=3002, cf=1.25, normalize=True),
+}
+
 CASES = dict(FULL)
 CASES.update(SMALL)
+CASES.update(LARGE)
 
 
 def get(name: str) -> Case:

@@ -30,7 +30,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 SMALL = list(moe_inputs.SMALL)
-FULL_SAMPLED = {"fastmoe_txl": 16, "mixtral": 6, "skywork_m_zipf": 6, "many_small": 16}
+FULL_SAMPLED = {"fastmoe_txl": 16, "mixtral": 6, "skywork_m_zipf": 6, "many_small": 16, "large_t_bwd": 12}
 
 
 def act_code(case):

@@ -410,6 +410,19 @@ def test_forward_full_size_sampled(name):
     print(f"  max-abs-rel {err:.3e} on {len(toks)} tokens, dropped {case.T * case.k - disp['P']}", flush=True)
 
 
+def test_forward_large_t():
+    """About a million tokens (given logits, capacity 1.0): routing and the
+    permutation in full, outputs on sampled tokens."""
+    case = moe_inputs.get("large_t_fwd")
+    inp = inputs(case.name)
+    print(f"[forward-large] {case.name} T={case.T}", flush=True)
+    out = run_forward(case, inp)
+    _ze, _z32, _idx, _w, disp = oracle_route(case, inp)
+    toks = sample_tokens(case, inp, disp)
+    err, _ = check_forward(case, inp, out, toks)
+    print(f"  max-abs-rel {err:.3e} on {len(toks)} tokens, dropped {case.T * case.k - disp['P']}", flush=True)
+
+
 def test_forward_deterministic_and_workspace_independent():
     case = moe_inputs.get("skywork_m_zipf_s")
     inp = inputs(case.name)
