@@ -88,7 +88,7 @@ def _load():
     lib.orc_expert_ffn_fp8.argtypes = [I, I, I, P, P, P, P, I, P, D, P, P]
     lib.orc_ffn_rows_fp8.argtypes = [I, I, I, I, P, P, P, P, P, P, P, I, P, P, P]
     lib.orc_down_rows_fp8.argtypes = [I, I, I, P, P, P, P, P, I, P, P]
-    lib.orc_backward.argtypes = [I, I, I, I, I, I, I, I, D, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_backward.argtypes = [I, I, I, I, I, I, I, I, D, D, D, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.orc_forward_tokens_fp8.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P]
     _lib = lib
     return lib
@@ -447,10 +447,12 @@ def quant_weights_fp8(W):
 
 
 # ---------------------------------------------------------------- backward
-def backward(x, Wg, W1, W2, z32, topk_idx, slot, dy, act, F, normalize_flag=False, lam=1.0):
+def backward(x, Wg, W1, W2, z32, topk_idx, slot, dy, act, F, normalize_flag=False, lam=1.0, aux_coef=0.0,
+             z_coef=0.0):
     """Gradient of the layer (see orc_backward): dict of float64 dx [T,d], dWg
     [E,d], dbg [E], dW1 [E,n1,d], dW2 [E,d,F], dz [T,E].  Wg None means the
-    logits were given: dWg and dbg come back as zeros and dx has no gate term."""
+    logits were given: dWg and dbg come back as zeros and dx has no gate term.
+    aux_coef, z_coef: the balancing losses of router_stats added to the loss."""
     x = _c(x)
     T, d = x.shape
     W1 = _c(W1)
@@ -466,7 +468,8 @@ def backward(x, Wg, W1, W2, z32, topk_idx, slot, dy, act, F, normalize_flag=Fals
     Wgc = None if Wg is None else _c(Wg)
     out = {"dx": np.empty((T, d)), "dWg": np.empty((E, d)), "dbg": np.empty(E), "dW1": np.empty((E, n1, d)),
            "dW2": np.empty((E, d, F)), "dz": np.empty((T, E))}
-    _load().orc_backward(T, d, E, k, F, int(act), _dtype_code(x), int(bool(normalize_flag)), float(lam), _ptr(x),
+    _load().orc_backward(T, d, E, k, F, int(act), _dtype_code(x), int(bool(normalize_flag)), float(lam),
+                         float(aux_coef), float(z_coef), _ptr(x),
                          _ptr(Wgc), _ptr(W1), _ptr(W2), _ptr(z), _ptr(idx), _ptr(sl), _ptr(dyc), _ptr(out["dx"]),
                          _ptr(out["dWg"]), _ptr(out["dbg"]), _ptr(out["dW1"]), _ptr(out["dW2"]), _ptr(out["dz"]))
     return out

@@ -655,11 +655,18 @@ void orc_forward_tokens_fp8(int d, int k, int F, int act, int dtype, const void*
  *   dz = ds, or with the normalisation s = lambda zh, zh = (z - mu)/sigma:
  *   dz = (lambda/sigma) (ds - mean(ds) - zh mean(ds zh)); sigma == 0 gives 0.
  * Gate: dWg[e] += dz[e] x_t, dbg[e] += dz[e], dx_t += sum_e dz[e] Wg[e].
+ * Balancing losses (orc_router_stats' definitions), added to the loss with
+ * coefficients aux_coef and z_coef:
+ *   aux = E sum_e f_e P_e, f_e = counts_e / (T k) over all choices (constant),
+ *     P_e = (1/T) sum_t p[t,e]  =>  dp[t,e] += aux_coef E f_e / T, before
+ *     the softmax and normalisation backward;
+ *   Z-loss = (1/T) sum_t lse(z_t)^2 on the raw logits  =>
+ *     dz[t,e] += z_coef (2/T) lse(z_t) softmax(z_t)[e].
  * Outputs (double): dx [T][d], dWg [E][d], dbg [E], dW1 [E][n1][d], dW2 [E][d][F];
  * Wg == NULL means the logits were given (no gate): dWg, dbg and the gate term
  * of dx are skipped.  dz (nullable) [T][E] receives the logit gradient. */
 void orc_backward(int T, int d, int E, int k, int F, int act, int dtype, int normalize, double lambda,
-                  const void* x, const void* Wg, const void* W1, const void* W2, const float* z32,
+                  double aux_coef, double z_coef, const void* x, const void* Wg, const void* W1, const void* W2, const float* z32,
                   const int32_t* idx, const int32_t* slot, const void* dy, double* dx, double* dWg, double* dbg,
                   double* dW1, double* dW2, double* dz_out)
 {
@@ -678,6 +685,14 @@ void orc_backward(int T, int d, int E, int k, int F, int act, int dtype, int nor
     double* p = (double*)malloc(sizeof(double) * (size_t)E);
     double* dp = (double*)malloc(sizeof(double) * (size_t)E);
     double* dzt = (double*)malloc(sizeof(double) * (size_t)E);
+    double* aux_dp = (double*)malloc(sizeof(double) * (size_t)E);  /* aux_coef E f_e / T */
+    for (int e = 0; e < E; ++e)
+        aux_dp[e] = 0.0;
+    for (size_t a = 0; a < (size_t)T * k; ++a)
+        if (idx[a] >= 0 && idx[a] < E)
+            aux_dp[idx[a]] += 1.0;
+    for (int e = 0; e < E; ++e)
+        aux_dp[e] = aux_coef * (double)E * (aux_dp[e] / ((double)T * k)) / (double)T;
     for (int t = 0; t < T; ++t) {
         double* dxt = dx + (size_t)t * d;
         for (int i = 0; i < d; ++i) {
@@ -687,7 +702,7 @@ void orc_backward(int T, int d, int E, int k, int F, int act, int dtype, int nor
         }
         orc_gate_probs(E, z32 + (size_t)t * E, normalize, lambda, p);
         for (int e = 0; e < E; ++e)
-            dp[e] = 0.0;
+            dp[e] = aux_dp[e];
         for (int j = 0; j < k; ++j) {
             const size_t a = (size_t)t * k + j;
             if (slot[a] < 0)
@@ -779,6 +794,18 @@ void orc_backward(int T, int d, int E, int k, int F, int act, int dtype, int nor
                 }
             }
         }
+        if (z_coef != 0.0) {  /* Z-loss on the raw logits */
+            const float* zt = z32 + (size_t)t * E;
+            double m = -INFINITY;
+            for (int e = 0; e < E; ++e)
+                m = fmax(m, (double)zt[e]);
+            double sum = 0.0;
+            for (int e = 0; e < E; ++e)
+                sum += exp((double)zt[e] - m);
+            const double lse = m + log(sum);
+            for (int e = 0; e < E; ++e)
+                dzt[e] += z_coef * 2.0 / (double)T * lse * exp((double)zt[e] - m) / sum;
+        }
         if (dz_out)
             for (int e = 0; e < E; ++e)
                 dz_out[(size_t)t * E + e] = dzt[e];
@@ -792,5 +819,5 @@ void orc_backward(int T, int d, int E, int k, int F, int act, int dtype, int nor
             }
         }
     }
-    free(xt); free(dyt); free(u); free(h); free(o); free(dh); free(du); free(p); free(dp); free(dzt);
+    free(xt); free(dyt); free(u); free(h); free(o); free(dh); free(du); free(p); free(dp); free(dzt); free(aux_dp);
 }

@@ -809,3 +809,48 @@ def test_backward_degenerate_cases():
     # a dz row sums to zero: softmax (and the standardisation) are shift invariant
     g = oracle.backward(x, Wg, W1, W2, z32, idx, slot, dy, oracle.RELU, F, True, 2.0)
     assert np.allclose(g["dz"].sum(axis=1), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("normalize,with_dy", [(False, True), (True, True), (True, False)])
+def test_backward_balancing_losses_central_differences(normalize, with_dy):
+    """The aux and Z-loss terms of orc_backward against central differences of
+    sum(y dy) + a aux + b z_loss, the losses from router_stats (pinned on their
+    own above); with dy = 0 the losses alone."""
+    T, d, E, k, F = 7, 64, 4, 2, 64
+    act = oracle.SWIGLU
+    a_coef, b_coef, lam = 0.37, 0.21, 0.8
+    x = RNG.standard_normal((T, d)).astype(np.float32)
+    Wg = (RNG.standard_normal((E, d)) * 0.3).astype(np.float32)
+    bg = (np.arange(E) * 0.5).astype(np.float32)
+    W1 = (RNG.standard_normal((E, 2 * F, d)) * 0.1).astype(np.float32)
+    W2 = (RNG.standard_normal((E, d, F)) * 0.1).astype(np.float32)
+    dy = RNG.standard_normal((T, d)).astype(np.float32) if with_dy else np.zeros((T, d), np.float32)
+
+    def loss(x, Wg, bg, W1, W2):
+        out = oracle.moe_forward(x, Wg, bg, W1, W2, k=k, F=F, act=act, normalize_flag=normalize, lam=lam)
+        st = oracle.router_stats(out["z32"], out["counts"], out["P"], k, normalize, lam)
+        return float((out["y"] * dy.astype(np.float64)).sum() + a_coef * st["aux"] + b_coef * st["z_loss"]), out
+
+    _l0, out0 = loss(x, Wg, bg, W1, W2)
+    g = oracle.backward(x, Wg, W1, W2, out0["z32"], out0["topk_idx"], out0["slot"], dy, act, F, normalize, lam,
+                        aux_coef=a_coef, z_coef=b_coef)
+    checks = [("x", (2, 5), "dx"), ("x", (6, 40), "dx"), ("Wg", (1, 10), "dWg"), ("Wg", (3, 63), "dWg"),
+              ("bg", (0,), "dbg"), ("bg", (2,), "dbg")]
+    params = {"x": x, "Wg": Wg, "bg": bg, "W1": W1, "W2": W2}
+    for pname, at, gname in checks:
+        base = params[pname]
+        h = np.float32(2.0 ** -9) * max(1.0, abs(float(base[at])))
+        vals = []
+        for sgn in (1, -1):
+            q = {n: v.copy() for n, v in params.items()}
+            q[pname][at] = base[at] + sgn * h
+            l, out = loss(**q)
+            assert np.array_equal(out["topk_idx"], out0["topk_idx"])  # routing unchanged by the step
+            vals.append(l)
+        step = float(np.float32(base[at] + h)) - float(np.float32(base[at] - h))
+        fd = (vals[0] - vals[1]) / step
+        an = g[gname][at]
+        assert abs(fd - an) <= 2e-3 * max(1e-2, abs(an)), (pname, at, fd, an)
+    # the terms are really there: without them the gate gradient differs
+    g0 = oracle.backward(x, Wg, W1, W2, out0["z32"], out0["topk_idx"], out0["slot"], dy, act, F, normalize, lam)
+    assert np.max(np.abs(g["dWg"] - g0["dWg"])) > 1e-3 * np.max(np.abs(g["dWg"]))
