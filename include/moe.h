@@ -268,8 +268,24 @@ moe_status moe_forward_train(const moe_problem* p, const void* x, const void* Wg
  * 32-bit offsets. */
 moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes);
 
+/* Balancing losses added to the training loss (their values are
+ * moe_router_stats' aux and Z-loss; the auxiliary loss keeps experts
+ * balanced: Megatron-Core page, "MoE负载均衡的挑战与应对" and "关键特性";
+ * Skywork news, 技术创新 2, with a coefficient that follows the drop rate).
+ * moe_backward adds their gradients:
+ *   aux_coef * aux, aux = E sum_e f_e P_e (f_e = counts_e / (T k), constant):
+ *     dp[t,e] += aux_coef E f_e / T before the softmax backward;
+ *   z_coef * Z-loss, Z-loss = (1/T) sum_t lse(z_t)^2 on the raw logits:
+ *     dz[t,e] += z_coef (2/T) lse(z_t) softmax(z_t)[e]. */
+typedef struct {
+    float aux_coef;
+    float z_coef;
+} moe_router_losses;
+
 /* Gradients given dy = dL/dy [T][d] (dtype) and the forward's logits, info and
- * saved tensors (from moe_forward_train on the same inputs):
+ * saved tensors (from moe_forward_train on the same inputs), and optionally
+ * the balancing losses (losses == NULL: none; info->counts is read when
+ * aux_coef != 0):
  *   dx [T][d] dtype; dW1 [E][n1][d], dW2 [E][d][F] fp32;
  *   dWg [E][d], dbg [E] fp32 (required when Wg != NULL; Wg == NULL means the
  *   logits were given and there is no gate gradient).
@@ -283,8 +299,8 @@ moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes);
  * every run).  Needs ws_bytes >= moe_backward_workspace_size. */
 moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, const void* Wg, const void* W1,
                         const void* W2, const float* logits, const moe_route_info* info, const moe_saved* saved,
-                        void* dx, float* dWg, float* dbg, float* dW1, float* dW2, void* ws, size_t ws_bytes,
-                        void* stream);
+                        const moe_router_losses* losses, void* dx, float* dWg, float* dbg, float* dW1, float* dW2,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- FP8 experts
  * Expert weights as OCP FP8 E4M3 codes (Skywork-MoE model card: an FP8

@@ -48,6 +48,10 @@ class RouteInfo(ctypes.Structure):
                 ("offsets", ctypes.c_void_p), ("slot", ctypes.c_void_p), ("src_token", ctypes.c_void_p)]
 
 
+class RouterLosses(ctypes.Structure):
+    _fields_ = [("aux_coef", ctypes.c_float), ("z_coef", ctypes.c_float)]
+
+
 class Saved(ctypes.Structure):
     _fields_ = [("u", ctypes.c_void_p), ("h", ctypes.c_void_p), ("y_perm", ctypes.c_void_p)]
 
@@ -92,8 +96,8 @@ def load() -> ctypes.CDLL:
     lib.moe_forward_train.argtypes = [PP, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), ctypes.POINTER(Saved), P,
                                       ctypes.c_size_t, P]
     lib.moe_backward_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
-    lib.moe_backward.argtypes = [PP, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), ctypes.POINTER(Saved), P, P, P,
-                                 P, P, P, ctypes.c_size_t, P]
+    lib.moe_backward.argtypes = [PP, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), ctypes.POINTER(Saved),
+                                 ctypes.POINTER(RouterLosses), P, P, P, P, P, P, ctypes.c_size_t, P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = st
     _lib = lib
@@ -276,10 +280,15 @@ def moe_backward_workspace_size(p) -> int:
     return n.value
 
 
-def moe_backward(p, dy, x, Wg, W1, W2, logits, info, saved, dx, dWg, dbg, dW1, dW2, ws=None, stream=None):
+def moe_backward(p, dy, x, Wg, W1, W2, logits, info, saved, dx, dWg, dbg, dW1, dW2, ws=None, stream=None,
+                 aux_coef=0.0, z_coef=0.0):
+    """aux_coef, z_coef: coefficients of the balancing losses (auxiliary
+    loss, Z-loss) whose gradients are added; both 0 passes no losses."""
     ri = _route_info(info) if info is not None else None
     sv = _saved(saved) if saved is not None else None
+    ls = RouterLosses(float(aux_coef), float(z_coef)) if (aux_coef or z_coef) else None
     _check(load().moe_backward(ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(Wg), _ptr(W1), _ptr(W2), _ptr(logits),
                                ctypes.byref(ri) if ri is not None else None,
-                               ctypes.byref(sv) if sv is not None else None, _ptr(dx), _ptr(dWg), _ptr(dbg),
+                               ctypes.byref(sv) if sv is not None else None,
+                               ctypes.byref(ls) if ls is not None else None, _ptr(dx), _ptr(dWg), _ptr(dbg),
                                _ptr(dW1), _ptr(dW2), _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -32,7 +32,8 @@ hipError_t moe_launch_combine_bwd(int dtype, const void* dy, const void* y_perm,
                                   const float* topk_w, int T, int d, int k, int max_rows, void* d_yp, float* d_w,
                                   hipStream_t stream);
 hipError_t moe_launch_router_bwd(const float* logits, const int32_t* topk_idx, const int32_t* slot, const float* d_w,
-                                 int T, int E, int k, int normalize, float lambda, float* dz, hipStream_t stream);
+                                 int T, int E, int k, int normalize, float lambda, float aux_coef, float z_coef,
+                                 const int32_t* counts, float* dz, hipStream_t stream);
 hipError_t moe_launch_kofs(const int32_t* offsets, int E, int max_rows, int align, int32_t* kofs, hipStream_t stream);
 hipError_t moe_launch_transpose(int dtype, const void* src, int B, int R, int C, void* dst, hipStream_t stream);
 hipError_t moe_launch_seg_transpose(int dtype, const void* src, const int32_t* gather, int gather_rows,
@@ -917,8 +918,8 @@ moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes)
 
 moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, const void* Wg, const void* W1,
                         const void* W2, const float* logits, const moe_route_info* info, const moe_saved* saved,
-                        void* dx, float* dWg, float* dbg, float* dW1, float* dW2, void* ws, size_t ws_bytes,
-                        void* stream)
+                        const moe_router_losses* losses, void* dx, float* dWg, float* dbg, float* dW1, float* dW2,
+                        void* ws, size_t ws_bytes, void* stream)
 {
     CHECK(check_bwd(p));
     hipStream_t s = (hipStream_t)stream;
@@ -949,6 +950,11 @@ moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, con
     CHECK(check_ptr(saved->u, "saved u", 16));
     CHECK(check_ptr(saved->h, "saved h", 16));
     CHECK(check_ptr(saved->y_perm, "saved y_perm", 16));
+    const float aux_coef = losses ? losses->aux_coef : 0.0f, z_coef = losses ? losses->z_coef : 0.0f;
+    if (!std::isfinite(aux_coef) || !std::isfinite(z_coef))
+        return fail(MOE_ERR_INVALID_ARG, "balancing-loss coefficients must be finite");
+    if (aux_coef != 0.0f)
+        CHECK(check_ptr(info->counts, "info counts", 4));
     CHECK(check_ptr(dx, "dx", 16));
     CHECK(check_ptr(dW1, "dW1", 16));
     CHECK(check_ptr(dW2, "dW2", 16));
@@ -976,7 +982,8 @@ moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, con
     CHECK(hip_status(moe_launch_combine_bwd(dt, dy, saved->y_perm, info->slot, info->topk_w, T, d, k, rows, d_yp, d_w,
                                             s), "combine backward launch"));
     CHECK(hip_status(moe_launch_router_bwd(logits, info->topk_idx, info->slot, d_w, T, E, k, p->normalize, p->lambda,
-                                           dz, s), "router backward launch"));
+                                           aux_coef, z_coef, info->counts, dz, s),
+                     "router backward launch"));
     // input gradients of the expert layers: dh = d_yp W2[e] (+ activation backward), dx_perm = du W1[e]
     const int depi = p->act == MOE_ACT_SWIGLU ? 4 : 3;
     if (p->dtype == MOE_BF16) {

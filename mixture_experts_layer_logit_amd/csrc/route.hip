@@ -273,6 +273,11 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
 // ds = p (dp - <p, dp>) through the softmax, and with the normalisation
 // s = lambda zh, zh = (z - mu) / sigma:
 //   dz = (lambda / sigma) (ds - mean(ds) - zh mean(ds zh)),  0 when sigma == 0.
+// Balancing losses (the router statistics' definitions) with coefficients
+// aux_coef and z_coef: aux = E sum_e f_e P_e with f_e = counts_e / (T k)
+// constant adds aux_coef E f_e / T to dp before the softmax backward; the
+// Z-loss (1/T) sum_t lse(z_t)^2 on the raw logits adds
+// z_coef (2/T) lse(z_t) softmax(z_t) to dz.
 // fp64 throughout (the router's arithmetic), stored fp32.  One wavefront per
 // token.
 template <int VPL>
@@ -280,7 +285,9 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
                                                              const int32_t* __restrict__ topk_idx,
                                                              const int32_t* __restrict__ slot,
                                                              const float* __restrict__ d_w, int T, int E, int k,
-                                                             int normalize, float lambda, float* __restrict__ dz)
+                                                             int normalize, float lambda, float aux_coef,
+                                                             float z_coef, const int32_t* __restrict__ counts,
+                                                             float* __restrict__ dz)
 {
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -296,10 +303,12 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
     double ex[VPL], denom;
     token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
     double p[VPL], dp[VPL];
+    const double aux_scale = (double)aux_coef * (double)E / ((double)T * (double)k) / (double)T;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
         p[i] = ex[i] / denom;
-        dp[i] = 0.0;
+        dp[i] = (aux_coef != 0.0f && e < E) ? aux_scale * (double)counts[e] : 0.0;
     }
     for (int j = 0; j < k; ++j) {
         const size_t a = (size_t)t * k + j;
@@ -351,6 +360,25 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
             for (int i = 0; i < VPL; ++i)
                 ds[i] = (double)lambda / sigma * (ds[i] - m1 - zh[i] * m2);
         }
+    }
+    if (z_coef != 0.0f) {  // Z-loss on the raw logits
+        double m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (lane + kWave * i < E)
+                m = fmax(m, (double)z[i]);
+        m = wave_max(m);
+        double q[VPL], part = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            q[i] = (lane + kWave * i < E) ? exp((double)z[i] - m) : 0.0;
+            part += q[i];
+        }
+        const double sum = wave_sum(part);
+        const double c = (double)z_coef * 2.0 / (double)T * (m + log(sum)) / sum;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            ds[i] += c * q[i];
     }
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -577,21 +605,25 @@ extern "C" hipError_t moe_launch_router_stats(const float* logits, int T, int E,
 
 extern "C" hipError_t moe_launch_router_bwd(const float* logits, const int32_t* topk_idx, const int32_t* slot,
                                             const float* d_w, int T, int E, int k, int normalize, float lambda,
-                                            float* dz, hipStream_t stream)
+                                            float aux_coef, float z_coef, const int32_t* counts, float* dz,
+                                            hipStream_t stream)
 {
     using namespace moe;
     const dim3 grid((T + 3) / 4), block(256);
     const int vpl = (E + kWave - 1) / kWave;
+    auto go = [&](auto v) {
+        moe_router_bwd_kernel<decltype(v)::value><<<grid, block, 0, stream>>>(
+            logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, aux_coef, z_coef, counts, dz);
+    };
     if (vpl <= 1)
-        moe_router_bwd_kernel<1><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+        go(std::integral_constant<int, 1>{});
     else if (vpl <= 2)
-        moe_router_bwd_kernel<2><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+        go(std::integral_constant<int, 2>{});
     else if (vpl <= 4)
-        moe_router_bwd_kernel<4><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+        go(std::integral_constant<int, 4>{});
     else if (vpl <= 8)
-        moe_router_bwd_kernel<8><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda, dz);
+        go(std::integral_constant<int, 8>{});
     else
-        moe_router_bwd_kernel<16><<<grid, block, 0, stream>>>(logits, topk_idx, slot, d_w, T, E, k, normalize, lambda,
-                                                              dz);
+        go(std::integral_constant<int, 16>{});
     return hipGetLastError();
 }

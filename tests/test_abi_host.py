@@ -265,7 +265,8 @@ def test_backward_entry_points_reject_bad_arguments():
     bad_saved = moe.Saved(FAKE, FAKE + 2, FAKE)
     assert lib.moe_forward_train(pp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, ri, ctypes.byref(bad_saved), FAKE,
                                  ws, None) == moe.MOE_ERR_INVALID_ARG
-    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ri, sv, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bws, None]
+    # dy, x, Wg, W1, W2, logits, info, saved, losses, dx, dWg, dbg, dW1, dW2, ws, ws_bytes, stream
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ri, sv, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bws, None]
     # short workspace; no route info; a gate without its gradient outputs; null dW2
     a = list(args)
     a[-2] = bws - 1
@@ -274,15 +275,26 @@ def test_backward_entry_points_reject_bad_arguments():
     a[6] = None
     assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
     a = list(args)
-    a[9] = None
+    a[10] = None
     assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
     a = list(args)
-    a[12] = None
+    a[13] = None
     assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
+    # balancing losses: non-finite coefficients; the auxiliary loss needs the counts
+    for bad in (moe.RouterLosses(float("nan"), 0.0), moe.RouterLosses(0.0, float("inf"))):
+        a = list(args)
+        a[8] = ctypes.byref(bad)
+        assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
+    no_counts = moe.RouteInfo(FAKE, FAKE, None, FAKE, FAKE, FAKE)
+    aux = moe.RouterLosses(0.01, 0.0)
+    a = list(args)
+    a[6], a[8] = ctypes.byref(no_counts), ctypes.byref(aux)
+    assert lib.moe_backward(pp, *a) == moe.MOE_ERR_INVALID_ARG
+    assert b"counts" in lib.moe_last_error()
     # T == 0: the training forward is a no-op; the backward still needs its weight-gradient outputs
     p0 = moe.problem(0, 64, 8, 2, 64)
     p0p = ctypes.byref(p0)
     assert lib.moe_forward_train(p0p, None, None, None, None, None, None, None, None, None, None, 0, None) == \
         moe.MOE_OK
     assert lib.moe_backward(p0p, None, None, None, None, None, None, None, None, None, None, None, None, None, None,
-                            0, None) == moe.MOE_ERR_INVALID_ARG
+                            None, 0, None) == moe.MOE_ERR_INVALID_ARG

@@ -37,8 +37,9 @@ def act_code(case):
     return oracle.SWIGLU if case.act == "swiglu" else oracle.RELU
 
 
-def run_train(case, inp, dy, ws_fill=None):
-    """moe_forward_train then moe_backward; host copies of every output."""
+def run_train(case, inp, dy, ws_fill=None, aux_coef=0.0, z_coef=0.0):
+    """moe_forward_train then moe_backward (with the balancing losses' gradients
+    when the coefficients are nonzero); host copies of every output."""
     p = problem_of(case)
     T, E, k, d, F = case.T, case.E, case.k, case.d, case.F
     n1 = case.n1
@@ -75,7 +76,8 @@ def run_train(case, inp, dy, ws_fill=None):
     dW2 = torch.full((E, d, F), 7.0, dtype=torch.float32, device="cuda")
     dWg = torch.full((E, d), 7.0, dtype=torch.float32, device="cuda") if Wg is not None else None
     dbg = torch.full((E,), 7.0, dtype=torch.float32, device="cuda") if Wg is not None else None
-    moe.moe_backward(p, dev(dy), x, Wg, W1, W2, logits, info, saved, dx, dWg, dbg, dW1, dW2, bws)
+    moe.moe_backward(p, dev(dy), x, Wg, W1, W2, logits, info, saved, dx, dWg, dbg, dW1, dW2, bws,
+                     aux_coef=aux_coef, z_coef=z_coef)
     torch.cuda.synchronize()
     out = {key: host(v) for key, v in info.items()}
     out.update(y=host(y), logits=host(logits), dx=host(dx), dW1=host(dW1), dW2=host(dW2))
@@ -114,7 +116,7 @@ def within(got, ref, tol, extra_rows=None):
     return worst
 
 
-def check_backward(case, inp, out, dy, tokens=None):
+def check_backward(case, inp, out, dy, tokens=None, aux_coef=0.0, z_coef=0.0):
     z32, idx, w, disp = oracle_route(case, inp)
     assert np.array_equal(out["topk_idx"], idx)
     assert np.array_equal(out["slot"], disp["slot"])
@@ -127,8 +129,9 @@ def check_backward(case, inp, out, dy, tokens=None):
     errs = {"y": maxrel(out["y"][S], y_ref)}
     assert errs["y"] <= tol, errs
     x_s = inp["x"][S]
+    assert tokens is None or not (aux_coef or z_coef), "the balancing losses reach every token"
     ref = oracle.backward(x_s, inp.get("Wg"), inp["W1"], inp["W2"], z32[S], idx[S], disp["slot"][S], dy[S],
-                          act_code(case), case.F, case.normalize, case.lam)
+                          act_code(case), case.F, case.normalize, case.lam, aux_coef=aux_coef, z_coef=z_coef)
     # ReLU decisions the two sides may take differently, and the most they can
     # change: dh_f <= sum_i |W2[e,i,f] dy_t,i| (gate weight <= 1) moves
     # dW1[e,f,:] by dh_f |x_t| and dx_t by dh_f |W1[e,f,:]|
@@ -246,3 +249,23 @@ def test_backward_edges(kind):
     if kind == "constant_norm":  # sigma == 0: no gradient reaches the logits
         assert np.all(out["dWg"] == 0.0) and np.all(out["dbg"] == 0.0)
     print("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("name,dy_zero", [("mixtral_s", False), ("skywork_m_zipf_s", False),
+                                          ("skywork_m_zipf_s", True)])
+def test_backward_balancing_losses(name, dy_zero):
+    """The auxiliary loss and Z-loss gradients (coefficients 0.3 and 0.05); with
+    dy = 0 they are the only source, so the expert weight gradients are 0."""
+    case = moe_inputs.get(name)
+    print(f"[backward-losses] {name} dy_zero={dy_zero}", flush=True)
+    inp = moe_inputs.make(case)
+    dy = moe_inputs.make_dy(case)
+    if dy_zero:
+        dy = np.zeros_like(dy)
+    out = run_train(case, inp, dy, aux_coef=0.3, z_coef=0.05)
+    errs = check_backward(case, inp, out, dy, aux_coef=0.3, z_coef=0.05)
+    if dy_zero:
+        assert np.all(out["dW1"] == 0.0) and np.all(out["dW2"] == 0.0)
+        assert np.any(out["dWg"] != 0.0)
+    print("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+
