@@ -247,7 +247,10 @@ moe_status moe_combine_shared(const moe_problem* p, const void* y_perm, const in
  * layers, the softmax, the normalisation and the gate; the top-k choice and
  * the capacity drops pass no gradient (a dropped choice does not touch y).
  * moe_forward_train is moe_forward keeping what the backward needs: logits,
- * every info field, and the saved tensors below ([T*k] rows each, dtype). */
+ * every info field, and the saved tensors below ([T*k] rows each, dtype).
+ * A shared expert (moe_shared_expert) trains through the same two calls as a
+ * layer with E = 1, k = 1 and given logits: the softmax of a single logit is
+ * exactly 1, so that layer's output is the shared expert's. */
 typedef struct {
     void* u;      /* [T*k][n1] pre-activation x W1[e]^T (gate then up columns for SwiGLU) */
     void* h;      /* [T*k][F] activation output */

@@ -207,7 +207,7 @@ def test_backward_deterministic_and_workspace_independent(name):
 
 
 @pytest.mark.parametrize("kind", ["T0", "T1", "E_equals_k", "k1_norm", "single_expert", "heavy_drop", "all_to_one",
-                                  "constant_norm", "fp32_swiglu_norm", "fp32_relu_given"])
+                                  "constant_norm", "fp32_swiglu_norm", "fp32_relu_given", "shared_expert_e1"])
 def test_backward_edges(kind):
     print(f"[backward-edge] {kind}", flush=True)
     base = moe_inputs.get("mixtral_s").with_(bias="none")
@@ -229,6 +229,10 @@ def test_backward_edges(kind):
         case = base.with_(name="bedge_const", normalize=True, T=64)
     elif kind == "fp32_swiglu_norm":
         case = base.with_(name="bedge_f32", dtype="f32", x_std=0.5, normalize=True, lam=2.0, cf=1.0, T=300)
+    elif kind == "shared_expert_e1":
+        # a shared expert is the layer with one expert, top-1 and given logits
+        # (the softmax of a single logit is exactly 1): its training step
+        case = base.with_(name="bedge_shared", E=1, k=1, logits="given")
     else:
         case = moe_inputs.get("tiny_fp32").with_(name="bedge_f32_given", logits="given", E=6, k=3, T=200, cf=1.0)
     inp = moe_inputs.make(case)
@@ -246,6 +250,9 @@ def test_backward_edges(kind):
         assert np.all(out["dWg"] == 0.0) and np.all(out["dbg"] == 0.0)
         return
     errs = check_backward(case, inp, out, dy)
+    if kind == "shared_expert_e1":  # the same output as the oracle's shared expert
+        ys = oracle.shared_expert(inp["x"], inp["W1"][0], inp["W2"][0], act_code(case), case.F)
+        assert maxrel(out["y"], ys) <= TOL[case.dtype]
     if kind == "constant_norm":  # sigma == 0: no gradient reaches the logits
         assert np.all(out["dWg"] == 0.0) and np.all(out["dbg"] == 0.0)
     print("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
