@@ -194,6 +194,7 @@ def main():
                      "kernel": "moe_expert_up: moe_grouped_gemm_kernel (up-projection + activation) and its K-split reduction"},
     }
     result.update(lay.summary(res, ms_per_step))
+    result["graph_replay"] = lay.time_graph(args.steps)
 
     # rows beyond the layer step: router statistics, shared expert
     if not args.no_next_rows:
@@ -221,6 +222,7 @@ def main():
             msps = r["elapsed"] * 1e3 / steps
             o = {"workload": workload_name(c), "tokens_per_s": c.T * steps / r["elapsed"], "ms_per_step": msps}
             o.update(lo.summary(r, msps))
+            o["graph_replay"] = lo.time_graph(steps)
             others[name] = o
             del lo, w, ri
             torch.cuda.empty_cache()
@@ -317,6 +319,32 @@ class Layer:
         stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
                     for i, n in enumerate(self.NAMES)}
         return {"stage_ms": stage_ms, "elapsed": elapsed, "P": int(self.offsets[-1].item())}
+
+    def time_graph(self, steps):
+        """The same step captured once in a HIP graph (every entry point only
+        launches kernels on the given stream) and replayed: the step without
+        the host's per-launch cost."""
+        import numpy as np
+        import torch
+        self.step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            self.step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        with torch.cuda.stream(self.stream):
+            ev[0].record(self.stream)
+            for i in range(steps):
+                g.replay()
+                ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+        del g
+        return {"ms_per_step": ms, "tokens_per_s": self.case.T / (ms * 1e-3)}
 
     def up_flops(self, P):
         return 2.0 * P * self.case.d * self.n1
