@@ -18,7 +18,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB names another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1

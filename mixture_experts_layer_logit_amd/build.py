@@ -57,5 +57,39 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str) -> str:
+    """A copy of libmoe.so whose host code (api.cpp: argument checks,
+    workspace layouts, launch set-up) carries AddressSanitizer and
+    UndefinedBehaviorSanitizer checks; device code is not instrumented.  The
+    kernels' objects come from the last build().  Load it with clang's ASan
+    runtime preloaded (LD_PRELOAD) and MOE_LIB=<out>."""
+    objs = [os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "api.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError(f"run build() first: {missing}")
+    # each sanitizer flag applies to the host compilation only
+    san = []
+    for check in ("address", "undefined"):
+        san += ["-Xarch_host", "-fsanitize=" + check]
+    san += ["-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_obj = out + ".api.o"
+    flags = [f for f in COMMON if f != "-O3"] + ["-O1", "-g"]
+    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj] + flags + san
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on api.cpp (sanitized):\n{r.stdout}\n{r.stderr}")
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libsan"] + san + ["-o", out] + objs + [api_obj]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.remove(api_obj)
+    return out
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime that build_host_sanitized() links against."""
+    r = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang++"),
+                        "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
     build()

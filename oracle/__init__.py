@@ -35,6 +35,9 @@ SWIGLU = 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A sanitizer build of the same source may be loaded instead (host-code
+# checks run the pins against it in a child process).
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
 _lib = None
 
 
@@ -49,13 +52,27 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(out: str) -> str:
+    """The same source with AddressSanitizer and UndefinedBehaviorSanitizer
+    checks (gcc), for host-code checks of the oracle: load it in a child
+    process with gcc's libasan and libubsan preloaded and MOE_ORACLE_LIB=<out>."""
+    cmd = ["gcc", "-O1", "-g", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-o", out, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     I = ctypes.c_int
     D = ctypes.c_double
