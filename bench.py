@@ -131,6 +131,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mode", default="layer", choices=["layer", "copy", "train"])
     args = ap.parse_args()
@@ -194,7 +195,8 @@ def main():
                      "kernel": "moe_expert_up: moe_grouped_gemm_kernel (up-projection + activation) and its K-split reduction"},
     }
     result.update(lay.summary(res, ms_per_step))
-    result["graph_replay"] = lay.time_graph(args.steps)
+    if not args.no_graph:
+        result["graph_replay"] = lay.time_graph(args.steps)
 
     # rows beyond the layer step: router statistics, shared expert
     if not args.no_next_rows:
@@ -222,7 +224,8 @@ def main():
             msps = r["elapsed"] * 1e3 / steps
             o = {"workload": workload_name(c), "tokens_per_s": c.T * steps / r["elapsed"], "ms_per_step": msps}
             o.update(lo.summary(r, msps))
-            o["graph_replay"] = lo.time_graph(steps)
+            if not args.no_graph:
+                o["graph_replay"] = lo.time_graph(steps)
             others[name] = o
             del lo, w, ri
             torch.cuda.empty_cache()
