@@ -86,3 +86,72 @@ def run_forward(case, inp, ws_fill=None):
     out["y"] = host(y)
     out["logits"] = host(logits)
     return out
+
+
+def run_train(case, inp, dy, ws_fill=None, aux_coef=0.0, z_coef=0.0):
+    """moe_forward_train then moe_backward (with the balancing losses' gradients
+    when the coefficients are nonzero); host copies of every output."""
+    p = problem_of(case)
+    T, E, k, d, F = case.T, case.E, case.k, case.d, case.F
+    n1 = case.n1
+    tdt = torch_dtype(case)
+    x = dev(inp["x"])
+    W1 = dev(inp["W1"])
+    W2 = dev(inp["W2"])
+    Wg = dev(inp["Wg"]) if inp.get("Wg") is not None else None
+    bg = dev(inp["bg"]) if inp.get("bg") is not None else None
+    if Wg is None:
+        logits = dev(inp["logits"])
+    else:
+        logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    y = torch.empty(T, d, dtype=tdt, device="cuda")
+    info = {
+        "topk_idx": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+        "topk_w": torch.empty(T, k, dtype=torch.float32, device="cuda"),
+        "counts": torch.empty(E, dtype=torch.int32, device="cuda"),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+        "slot": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+        "src_token": torch.full((T * k,), -7, dtype=torch.int32, device="cuda"),
+    }
+    saved = {"u": torch.empty(T * k, n1, dtype=tdt, device="cuda"),
+             "h": torch.empty(T * k, F, dtype=tdt, device="cuda"),
+             "y_perm": torch.empty(T * k, d, dtype=tdt, device="cuda")}
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    moe.moe_forward_train(p, x, Wg, bg, W1, W2, y, logits, info, saved, ws)
+    del ws
+    bws = torch.empty(moe.moe_backward_workspace_size(p), dtype=torch.uint8, device="cuda")
+    if ws_fill is not None:
+        bws.fill_(ws_fill)
+    dx = torch.empty(T, d, dtype=tdt, device="cuda")
+    dW1 = torch.full((E, n1, d), 7.0, dtype=torch.float32, device="cuda")
+    dW2 = torch.full((E, d, F), 7.0, dtype=torch.float32, device="cuda")
+    dWg = torch.full((E, d), 7.0, dtype=torch.float32, device="cuda") if Wg is not None else None
+    dbg = torch.full((E,), 7.0, dtype=torch.float32, device="cuda") if Wg is not None else None
+    moe.moe_backward(p, dev(dy), x, Wg, W1, W2, logits, info, saved, dx, dWg, dbg, dW1, dW2, bws,
+                     aux_coef=aux_coef, z_coef=z_coef)
+    torch.cuda.synchronize()
+    out = {key: host(v) for key, v in info.items()}
+    out.update(y=host(y), logits=host(logits), dx=host(dx), dW1=host(dW1), dW2=host(dW2))
+    if Wg is not None:
+        out.update(dWg=host(dWg), dbg=host(dbg))
+    return out
+
+
+def within(got, ref, tol, extra_rows=None):
+    """|got - ref| <= tol max|ref| everywhere, plus extra_rows[key] (a vector
+    over the last axis) on the rows named by extra_rows' keys; returns the
+    max-abs-rel error over the rows without extra allowance."""
+    got = np.asarray(got)
+    g = to_f64(got) if got.dtype in (np.uint16, np.float32) else got.astype(np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    scale = scale if scale > 0 else 1.0
+    err = np.abs(g - ref)
+    del g
+    for key, extra in (extra_rows or {}).items():
+        over = err[key] - (tol * scale + extra)
+        assert np.all(over <= 0), f"row {key}: {float(over.max()):.3e} beyond the bound"
+        err[key] = 0.0
+    worst = float(err.max() / scale) if err.size else 0.0
+    assert worst <= tol, f"max-abs-rel {worst:.3e} > {tol}"
+    return worst
