@@ -483,6 +483,213 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
     }
 }
 
+// Activation-backward epilogue through LDS (bf16 outputs).  The direct
+// epilogue reads u and writes du 8 bytes per lane with the 32 lanes of a
+// wave half on 32 different rows, so every wave instruction touches 32
+// cache lines.  Here each row fragment i of every wave (kRowsPass rows) is
+// first staged as fp32 dh [row][column] in a stage buffer (16-byte chunks
+// XOR-swizzled by row, as in the plain epilogue below), then processed in
+// the row domain: a thread takes 8 consecutive columns of one row (16-byte
+// loads of u and stores of du, a wave covering whole row runs).  The
+// arithmetic is that of store_tile, element by element.  The fragment's u
+// loads are issued before its staging, so their latency overlaps it.
+template <typename OT, typename S, int EPI>
+__device__ __forceinline__ void store_tile_lds_bwd(const Acc<S>& acc, typename OT::storage* __restrict__ C,
+                                                   const TileDec& t, int Nout, int ncols, int wave, EpiArgs ep, int F,
+                                                   uint8_t* buf0, uint8_t* buf1)
+{
+    static_assert(OT::kBytes == 2, "bf16 outputs");
+    static_assert(EPI == EPI_DRELU || EPI == EPI_DSWIGLU, "activation-backward epilogues");
+    typedef typename OT::storage T;
+    constexpr int kRowsPass = S::WM * 32;
+    constexpr int kRowBytes = S::BN * 4;  // fp32 staging
+    constexpr int kChunks = kRowBytes / 16;
+    constexpr int kGroups = S::BN / 8;    // 8-column groups of a row
+    constexpr int kPerThread = kRowsPass * kGroups / S::kThreads;
+    static_assert(kRowsPass * kRowBytes <= S::kStage, "one fp32 row fragment of the tile fits a stage buffer");
+    static_assert(kRowsPass * kGroups % S::kThreads == 0, "whole groups per thread");
+    constexpr bool kPair = EPI == EPI_DSWIGLU;
+    int tid = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    const int r = wm * 32 + (lane & 31);  // this lane's staging row within a pass
+    const T* U = (const T*)ep.aux_in;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < S::kFM; ++i) {
+        uint8_t* buf = (i & 1) ? buf1 : buf0;
+        uint4 ug[kPerThread], uv[kPair ? kPerThread : 1];
+#pragma unroll
+        for (int it = 0; it < kPerThread; ++it) {
+            const int c = tid + it * S::kThreads;
+            const int rr = c / kGroups, q = c % kGroups;
+            const int m = (rr / 32) * S::kWaveM + i * 32 + (rr % 32);
+            const int n = t.n0 + 8 * q;
+            ug[it] = uint4{0, 0, 0, 0};
+            if constexpr (kPair)
+                uv[it] = uint4{0, 0, 0, 0};
+            if (m < t.rows && n < ncols) {
+                const T* urow = U + (size_t)(t.row0 + m) * ep.aux_ld;
+                ug[it] = *reinterpret_cast<const uint4*>(urow + n);
+                if constexpr (kPair)
+                    uv[it] = *reinterpret_cast<const uint4*>(urow + F + n);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < S::kFN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int byte = (wn * S::kWaveN + j * 32 + 8 * g4 + 4 * (lane >> 5)) * 4;
+                *reinterpret_cast<float4*>(buf + r * kRowBytes + (((byte >> 4) ^ (r % kChunks)) << 4)) =
+                    make_float4(acc.v[i][j][4 * g4], acc.v[i][j][4 * g4 + 1], acc.v[i][j][4 * g4 + 2],
+                                acc.v[i][j][4 * g4 + 3]);
+            }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < kPerThread; ++it) {
+            const int c = tid + it * S::kThreads;
+            const int rr = c / kGroups, q = c % kGroups;
+            const int m = (rr / 32) * S::kWaveM + i * 32 + (rr % 32);
+            const int n = t.n0 + 8 * q;
+            if (m >= t.rows || n >= ncols)
+                continue;
+            const float4 d0 = *reinterpret_cast<const float4*>(buf + rr * kRowBytes + (((2 * q) ^ (rr % kChunks)) << 4));
+            const float4 d1 =
+                *reinterpret_cast<const float4*>(buf + rr * kRowBytes + (((2 * q + 1) ^ (rr % kChunks)) << 4));
+            const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            float g[8], gv[8], out[8], out2[8];
+            unpack4<OT>(uint2{ug[it].x, ug[it].y}, g);
+            unpack4<OT>(uint2{ug[it].z, ug[it].w}, g + 4);
+            if constexpr (kPair) {
+                unpack4<OT>(uint2{uv[it].x, uv[it].y}, gv);
+                unpack4<OT>(uint2{uv[it].z, uv[it].w}, gv + 4);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float u = dh[e];
+                if constexpr (kPair) {
+                    const float sg = 1.0f / (1.0f + __expf(-g[e]));
+                    out2[e] = u * g[e] * sg;
+                    u = u * gv[e] * sg * (1.0f + g[e] * (1.0f - sg));
+                } else {
+                    u = g[e] > 0.0f ? u : 0.0f;
+                }
+                out[e] = u;
+            }
+            T* crow = C + (size_t)(t.row0 + m) * Nout;
+            uint4 o;
+            o.x = f32_to_bf16_bits(out[0]) | (f32_to_bf16_bits(out[1]) << 16);
+            o.y = f32_to_bf16_bits(out[2]) | (f32_to_bf16_bits(out[3]) << 16);
+            o.z = f32_to_bf16_bits(out[4]) | (f32_to_bf16_bits(out[5]) << 16);
+            o.w = f32_to_bf16_bits(out[6]) | (f32_to_bf16_bits(out[7]) << 16);
+            *reinterpret_cast<uint4*>(crow + n) = o;
+            if constexpr (kPair) {
+                o.x = f32_to_bf16_bits(out2[0]) | (f32_to_bf16_bits(out2[1]) << 16);
+                o.y = f32_to_bf16_bits(out2[2]) | (f32_to_bf16_bits(out2[3]) << 16);
+                o.z = f32_to_bf16_bits(out2[4]) | (f32_to_bf16_bits(out2[5]) << 16);
+                o.w = f32_to_bf16_bits(out2[6]) | (f32_to_bf16_bits(out2[7]) << 16);
+                *reinterpret_cast<uint4*>(crow + F + n) = o;
+            }
+        }
+    }
+}
+
+// Forward activation epilogue through LDS (bf16, unscaled): the staging of
+// store_tile_lds_bwd, then per thread 8 consecutive output columns of one
+// row.  ReLU: h = max(u, 0) over the tile's BN columns.  SwiGLU: a wave's
+// accumulator columns are kWaveN/2 gate columns then the matching up
+// columns, so h column c of the tile (BN/2 of them) takes its gate value
+// from staged column (c / half) * kWaveN + c % half and its up value half
+// further.  aux_out (nullable): the pre-activation u is stored as well, at
+// column n (gate or ReLU) and F + n (up).
+template <typename OT, typename S, int EPI>
+__device__ __forceinline__ void store_tile_lds_fwd(const Acc<S>& acc, typename OT::storage* __restrict__ C,
+                                                   const TileDec& t, int Nout, int ncols, int wave, EpiArgs ep, int F,
+                                                   uint8_t* buf0, uint8_t* buf1)
+{
+    static_assert(OT::kBytes == 2, "bf16 outputs");
+    static_assert(EPI == EPI_RELU || EPI == EPI_SWIGLU, "forward activation epilogues");
+    typedef typename OT::storage T;
+    constexpr bool kGlu = EPI == EPI_SWIGLU;
+    constexpr int kHalf = S::kWaveN / 2;
+    constexpr int kRowsPass = S::WM * 32;
+    constexpr int kRowBytes = S::BN * 4;  // fp32 staging
+    constexpr int kChunks = kRowBytes / 16;
+    constexpr int kOutCols = kGlu ? S::BN / 2 : S::BN;
+    constexpr int kGroups = kOutCols / 8;  // 8-column groups of an output row
+    constexpr int kPerThread = kRowsPass * kGroups / S::kThreads;
+    static_assert(kRowsPass * kRowBytes <= S::kStage, "one fp32 row fragment of the tile fits a stage buffer");
+    static_assert(kRowsPass * kGroups % S::kThreads == 0, "whole groups per thread");
+    static_assert(!kGlu || kHalf % 8 == 0, "a group stays within one wave's gate columns");
+    int tid = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    const int r = wm * 32 + (lane & 31);
+    T* P = (T*)ep.aux_out;
+    auto staged = [&](uint8_t* buf, int rr, int col) {  // 4 fp32 values at staged column col (a multiple of 4)
+        return *reinterpret_cast<const float4*>(buf + rr * kRowBytes + ((((col * 4) >> 4) ^ (rr % kChunks)) << 4));
+    };
+    auto pack8 = [](const float* v) {
+        uint4 o;
+        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        o.z = f32_to_bf16_bits(v[4]) | (f32_to_bf16_bits(v[5]) << 16);
+        o.w = f32_to_bf16_bits(v[6]) | (f32_to_bf16_bits(v[7]) << 16);
+        return o;
+    };
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < S::kFM; ++i) {
+        uint8_t* buf = (i & 1) ? buf1 : buf0;
+#pragma unroll
+        for (int j = 0; j < S::kFN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int byte = (wn * S::kWaveN + j * 32 + 8 * g4 + 4 * (lane >> 5)) * 4;
+                *reinterpret_cast<float4*>(buf + r * kRowBytes + (((byte >> 4) ^ (r % kChunks)) << 4)) =
+                    make_float4(acc.v[i][j][4 * g4], acc.v[i][j][4 * g4 + 1], acc.v[i][j][4 * g4 + 2],
+                                acc.v[i][j][4 * g4 + 3]);
+            }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < kPerThread; ++it) {
+            const int c = tid + it * S::kThreads;
+            const int rr = c / kGroups, q = c % kGroups;
+            const int m = (rr / 32) * S::kWaveM + i * 32 + (rr % 32);
+            const int oc = 8 * q;  // output column within the tile
+            const int n = t.n0 + oc;
+            if (m >= t.rows || n >= ncols)
+                continue;
+            const int sc0 = kGlu ? (oc / kHalf) * S::kWaveN + oc % kHalf : oc;  // staged column of the first value
+            const float4 a0 = staged(buf, rr, sc0), a1 = staged(buf, rr, sc0 + 4);
+            const float u[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            float up[8], h[8];
+            if constexpr (kGlu) {
+                const float4 b0 = staged(buf, rr, sc0 + kHalf), b1 = staged(buf, rr, sc0 + kHalf + 4);
+                const float v[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    up[e] = v[e];
+                    h[e] = u[e] / (1.0f + __expf(-u[e])) * v[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = fmaxf(u[e], 0.0f);
+            }
+            *reinterpret_cast<uint4*>(C + (size_t)(t.row0 + m) * Nout + n) = pack8(h);
+            if (P) {
+                T* prow = P + (size_t)(t.row0 + m) * ep.aux_ld;
+                *reinterpret_cast<uint4*>(prow + n) = pack8(u);
+                if constexpr (kGlu)
+                    *reinterpret_cast<uint4*>(prow + F + n) = pack8(up);
+            }
+        }
+    }
+}
+
 // Plain epilogue (no activation, no scales) through LDS.  Direct stores
 // from the accumulators write 4 consecutive values of 32 different rows per
 // instruction, pieces HBM takes at well under half its write bandwidth; so
@@ -974,6 +1181,10 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         if (slot < 0) {
             if constexpr (EPI == EPI_NONE && ET::kBytes != 1)  // unscaled plain output
                 store_tile_lds<OT, S, KG>(acc, Cb, t, Nout, ncols, wave, lds0, lds1);
+            else if constexpr ((EPI == EPI_DRELU || EPI == EPI_DSWIGLU) && OT::kBytes == 2)
+                store_tile_lds_bwd<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, F, lds0, lds1);
+            else if constexpr ((EPI == EPI_RELU || EPI == EPI_SWIGLU) && ET::kBytes == 2 && OT::kBytes == 2)
+                store_tile_lds_fwd<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, F, lds0, lds1);
             else
                 store_tile<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, gather, Nw, F);
         } else {
