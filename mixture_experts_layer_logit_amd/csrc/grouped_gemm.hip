@@ -595,21 +595,23 @@ __device__ __forceinline__ void store_tile_lds_bwd(const Acc<S>& acc, typename O
     }
 }
 
-// Forward activation epilogue through LDS (bf16, unscaled): the staging of
+// Forward epilogue through LDS (bf16 outputs): the staging of
 // store_tile_lds_bwd, then per thread 8 consecutive output columns of one
-// row.  ReLU: h = max(u, 0) over the tile's BN columns.  SwiGLU: a wave's
-// accumulator columns are kWaveN/2 gate columns then the matching up
-// columns, so h column c of the tile (BN/2 of them) takes its gate value
-// from staged column (c / half) * kWaveN + c % half and its up value half
-// further.  aux_out (nullable): the pre-activation u is stored as well, at
-// column n (gate or ReLU) and F + n (up).
+// row.  None: the value itself; ReLU: h = max(u, 0) over the tile's BN
+// columns.  SwiGLU: a wave's accumulator columns are kWaveN/2 gate columns
+// then the matching up columns, so h column c of the tile (BN/2 of them)
+// takes its gate value from staged column (c / half) * kWaveN + c % half and
+// its up value half further.  With scales (FP8 operands) u = acc *
+// (a_scale(row) * w_scale(column)) first, as in store_tile.  aux_out
+// (nullable): the pre-activation u is stored as well, at column n (gate or
+// ReLU) and F + n (up).
 template <typename OT, typename S, int EPI>
 __device__ __forceinline__ void store_tile_lds_fwd(const Acc<S>& acc, typename OT::storage* __restrict__ C,
-                                                   const TileDec& t, int Nout, int ncols, int wave, EpiArgs ep, int F,
-                                                   uint8_t* buf0, uint8_t* buf1)
+                                                   const TileDec& t, int Nout, int ncols, int wave, EpiArgs ep,
+                                                   const int32_t* gather, int Nw, int F, uint8_t* buf0, uint8_t* buf1)
 {
     static_assert(OT::kBytes == 2, "bf16 outputs");
-    static_assert(EPI == EPI_RELU || EPI == EPI_SWIGLU, "forward activation epilogues");
+    static_assert(EPI == EPI_NONE || EPI == EPI_RELU || EPI == EPI_SWIGLU, "forward epilogues");
     typedef typename OT::storage T;
     constexpr bool kGlu = EPI == EPI_SWIGLU;
     constexpr int kHalf = S::kWaveN / 2;
@@ -664,20 +666,33 @@ __device__ __forceinline__ void store_tile_lds_fwd(const Acc<S>& acc, typename O
                 continue;
             const int sc0 = kGlu ? (oc / kHalf) * S::kWaveN + oc % kHalf : oc;  // staged column of the first value
             const float4 a0 = staged(buf, rr, sc0), a1 = staged(buf, rr, sc0 + 4);
-            const float u[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            float u[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             float up[8], h[8];
             if constexpr (kGlu) {
                 const float4 b0 = staged(buf, rr, sc0 + kHalf), b1 = staged(buf, rr, sc0 + kHalf + 4);
                 const float v[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    up[e] = v[e];
-                    h[e] = u[e] / (1.0f + __expf(-u[e])) * v[e];
-                }
-            } else {
-#pragma unroll
                 for (int e = 0; e < 8; ++e)
+                    up[e] = v[e];
+            }
+            if (ep.w) {
+                const float as = ep.a ? ep.a[gather ? gather[t.row0 + m] : t.row0 + m] : 1.0f;
+                const float* wsc = ep.w + (size_t)t.e * Nw;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    u[e] *= as * wsc[n + e];
+                    if constexpr (kGlu)
+                        up[e] *= as * wsc[F + n + e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (kGlu)
+                    h[e] = u[e] / (1.0f + __expf(-u[e])) * up[e];
+                else if constexpr (EPI == EPI_RELU)
                     h[e] = fmaxf(u[e], 0.0f);
+                else
+                    h[e] = u[e];
             }
             *reinterpret_cast<uint4*>(C + (size_t)(t.row0 + m) * Nout + n) = pack8(h);
             if (P) {
@@ -1183,8 +1198,8 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 store_tile_lds<OT, S, KG>(acc, Cb, t, Nout, ncols, wave, lds0, lds1);
             else if constexpr ((EPI == EPI_DRELU || EPI == EPI_DSWIGLU) && OT::kBytes == 2)
                 store_tile_lds_bwd<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, F, lds0, lds1);
-            else if constexpr ((EPI == EPI_RELU || EPI == EPI_SWIGLU) && ET::kBytes == 2 && OT::kBytes == 2)
-                store_tile_lds_fwd<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, F, lds0, lds1);
+            else if constexpr (EPI != EPI_DRELU && EPI != EPI_DSWIGLU && OT::kBytes == 2)  // activation or scales
+                store_tile_lds_fwd<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, gather, Nw, F, lds0, lds1);
             else
                 store_tile<OT, S, EPI>(acc, Cb, t, Nout, ncols, wave, sc, gather, Nw, F);
         } else {
