@@ -4,10 +4,11 @@
 // "4090推理": FP8-quantised inference; Megatron-Core page, "关键特性": FP8
 // among the coming features).  Every row gets the smallest power-of-two
 // scale s with max|row| <= 448 s, and each value v becomes the E4M3 code
-// nearest to v / s (ties to even, magnitudes >= 448 saturate to 448).  The
-// scale is a power of two, so v / s is exact and every code is decided
-// exactly: the rounding below is done on the exact value, in integer-exact
-// fp32 steps.
+// nearest to v / s (ties to even).  The scale is a power of two, so v / s is
+// exact and every code is decided exactly; gfx950's packed conversion
+// (v_cvt_pk_fp8_f32, OCP E4M3, round to nearest even) does the rounding, and
+// |v / s| <= 448 (the largest E4M3 value) by the choice of s, so it never
+// overflows.
 //
 // bf16 rows up to 16384 values: one block per row, read once into registers.
 // Longer rows and fp32 rows: one wavefront per row, two passes (max|v|, then
@@ -28,26 +29,15 @@ __device__ __forceinline__ int fp8_scale_exp(float amax)
     return m <= 0.875f ? x - 9 : x - 8;
 }
 
-// E4M3 code nearest to a finite v (ties to even; |v| >= 448 gives +-448).
-__device__ __forceinline__ uint32_t e4m3_encode(float v)
+// E4M3 codes of 8 values scaled by 2^-e (|f / 2^e| <= 448), little-endian
+// bytes in value order.
+__device__ __forceinline__ uint2 e4m3_encode8(const float* f, int e)
 {
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t sgn = (bits >> 24) & 0x80u;
-    const float a = fabsf(v);
-    if (a >= 448.0f)
-        return sgn | 0x7Eu;
-    if (a < 0.015625f) {  // below 2^-6: subnormal codes, step 2^-9 (a * 512 is exact)
-        return sgn | (uint32_t)rintf(a * 512.0f);
-    }
-    const uint32_t ab = __float_as_uint(a);
-    int ex = (int)((ab >> 23) & 0xffu) - 127;                       // a = m * 2^ex, m in [1, 2)
-    const float m = __uint_as_float((ab & 0x007fffffu) | 0x3f800000u);
-    float q = rintf(m * 8.0f);                                       // 8..16, exact product
-    if (q == 16.0f) {
-        q = 8.0f;
-        ex += 1;
-    }
-    return sgn | (uint32_t)((ex + 7) << 3) | ((uint32_t)q - 8u);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[0], -e), ldexpf(f[1], -e), 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[2], -e), ldexpf(f[3], -e), lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[4], -e), ldexpf(f[5], -e), 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f[6], -e), ldexpf(f[7], -e), hi, true);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
 template <typename ET>
@@ -77,11 +67,7 @@ __global__ __launch_bounds__(256) void moe_quantize_fp8_kernel(const typename ET
     for (int c = lane; c < nvec; c += kWave) {
         float f[8];
         load8(row + (size_t)c * 8, f);
-        uint32_t w[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            w[i / 4] |= e4m3_encode(ldexpf(f[i], -e)) << (8 * (i % 4));
-        *reinterpret_cast<uint2*>(out + (size_t)c * 8) = make_uint2(w[0], w[1]);
+        *reinterpret_cast<uint2*>(out + (size_t)c * 8) = e4m3_encode8(f, e);
     }
     if (lane == 0)
         scales[r] = ldexpf(1.0f, e);
@@ -130,11 +116,7 @@ __global__ __launch_bounds__(256) void moe_quantize_fp8_bf16_kernel(const uint16
         if (c < nvec) {
             float f[8];
             unpack8(buf[i], f, bf16_t{});
-            uint32_t w[2] = {0u, 0u};
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                w[q / 4] |= e4m3_encode(ldexpf(f[q], -e)) << (8 * (q % 4));
-            *reinterpret_cast<uint2*>(out + (size_t)c * 8) = make_uint2(w[0], w[1]);
+            *reinterpret_cast<uint2*>(out + (size_t)c * 8) = e4m3_encode8(f, e);
         }
     }
     if (threadIdx.x == 0)
