@@ -150,3 +150,113 @@ def test_random_shape(i):
     assert np.all(out["dW1"][~reached] == 0.0) and np.all(out["dW2"][~reached] == 0.0)
     print(f"  P={disp['P']} dropped={case.T * case.k - disp['P']} " +
           ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+
+
+# ------------------------------------------------------------------ FP8 layer
+N_FP8_CASES = 12
+
+
+def random_fp8_case(i):
+    """bf16 activations, d and F multiples of 128 (the FP8 layer's limits)."""
+    g = np.random.default_rng([7718, i])
+    E = int(g.choice([1, 2, 5, 8, 16, 33, 64]))
+    return moe_inputs.Case(
+        name=f"rand_fp8_{i}",
+        T=int(g.choice([1, 3, 64, 129, 300, 777])),
+        d=128 * int(g.integers(1, 5)),
+        E=E, k=int(g.integers(1, min(E, 8) + 1)),
+        F=128 * int(g.integers(1, 5)),
+        act=str(g.choice(["relu", "swiglu"])), dtype="bf16",
+        seed=7718 * 1000 + i,
+        normalize=bool(g.integers(0, 2)),
+        lam=float(g.choice([0.5, 1.0, 2.0])),
+        cf=float(g.choice([0.0, 0.0, 0.5, 1.0, 1.25])),
+        logits=str(g.choice(["gate", "gate", "given"])),
+        x_std=1.0, w_std=0.05, wg_std=0.05)
+
+
+def fp8_code_allowance(case, inp, W1q, w1s, W2q, w2s, w, disp):
+    """Per-token allowance [T, d] for the FP8 layer: the GPU quantises its
+    bf16 h, within 2^-9 (one bf16 rounding) plus 2^-16 (fp32 arithmetic, far
+    below it) relative of the exact h, while the oracle quantises the exact
+    h.  A code can differ only where [|v|(1 - rel), |v|(1 + rel)] (v = h /
+    2^e in the row's scale) holds a rounding midpoint of the E4M3 grid; it
+    then moves by at most the gap between the two neighbours, times the row
+    scale.  A row whose scale exponent itself is ambiguous gets twice the
+    coarser gap on every element.  The change reaches y[t] through w_j |W2|
+    (dequantised)."""
+    xq, xs = oracle.quant_rows_fp8(inp["x"])
+    src = disp["src_token"]
+    P, F, d = disp["P"], case.F, case.d
+    out = np.zeros((case.T, d))
+    if P == 0:
+        return out
+    _, h = oracle.ffn_rows_fp8(xq[src], xs[src], disp["offsets"], W1q, w1s, W2q, w2s, act_code(case), F,
+                               want_h=True)
+    grid = np.abs(oracle.e4m3_decode(np.arange(128, dtype=np.uint8)))
+    mags = np.unique(grid[np.isfinite(grid)])  # the grid, 0 .. 448 (the NaN code left out)
+    mids = (mags[1:] + mags[:-1]) / 2
+    gaps = mags[1:] - mags[:-1]
+    rel = 2.0 ** -9 + 2.0 ** -16
+    amax = np.max(np.abs(h), axis=1)
+    e = np.array([oracle.fp8_scale_exp(a) for a in amax])
+    ambiguous = np.array([oracle.fp8_scale_exp(a * (1 - rel)) != oracle.fp8_scale_exp(a * (1 + rel)) for a in amax])
+    s = 2.0 ** e
+    a = np.abs(h) / s[:, None]
+    lo = np.searchsorted(mids, a * (1 - rel), side="left")
+    hi = np.searchsorted(mids, a * (1 + rel), side="right")
+    coef = np.where(hi > lo, gaps[np.minimum(lo, gaps.size - 1)], 0.0) * s[:, None]
+    coarse = gaps[np.minimum(np.searchsorted(mids, a), gaps.size - 1)] * s[:, None] * 2
+    coef[ambiguous] = 2 * coarse[ambiguous]
+    per_row = np.zeros((P, d))
+    offs = disp["offsets"]
+    for e in range(case.E):
+        r0, r1 = offs[e], offs[e + 1]
+        if r1 > r0:
+            W2d = np.abs(oracle.e4m3_decode(W2q[e]) * np.asarray(w2s[e], np.float64)[:, None])  # [d, F]
+            per_row[r0:r1] = coef[r0:r1] @ W2d.T
+    for t in range(case.T):
+        for j in range(case.k):
+            r = disp["slot"][t, j]
+            if r >= 0:
+                out[t] += w[t, j] * per_row[r]
+    return out
+
+
+@pytest.mark.parametrize("i", range(N_FP8_CASES))
+def test_random_shape_fp8(i):
+    case = random_fp8_case(i)
+    print(f"[random-fp8] {case.name}: T={case.T} d={case.d} E={case.E} k={case.k} F={case.F} {case.act} "
+          f"norm={case.normalize} cf={case.cf} logits={case.logits}", flush=True)
+    inp = moe_inputs.make(case)
+    W1q, w1s = oracle.quant_weights_fp8(inp["W1"])
+    W2q, w2s = oracle.quant_weights_fp8(inp["W2"])
+    p = problem_of(case)
+    T, E, k, d = case.T, case.E, case.k, case.d
+    gate = case.logits == "gate"
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda") if gate else dev(inp["logits"])
+    info = {"topk_idx": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+            "slot": torch.empty(T, k, dtype=torch.int32, device="cuda")}
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_fp8_workspace_size(p), dtype=torch.uint8, device="cuda")
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.uint8)).cuda()  # noqa: E731
+    moe.moe_forward_fp8(p, dev(inp["x"]), dev(inp["Wg"]) if gate else None,
+                        dev(inp["bg"]) if gate and inp["bg"] is not None else None, u8(W1q), dev(w1s), u8(W2q),
+                        dev(w2s), y, logits=logits, info=info, ws=ws)
+    torch.cuda.synchronize()
+    z32 = host(logits) if gate else inp["logits"]
+    idx, w = oracle.route(z32, k, case.normalize, case.lam)
+    disp = oracle.dispatch(idx, E, oracle.capacity(T, E, k, case.cf))
+    assert np.array_equal(host(info["topk_idx"]), idx)
+    assert np.array_equal(host(info["slot"]), disp["slot"])
+    ref = oracle.forward_tokens_fp8(inp["x"], W1q, w1s, W2q, w2s, idx, w, disp["slot"], act_code(case), case.F)
+    got = host(y)
+    err = maxrel(got, ref)
+    # the bf16 layer bar, plus the allowance for E4M3 codes of h that the
+    # GPU's bf16 h may round the other way
+    allow = fp8_code_allowance(case, inp, W1q, w1s, W2q, w2s, w, disp)
+    over = np.abs(to_f64(got) - ref) - (TOL["bf16"] * np.max(np.abs(ref)) + allow)
+    assert np.all(over <= 0), f"max-abs-rel {err:.3e}; {float(over.max()):.3e} beyond the bound"
+    gone = np.all(disp["slot"] < 0, axis=1)
+    assert not got[gone].any()
+    print(f"  P={disp['P']} max-abs-rel {err:.2e}", flush=True)
