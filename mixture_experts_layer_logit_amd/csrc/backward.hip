@@ -257,6 +257,78 @@ __global__ __launch_bounds__(256) void moe_seg_transpose_kernel(const typename E
         [&](int c) -> T* { return dst + (size_t)(c0 + c) * ld + q0; });
 }
 
+// bf16 version of the segment transpose without LDS: one wavefront per
+// 64 positions x 64 columns.  Lane l loads 8 columns (one 16-byte vector) of
+// the rows of positions 8 (l % 8) + i, i = 0..7, at columns 8 (l / 8) + 0..7,
+// transposes that 8 x 8 block in registers, and stores it as 8 columns x 8
+// positions (16-byte vectors): the 8 lanes of equal l / 8 load 8 whole
+// 128-byte row runs and store 8 whole 128-byte runs of destination rows.
+// Block: 4 wavefronts over 4 column tiles (blockIdx.y covers 256 columns).
+__global__ __launch_bounds__(256) void moe_seg_transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                                     const int32_t* __restrict__ gather,
+                                                                     int gather_rows,
+                                                                     const int32_t* __restrict__ offsets,
+                                                                     const int32_t* __restrict__ kofs, int E,
+                                                                     int max_rows, int C, int ld,
+                                                                     uint16_t* __restrict__ dst)
+{
+    const int lane = lane_id();
+    const int q0 = blockIdx.x * 64;
+    const int c0 = (blockIdx.y * 4 + threadIdx.x / kWave) * 64;
+    if (c0 >= C)
+        return;
+    // source row of position q0 + lane (-1: padding or an empty gather entry)
+    int row = -1;
+    {
+        const int q = q0 + lane;
+        if (q < kofs[E]) {
+            int lo = 0, hi = E;  // largest e with kofs[e] <= q
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (kofs[mid] <= q)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            const int a = min(max(offsets[lo], 0), max_rows);
+            const int b = min(max(offsets[lo + 1], a), max_rows);
+            const int r = a + (q - kofs[lo]);
+            if (r < b) {
+                row = r;
+                if (gather) {
+                    row = gather[r];
+                    if (row < 0 || row >= gather_rows)
+                        row = -1;
+                }
+            }
+        }
+    }
+    const int pg = lane % 8, cg = lane / 8;  // position group (8 positions), column group (8 columns)
+    uint32_t w[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = __shfl(row, 8 * pg + i);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r >= 0)
+            v = *reinterpret_cast<const uint4*>(src + (size_t)r * C + c0 + 8 * cg);
+        w[i][0] = v.x;
+        w[i][1] = v.y;
+        w[i][2] = v.z;
+        w[i][3] = v.w;
+    }
+    // output column j: positions 8 pg + 0..7, two per 32-bit word
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t o[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t a = w[2 * m][j / 2], b = w[2 * m + 1][j / 2];
+            o[m] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+        *reinterpret_cast<uint4*>(dst + (size_t)(c0 + 8 * cg + j) * ld + q0 + 8 * pg) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
 // dx[t] = sum over kept j (in order) of dx_perm[slot[t,j]], plus, with a
 // gate, sum over e (in order) of dz[t,e] Wg[e].  One wavefront per token.
 template <typename ET>
@@ -438,14 +510,15 @@ extern "C" hipError_t moe_launch_seg_transpose(int dtype, const void* src, const
                                                int C, int ld, void* dst, hipStream_t stream)
 {
     using namespace moe;
-    const dim3 grid(ld / 64, C / 64), block(256);
-    if (dtype == 0)
+    if (dtype == 0) {
+        const dim3 grid(ld / 64, C / 64), block(256);
         moe_seg_transpose_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)src, gather, gather_rows, offsets,
                                                                     kofs, E, max_rows, C, ld, (float*)dst);
-    else
-        moe_seg_transpose_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)src, gather, gather_rows,
-                                                                     offsets, kofs, E, max_rows, C, ld,
-                                                                     (uint16_t*)dst);
+    } else {
+        const dim3 grid(ld / 64, (C / 64 + 3) / 4), block(256);
+        moe_seg_transpose_bf16_kernel<<<grid, block, 0, stream>>>((const uint16_t*)src, gather, gather_rows, offsets,
+                                                                   kofs, E, max_rows, C, ld, (uint16_t*)dst);
+    }
     return hipGetLastError();
 }
 
