@@ -17,109 +17,103 @@ namespace moe {
 // tiling.  Routing decisions therefore do not depend on how this kernel (or
 // any other correct gate) orders its sums.
 //
-// Work split: a block of 4 wavefronts holds 4 / WPT token groups of 4 tokens,
-// WPT wavefronts per group, and runs over the experts in groups of 8.  Lane l
-// of the group's wavefront w takes the 8-element chunks w*64 + l, w*64 + l +
-// 64*WPT, ... of the model dimension, so x rows and Wg rows are read with
-// 16-byte loads (1 KB per wavefront instruction).  WPT follows d: one
-// wavefront per group when a row has at most 128 chunks (every lane busy, no
-// LDS, no barrier), up to 4 for long rows (enough wavefronts in flight at
-// moderate T).  A lane's 4 x 8 partial sums are reduced across its wavefront
-// by recursive halving (each exchange halves the values a lane holds: 32
-// values need 16+8+4+2+1+1 shuffles), then the group's wavefronts are added
-// in wave order through LDS.  Expert groups are spread over blockIdx.y (every
-// group of a block shares its e0, so the barriers stay uniform); x rows are
-// re-read per expert group from cache.
-constexpr int kGateTokPerGroup = 4;
-constexpr int kGateWaves = 4;
-constexpr int kGateExpGroup = 8;
+// Work split: the fp64 matrix cores (v_mfma_f64_16x16x4f64: D[i][j] +=
+// sum over 4 k of A[i][k] B[k][j], products exact, fp64 accumulation).  A
+// block owns 16 tokens x 16 experts; its kGateSplit wavefronts split the
+// model dimension into 32-element blocks (wavefront w takes blocks w, w +
+// kGateSplit, ...).  Lane l (operand row l % 16, k group g = l / 16) loads 8
+// consecutive elements of its token's x row and of its expert's Wg row (16
+// bytes of bf16, 32 of fp32) at 8 g within the block and feeds them as the
+// k = g column of 8 successive MFMAs: both operands take the block's k
+// values in the same permuted order, so the 8 MFMAs add every product of the
+// block.  The wavefronts' 16 x 16 partial sums then meet in LDS and are added
+// in wavefront order with the bias (fp64), and rounded once to fp32.  Output
+// layout of the MFMA (probed in bounds on the GPU): value r of lane l is
+// D[4 r + l / 16][l % 16].  Rows past T or E are computed from clamped rows
+// and not stored.
+constexpr int kGateSplit = 8;
+constexpr int kGateTile = 16;
+constexpr int kGateDepth = 4;
 
-template <typename ET, int WPT>
-__global__ __launch_bounds__(256) void moe_gate_logits_kernel(const typename ET::storage* __restrict__ x,
-                                                              const typename ET::storage* __restrict__ Wg,
-                                                              const float* __restrict__ bg,
-                                                              float* __restrict__ logits, int T, int d, int E)
+// 8 consecutive values of a row as loaded (16 bytes of bf16, 32 of fp32).
+template <typename ET>
+struct GateChunk;
+template <>
+struct GateChunk<bf16_t> {
+    uint4 v;
+    __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void unpack(float* f) const { unpack8(v, f, bf16_t{}); }
+};
+template <>
+struct GateChunk<f32_t> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p)
+    {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void unpack(float* f) const
+    {
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+};
+
+template <typename ET>
+__global__ __launch_bounds__(kGateSplit * kWave) void moe_gate_logits_kernel(
+    const typename ET::storage* __restrict__ x, const typename ET::storage* __restrict__ Wg,
+    const float* __restrict__ bg, float* __restrict__ logits, int T, int d, int E)
 {
-    constexpr int kVals = kGateTokPerGroup * kGateExpGroup;  // 32 sums per lane
-    constexpr int kGroups = kGateWaves / WPT;
-    __shared__ double s_part[WPT > 1 ? kGateWaves : 1][kVals];
+    typedef double f64x4 __attribute__((ext_vector_type(4)));
+    __shared__ double s_part[kGateSplit][kGateTile * kGateTile];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    const int wig = wave % WPT;
-    const int t0 = (blockIdx.x * kGroups + wave / WPT) * kGateTokPerGroup;  // uniform over the group
-    if (WPT == 1 && t0 >= T)
-        return;
-    const bool active = t0 < T;  // WPT > 1: every wavefront stays for the barriers
-    const int nchunk = d / 8;
-    for (int e0 = blockIdx.y * kGateExpGroup; e0 < E; e0 += gridDim.y * kGateExpGroup) {
-        double acc[kVals];
+    const int t0 = blockIdx.x * kGateTile, e0 = blockIdx.y * kGateTile;
+    const int i = lane % kGateTile, g = lane / kGateTile;
+    const typename ET::storage* xr = x + (size_t)min(t0 + i, T - 1) * d + 8 * g;
+    const typename ET::storage* wr = Wg + (size_t)min(e0 + i, E - 1) * d + 8 * g;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    // this wavefront's blocks: wave, wave + kGateSplit, ...; their raw 16- or
+    // 32-byte chunks go through a ring of kGateDepth register slots, refilled
+    // kGateDepth blocks ahead, so several loads are in flight per wavefront
+    const int nb = (d / 32 - wave + kGateSplit - 1) / kGateSplit;
+    typedef GateChunk<ET> Chunk;
+    Chunk xq[kGateDepth], wq[kGateDepth];
 #pragma unroll
-        for (int v = 0; v < kVals; ++v)
-            acc[v] = 0.0;
-        for (int c = wig * kWave + lane; active && c < nchunk; c += WPT * kWave) {
-            double xd[kGateTokPerGroup][8];
+    for (int q = 0; q < kGateDepth; ++q)
+        if (q < nb) {
+            xq[q].load(xr + (size_t)(wave + q * kGateSplit) * 32);
+            wq[q].load(wr + (size_t)(wave + q * kGateSplit) * 32);
+        }
+    for (int it = 0; it < nb; it += kGateDepth) {
 #pragma unroll
-            for (int tt = 0; tt < kGateTokPerGroup; ++tt) {
-                float xf[8];
-                const int t = min(t0 + tt, T - 1);  // rows past T are computed but not stored
-                load8(x + (size_t)t * d + (size_t)c * 8, xf);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    xd[tt][i] = (double)xf[i];
-            }
-#pragma unroll
-            for (int ee = 0; ee < kGateExpGroup; ++ee) {
-                const int e = min(e0 + ee, E - 1);
-                float wf[8];
-                load8(Wg + (size_t)e * d + (size_t)c * 8, wf);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const double wd = (double)wf[i];
-#pragma unroll
-                    for (int tt = 0; tt < kGateTokPerGroup; ++tt)
-                        acc[tt * kGateExpGroup + ee] = fma(xd[tt][i], wd, acc[tt * kGateExpGroup + ee]);
+        for (int q = 0; q < kGateDepth; ++q) {
+            if (it + q < nb) {
+                float xf[8], wf[8];
+                xq[q].unpack(xf);
+                wq[q].unpack(wf);
+                if (it + q + kGateDepth < nb) {
+                    const size_t off = (size_t)(wave + (it + q + kGateDepth) * kGateSplit) * 32;
+                    xq[q].load(xr + off);
+                    wq[q].load(wr + off);
                 }
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xf[s], (double)wf[s], acc, 0, 0, 0);
             }
         }
-        // Recursive halving over lane bits 5..1: after the exchange across
-        // bit b a lane keeps the half of its values selected by its own bit b.
-        double* v = acc;
-        int n = kVals;
+    }
 #pragma unroll
-        for (int bit = 5; bit >= 1; --bit) {
-            const int half = n / 2;
-            const bool upper = (lane >> bit) & 1;
+    for (int r = 0; r < 4; ++r)
+        s_part[wave][(4 * r + g) * kGateTile + i] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < kGateTile * kGateTile) {
+        const int t = t0 + threadIdx.x / kGateTile, e = e0 + threadIdx.x % kGateTile;
+        double sum = s_part[0][threadIdx.x];
 #pragma unroll
-            for (int i = 0; i < kVals / 2; ++i) {
-                if (i < half) {
-                    const double keep = upper ? v[half + i] : v[i];
-                    const double send = upper ? v[i] : v[half + i];
-                    v[i] = keep + __shfl_xor(send, 1 << bit);
-                }
-            }
-            n = half;
-        }
-        double sum = v[0] + __shfl_xor(v[0], 1);
-        // lane l now holds value index (l >> 1): token (l >> 4), expert ((l >> 1) & 7)
-        int idx = lane >> 1;
-        bool writer = (lane & 1) == 0;
-        if constexpr (WPT > 1) {
-            if (writer)
-                s_part[wave][idx] = sum;
-            __syncthreads();
-            writer = wig == 0 && lane < kVals;
-            idx = lane;
-            if (writer) {
-                sum = s_part[wave][idx];
-#pragma unroll
-                for (int w = 1; w < WPT; ++w)
-                    sum += s_part[wave + w][idx];
-            }
-            __syncthreads();  // s_part is reused by the next expert group
-        }
-        const int t = t0 + idx / kGateExpGroup;
-        const int e = e0 + idx % kGateExpGroup;
-        if (writer && active && t < T && e < E) {
+        for (int w = 1; w < kGateSplit; ++w)
+            sum += s_part[w][threadIdx.x];
+        if (t < T && e < E) {
             if (bg)
                 sum += (double)bg[e];
             logits[(size_t)t * E + e] = (float)sum;
@@ -522,26 +516,12 @@ extern "C" hipError_t moe_launch_gate(int dtype, const void* x, const void* Wg, 
                                       int T, int d, int E, hipStream_t stream)
 {
     using namespace moe;
-    const int nchunk = d / 8;
-    const int wpt = nchunk > 256 ? 4 : nchunk > 128 ? 2 : 1;
-    const int tok_per_block = kGateTokPerGroup * (kGateWaves / wpt);
-    const int egroups = (E + kGateExpGroup - 1) / kGateExpGroup;
-    const dim3 grid((T + tok_per_block - 1) / tok_per_block, egroups), block(kGateWaves * kWave);
-    auto go = [&](auto et, auto wpt_c) {
-        typedef decltype(et) ET;
-        typedef typename ET::storage S;
-        moe_gate_logits_kernel<ET, decltype(wpt_c)::value>
-            <<<grid, block, 0, stream>>>((const S*)x, (const S*)Wg, bg, logits, T, d, E);
-    };
-    if (dtype == 0) {
-        if (wpt == 4) go(f32_t{}, std::integral_constant<int, 4>{});
-        else if (wpt == 2) go(f32_t{}, std::integral_constant<int, 2>{});
-        else go(f32_t{}, std::integral_constant<int, 1>{});
-    } else {
-        if (wpt == 4) go(bf16_t{}, std::integral_constant<int, 4>{});
-        else if (wpt == 2) go(bf16_t{}, std::integral_constant<int, 2>{});
-        else go(bf16_t{}, std::integral_constant<int, 1>{});
-    }
+    const dim3 grid((T + kGateTile - 1) / kGateTile, (E + kGateTile - 1) / kGateTile), block(kGateSplit * kWave);
+    if (dtype == 0)
+        moe_gate_logits_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)x, (const float*)Wg, bg, logits, T, d, E);
+    else
+        moe_gate_logits_kernel<bf16_t>
+            <<<grid, block, 0, stream>>>((const uint16_t*)x, (const uint16_t*)Wg, bg, logits, T, d, E);
     return hipGetLastError();
 }
 
