@@ -169,6 +169,140 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
     }
 }
 
+// Small problems (T <= kSmallT tokens, E <= kSmallE experts): count, scan and
+// scatter in one block of 1024 threads, saving two launches.  Counts come
+// from LDS atomics over every assignment; then the tokens are walked in
+// chunks of 1024 (one per thread) with a running per-expert base: a
+// choice's rank is that base plus the counts of the earlier wavefronts of
+// the chunk plus its rank inside the wavefront (ballots, as in the scatter
+// kernel).  Same ranks, same rows, one launch.  Each chunk costs about 5 us
+// on the one CU, so beyond one chunk the three-kernel path is faster
+// (measured: 27 against 15 us at 4096 tokens, 8.7 against 12 us at 256).
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallT = 1024;
+constexpr int kSmallE = 256;
+
+__global__ __launch_bounds__(kSmallThreads) void moe_permute_small_kernel(const int32_t* __restrict__ topk_idx, int T,
+                                                                         int E, int k, long long C,
+                                                                         int32_t* __restrict__ counts,
+                                                                         int32_t* __restrict__ offsets,
+                                                                         int32_t* __restrict__ slot,
+                                                                         int32_t* __restrict__ src_token)
+{
+    constexpr int kWaves = kSmallThreads / kWave;
+    __shared__ int32_t s_cnt[kSmallE];
+    __shared__ int32_t s_off[kSmallE];
+    __shared__ int32_t s_run[kSmallE];
+    __shared__ int32_t wave_cnt[kWaves][kSmallE];
+    __shared__ int32_t wsum[kWaves];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    if (tid < E)
+        s_cnt[tid] = 0;
+    __syncthreads();
+    for (int a = tid; a < T * k; a += kSmallThreads) {
+        const int e = topk_idx[a];
+        if (e >= 0 && e < E)
+            atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    // counts, capacity clip, exclusive scan over experts
+    int kept = 0;
+    if (tid < E) {
+        counts[tid] = s_cnt[tid];
+        kept = s_cnt[tid];
+        if (C >= 0 && kept > C)
+            kept = (int)C;
+        s_run[tid] = 0;
+    }
+    int incl = kept;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(incl, o);
+        if (lane >= o)
+            incl += n;
+    }
+    if (lane == kWave - 1)
+        wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w)
+        base += wsum[w];
+    if (tid < E) {
+        s_off[tid] = base + incl - kept;
+        offsets[tid] = base + incl - kept;
+    }
+    if (tid == E - 1)
+        offsets[E] = base + incl;
+    int nbits = 0;
+    while ((1 << nbits) < E)
+        ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int t0 = 0; t0 < T; t0 += kSmallThreads) {
+        for (int i = tid; i < kWaves * E; i += kSmallThreads)
+            wave_cnt[i / E][i % E] = 0;
+        __syncthreads();
+        const int t = t0 + tid;
+        const bool live = t < T;
+        int my[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            my[j] = -1;
+            if (j < k && live) {
+                const int e = topk_idx[(size_t)t * k + j];
+                my[j] = (e >= 0 && e < E) ? e : -1;
+            }
+            if (my[j] >= 0)
+                atomicAdd(&wave_cnt[wave][my[j]], 1);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j >= k)
+                break;
+            const int e = my[j];
+            int r = 0;
+#pragma unroll
+            for (int j2 = 0; j2 < 8; ++j2) {
+                if (j2 >= k)
+                    break;
+                const int col = my[j2];
+                uint64_t peers = __ballot(col >= 0);
+                for (int b = 0; b < nbits; ++b) {
+                    const uint64_t ones = __ballot(col >= 0 && ((col >> b) & 1));
+                    peers &= (((e >> b) & 1) ? ones : ~ones);
+                }
+                r += __popcll(peers & below);
+            }
+            if (e < 0)
+                continue;
+            for (int w = 0; w < wave; ++w)
+                r += wave_cnt[w][e];
+            const long long rank = (long long)s_run[e] + r;
+            if (C < 0 || rank < C) {
+                const int row = s_off[e] + (int)rank;
+                slot[(size_t)t * k + j] = row;
+                src_token[row] = t;
+            } else {
+                slot[(size_t)t * k + j] = -1;
+            }
+        }
+        if (live) {
+            for (int j = 0; j < k; ++j)
+                if (my[j] < 0)
+                    slot[(size_t)t * k + j] = -1;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int add = 0;
+            for (int w = 0; w < kWaves; ++w)
+                add += wave_cnt[w][tid];
+            s_run[tid] += add;
+        }
+        // the next chunk clears wave_cnt only after this barrier
+        __syncthreads();
+    }
+}
+
 // One wavefront per token; the row is read once and written to each kept slot.
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_gather_kernel(const typename ET::storage* __restrict__ x,
@@ -219,10 +353,16 @@ extern "C" hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, con
                                          hipStream_t stream)
 {
     using namespace moe;
-    const int nchunks = (T + kChunk - 1) / kChunk;
-    moe_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, chunk_cnt);
-    moe_scan_kernel<<<1, 1024, 0, stream>>>(chunk_cnt, nchunks, E, C, counts, offsets);
-    moe_scatter_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, C, chunk_cnt, offsets, slot, src_token);
+    if (T <= kSmallT && E <= kSmallE) {
+        moe_permute_small_kernel<<<1, kSmallThreads, 0, stream>>>(topk_idx, T, E, k, C, counts, offsets, slot,
+                                                                   src_token);
+    } else {
+        const int nchunks = (T + kChunk - 1) / kChunk;
+        moe_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, chunk_cnt);
+        moe_scan_kernel<<<1, 1024, 0, stream>>>(chunk_cnt, nchunks, E, C, counts, offsets);
+        moe_scatter_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, C, chunk_cnt, offsets, slot,
+                                                           src_token);
+    }
     if (x_perm == nullptr)
         return hipGetLastError();
     const dim3 grid((T + 3) / 4);
