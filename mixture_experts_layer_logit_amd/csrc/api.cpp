@@ -981,9 +981,10 @@ moe_status moe_backward(const moe_problem* p, const void* dy, const void* x, con
     // combine and router
     CHECK(hip_status(moe_launch_combine_bwd(dt, dy, saved->y_perm, info->slot, info->topk_w, T, d, k, rows, d_yp, d_w,
                                             s), "combine backward launch"));
-    CHECK(hip_status(moe_launch_router_bwd(logits, info->topk_idx, info->slot, d_w, T, E, k, p->normalize, p->lambda,
-                                           aux_coef, z_coef, info->counts, dz, s),
-                     "router backward launch"));
+    if (Wg)  // with given logits nothing reads the logit gradient
+        CHECK(hip_status(moe_launch_router_bwd(logits, info->topk_idx, info->slot, d_w, T, E, k, p->normalize,
+                                               p->lambda, aux_coef, z_coef, info->counts, dz, s),
+                         "router backward launch"));
     // input gradients of the expert layers: dh = d_yp W2[e] (+ activation backward), dx_perm = du W1[e]
     const int depi = p->act == MOE_ACT_SWIGLU ? 4 : 3;
     if (p->dtype == MOE_BF16) {

@@ -330,53 +330,145 @@ __global__ __launch_bounds__(256) void moe_seg_transpose_bf16_kernel(const uint1
 }
 
 // dx[t] = sum over kept j (in order) of dx_perm[slot[t,j]], plus, with a
-// gate, sum over e (in order) of dz[t,e] Wg[e].  One wavefront per token.
+// gate, sum over e (in order) of dz[t,e] Wg[e].  A wavefront owns a slice of
+// the rows of kUnpTok consecutive tokens (kUnpVec 16-byte vectors per lane):
+// each gate row slice it loads serves all of its tokens, and the loads of two
+// choices of every token, or of four experts' gate rows, are issued before
+// they are added.
+constexpr int kUnpVec = 1;
+constexpr int kUnpTok = 2;
+
+template <typename ET>
+__device__ __forceinline__ void unpack_vec(const uint4& raw, float* f)  // 16 bytes
+{
+    if constexpr (ET::kBytes == 2) {
+        unpack8(raw, f, bf16_t{});
+    } else {
+        f[0] = __uint_as_float(raw.x);
+        f[1] = __uint_as_float(raw.y);
+        f[2] = __uint_as_float(raw.z);
+        f[3] = __uint_as_float(raw.w);
+    }
+}
+
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_unpermute_bwd_kernel(const typename ET::storage* __restrict__ dx_perm,
                                                                 const int32_t* __restrict__ slot, int T, int d, int k,
                                                                 int max_rows, const float* __restrict__ dz,
                                                                 const typename ET::storage* __restrict__ Wg, int E,
-                                                                typename ET::storage* __restrict__ dx)
+                                                                int nparts, typename ET::storage* __restrict__ dx)
 {
     constexpr int kPer = 16 / ET::kBytes;
     const int lane = lane_id();
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (t >= T)
+    const int unit = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int tg = unit / nparts;
+    const int part = unit - tg * nparts;
+    const int t0 = tg * kUnpTok;
+    if (t0 >= T)
         return;
+    const int ntok = min(kUnpTok, T - t0);
     const int nvec = d / kPer;
-    int rows[8];
+    const int v0 = part * kWave * kUnpVec;
+    float acc[kUnpTok][kUnpVec][kPer];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
-        if (rows[j] >= max_rows)
-            rows[j] = -1;
-    }
-    for (int v = lane; v < nvec; v += kWave) {
-        float acc[kPer];
+    for (int i = 0; i < kUnpTok; ++i)
 #pragma unroll
-        for (int q = 0; q < kPer; ++q)
-            acc[q] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (rows[j] < 0)
-                continue;
-            float g[kPer];
-            load_vec<ET>(dx_perm + (size_t)rows[j] * d + (size_t)v * kPer, g);
+        for (int u = 0; u < kUnpVec; ++u)
 #pragma unroll
             for (int q = 0; q < kPer; ++q)
-                acc[q] += g[q];
-        }
-        if (Wg) {
-            for (int e = 0; e < E; ++e) {
-                const float z = dz[(size_t)t * E + e];
-                float wv[kPer];
-                load_vec<ET>(Wg + (size_t)e * d + (size_t)v * kPer, wv);
+                acc[i][u][q] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += 2) {
+        int rows[kUnpTok][2];
 #pragma unroll
-                for (int q = 0; q < kPer; ++q)
-                    acc[q] = fmaf(z, wv[q], acc[q]);
+        for (int i = 0; i < kUnpTok; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int j = j0 + h;
+                rows[i][h] = (i < ntok && j < k) ? slot[(size_t)(t0 + i) * k + j] : -1;
+                if (rows[i][h] >= max_rows)
+                    rows[i][h] = -1;
+            }
+        uint4 raw[kUnpTok][2][kUnpVec];
+#pragma unroll
+        for (int i = 0; i < kUnpTok; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (rows[i][h] < 0)
+                    continue;
+                const uint4* src = reinterpret_cast<const uint4*>(dx_perm + (size_t)rows[i][h] * d);
+#pragma unroll
+                for (int u = 0; u < kUnpVec; ++u) {
+                    const int v = v0 + u * kWave + lane;
+                    if (v < nvec)
+                        raw[i][h][u] = src[v];
+                }
+            }
+#pragma unroll
+        for (int i = 0; i < kUnpTok; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (rows[i][h] < 0)
+                    continue;
+#pragma unroll
+                for (int u = 0; u < kUnpVec; ++u) {
+                    if (v0 + u * kWave + lane < nvec) {
+                        float g[kPer];
+                        unpack_vec<ET>(raw[i][h][u], g);
+#pragma unroll
+                        for (int q = 0; q < kPer; ++q)
+                            acc[i][u][q] += g[q];
+                    }
+                }
+            }
+    }
+    if (Wg) {
+        for (int e0 = 0; e0 < E; e0 += 4) {
+            uint4 raw[4][kUnpVec];
+            float z[kUnpTok][4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                if (e0 + h >= E)
+                    continue;
+#pragma unroll
+                for (int i = 0; i < kUnpTok; ++i)
+                    z[i][h] = i < ntok ? dz[(size_t)(t0 + i) * E + e0 + h] : 0.0f;
+                const uint4* src = reinterpret_cast<const uint4*>(Wg + (size_t)(e0 + h) * d);
+#pragma unroll
+                for (int u = 0; u < kUnpVec; ++u) {
+                    const int v = v0 + u * kWave + lane;
+                    if (v < nvec)
+                        raw[h][u] = src[v];
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                if (e0 + h >= E)
+                    continue;
+#pragma unroll
+                for (int u = 0; u < kUnpVec; ++u) {
+                    if (v0 + u * kWave + lane < nvec) {
+                        float wv[kPer];
+                        unpack_vec<ET>(raw[h][u], wv);
+#pragma unroll
+                        for (int i = 0; i < kUnpTok; ++i)
+#pragma unroll
+                            for (int q = 0; q < kPer; ++q)
+                                acc[i][u][q] = fmaf(z[i][h], wv[q], acc[i][u][q]);
+                    }
+                }
             }
         }
-        store_vec<ET>(dx + (size_t)t * d + (size_t)v * kPer, acc);
+    }
+#pragma unroll
+    for (int i = 0; i < kUnpTok; ++i) {
+        if (i >= ntok)
+            break;
+#pragma unroll
+        for (int u = 0; u < kUnpVec; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < nvec)
+                store_vec<ET>(dx + (size_t)(t0 + i) * d + (size_t)v * kPer, acc[i][u]);
+        }
     }
 }
 
@@ -384,7 +476,9 @@ __global__ __launch_bounds__(256) void moe_unpermute_bwd_kernel(const typename E
 // expert group of 16): partial[chunk][e][c] = sum over the chunk's tokens (in
 // order) of dz[t,e] x[t,c]; the column-group-0 blocks also write
 // partial_b[chunk][e] = sum over the chunk's tokens of dz[t,e].  Pass 2 adds
-// the chunks in order.
+// the chunks in order.  The chunk's dz values are staged in LDS (read as
+// broadcasts) and each thread loads x for 16 tokens before using them, so
+// the loads overlap instead of each token waiting for its own.
 constexpr int kGateChunk = 64;
 
 template <typename ET>
@@ -393,60 +487,103 @@ __global__ __launch_bounds__(256) void moe_gate_wgrad_kernel(const float* __rest
                                                              int E, float* __restrict__ partial,
                                                              float* __restrict__ partial_b)
 {
-    const int t0 = blockIdx.x * kGateChunk, t1 = min(T, t0 + kGateChunk);
-    const int c = blockIdx.y * 256 + threadIdx.x;
+    __shared__ float4 sdz[kGateChunk][4];  // [token of the chunk][experts e0..e0+15], zero past E
+    const int t0 = blockIdx.x * kGateChunk, nt = min(T, t0 + kGateChunk) - t0;
     const int e0 = blockIdx.z * 16;
+    for (int i = threadIdx.x; i < kGateChunk * 16; i += 256) {
+        const int tt = i >> 4, ee = i & 15;
+        reinterpret_cast<float*>(sdz)[i] = (tt < nt && e0 + ee < E) ? dz[(size_t)(t0 + tt) * E + e0 + ee] : 0.0f;
+    }
+    __syncthreads();
+    const int c = blockIdx.y * 256 + threadIdx.x;
     if (c < d) {
         float acc[16];
 #pragma unroll
         for (int ee = 0; ee < 16; ++ee)
             acc[ee] = 0.0f;
-        for (int t = t0; t < t1; ++t) {
-            float xv;
-            if constexpr (ET::kBytes == 2)
-                xv = __uint_as_float((uint32_t)x[(size_t)t * d + c] << 16);
-            else
-                xv = x[(size_t)t * d + c];
+        auto token = [&](int tt, float xt) {
+            float z[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 q = sdz[tt][g];
+                z[4 * g] = q.x;
+                z[4 * g + 1] = q.y;
+                z[4 * g + 2] = q.z;
+                z[4 * g + 3] = q.w;
+            }
 #pragma unroll
             for (int ee = 0; ee < 16; ++ee)
-                if (e0 + ee < E)
-                    acc[ee] = fmaf(dz[(size_t)t * E + e0 + ee], xv, acc[ee]);
+                acc[ee] = fmaf(z[ee], xt, acc[ee]);
+        };
+        auto load_x = [&](int tt) -> float {
+            const size_t at = (size_t)(t0 + tt) * d + c;
+            if constexpr (ET::kBytes == 2)
+                return __uint_as_float((uint32_t)x[at] << 16);
+            else
+                return x[at];
+        };
+        // whole batches of 16 tokens: the loads carry no branch, so all 16
+        // are in flight before the first is used; then the chunk's tail
+        int tb = 0;
+        for (; tb + 16 <= nt; tb += 16) {
+            float xv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                xv[u] = load_x(tb + u);
+            // keep the scheduler from interleaving the uses with the loads
+            // (it otherwise reuses one register per load and waits on each)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                token(tb + u, xv[u]);
         }
+        for (; tb < nt; ++tb)
+            token(tb, load_x(tb));
 #pragma unroll
         for (int ee = 0; ee < 16; ++ee)
             if (e0 + ee < E)
                 partial[((size_t)blockIdx.x * E + e0 + ee) * d + c] = acc[ee];
     }
     if (blockIdx.y == 0 && threadIdx.x < 16 && e0 + (int)threadIdx.x < E) {
-        const int e = e0 + threadIdx.x;
+        const float* col = reinterpret_cast<const float*>(sdz) + threadIdx.x;
         float sb = 0.0f;
-        for (int t = t0; t < t1; ++t)
-            sb += dz[(size_t)t * E + e];
-        partial_b[(size_t)blockIdx.x * E + e] = sb;
+        for (int tt = 0; tt < nt; ++tt)
+            sb += col[16 * tt];
+        partial_b[(size_t)blockIdx.x * E + e0 + threadIdx.x] = sb;
     }
 }
 
 // Pass 2: element i < E*d of dWg, then the E entries of dbg, each the sum of
-// its nchunks partials in chunk order.
-__global__ __launch_bounds__(256) void moe_gate_wgrad_reduce_kernel(const float* __restrict__ partial,
-                                                                    const float* __restrict__ partial_b, int nchunks,
-                                                                    int E, int d, float* __restrict__ dWg,
-                                                                    float* __restrict__ dbg)
+// its nchunks partials in chunk order (eight loads issued before they are
+// added).
+__global__ __launch_bounds__(64) void moe_gate_wgrad_reduce_kernel(const float* __restrict__ partial,
+                                                                   const float* __restrict__ partial_b, int nchunks,
+                                                                   int E, int d, float* __restrict__ dWg,
+                                                                   float* __restrict__ dbg)
 {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t i = (size_t)blockIdx.x * 64 + threadIdx.x;
     const size_t n = (size_t)E * d;
-    if (i < n) {
-        float s = 0.0f;
-        for (int ch = 0; ch < nchunks; ++ch)
-            s += partial[(size_t)ch * n + i];
-        dWg[i] = s;
-    } else if (i < n + E) {
-        const size_t e = i - n;
-        float s = 0.0f;
-        for (int ch = 0; ch < nchunks; ++ch)
-            s += partial_b[(size_t)ch * E + e];
-        dbg[e] = s;
+    if (i >= n + E)
+        return;
+    const float* src = i < n ? partial + i : partial_b + (i - n);
+    const size_t stride = i < n ? n : (size_t)E;
+    float s = 0.0f;
+    int ch = 0;
+    for (; ch + 8 <= nchunks; ch += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = src[(size_t)(ch + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            s += v[u];
     }
+    for (; ch < nchunks; ++ch)
+        s += src[(size_t)ch * stride];
+    if (i < n)
+        dWg[i] = s;
+    else
+        dbg[i - n] = s;
 }
 
 // n floats set to 0 (a kernel, so that a captured graph holds no memset node).
@@ -527,13 +664,18 @@ extern "C" hipError_t moe_launch_unpermute_bwd(int dtype, const void* dx_perm, c
                                                hipStream_t stream)
 {
     using namespace moe;
-    const dim3 grid((T + 3) / 4), block(256);
+    const int per = dtype == 0 ? 4 : 8;  // elements per 16-byte vector
+    const int nparts = (d / per + kWave * kUnpVec - 1) / (kWave * kUnpVec);
+    const long units = (long)((T + kUnpTok - 1) / kUnpTok) * nparts;
+    if (units == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((units + 3) / 4)), block(256);
     if (dtype == 0)
         moe_unpermute_bwd_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)dx_perm, slot, T, d, k, max_rows, dz,
-                                                                    (const float*)Wg, E, (float*)dx);
+                                                                    (const float*)Wg, E, nparts, (float*)dx);
     else
         moe_unpermute_bwd_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)dx_perm, slot, T, d, k,
-                                                                     max_rows, dz, (const uint16_t*)Wg, E,
+                                                                     max_rows, dz, (const uint16_t*)Wg, E, nparts,
                                                                      (uint16_t*)dx);
     return hipGetLastError();
 }
@@ -562,7 +704,7 @@ extern "C" hipError_t moe_launch_gate_wgrad(int dtype, const float* dz, const vo
     if (err != hipSuccess)
         return err;
     const size_t n = (size_t)E * d + E;
-    moe_gate_wgrad_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), block, 0, stream>>>(partial, partial_b, nch,
-                                                                                          E, d, dWg, dbg);
+    moe_gate_wgrad_reduce_kernel<<<dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream>>>(partial, partial_b, nch, E,
+                                                                                           d, dWg, dbg);
     return hipGetLastError();
 }

@@ -289,11 +289,15 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
         return;
     const float* zt = logits + (size_t)t * E;
     float z[VPL];
+    // unconditional loads (index clamped, padding zeroed after): all VPL
+    // are in flight together
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
-        z[i] = e < E ? zt[e] : 0.0f;
-    }
+    for (int i = 0; i < VPL; ++i)
+        z[i] = zt[min(lane + kWave * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (lane + kWave * i >= E)
+            z[i] = 0.0f;
     double ex[VPL], denom;
     token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
     double p[VPL], dp[VPL];
@@ -302,7 +306,8 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
     for (int i = 0; i < VPL; ++i) {
         const int e = lane + kWave * i;
         p[i] = ex[i] / denom;
-        dp[i] = (aux_coef != 0.0f && e < E) ? aux_scale * (double)counts[e] : 0.0;
+        const int32_t ce = counts[min(e, E - 1)];
+        dp[i] = (aux_coef != 0.0f && e < E) ? aux_scale * (double)ce : 0.0;
     }
     for (int j = 0; j < k; ++j) {
         const size_t a = (size_t)t * k + j;
@@ -411,11 +416,14 @@ __global__ __launch_bounds__(256) void moe_router_stats_kernel(const float* __re
     for (int t = blockIdx.x * 4 + wave; t < T; t += 4 * gridDim.x) {
         const float* zt = logits + (size_t)t * E;
         float z[VPL];
+        // unconditional loads (index clamped, padding zeroed after)
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int e = lane + kWave * i;
-            z[i] = e < E ? zt[e] : 0.0f;
-        }
+        for (int i = 0; i < VPL; ++i)
+            z[i] = zt[min(lane + kWave * i, E - 1)];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (lane + kWave * i >= E)
+                z[i] = 0.0f;
         double ex[VPL], denom;
         token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
 #pragma unroll
