@@ -14,7 +14,9 @@
 //           rank), counts, capacity clip, exclusive scan over experts
 //   scatter chunk by chunk again: rank = chunk base + earlier wavefronts'
 //           counts + rank inside the wavefront, the last from ballots that
-//           find the lanes holding the same expert; writes slot, src_token
+//           find the lanes holding the same expert; writes slot, src_token.
+//           When nchunks*E is small it does the scan's work itself and the
+//           scan is not launched
 //   gather  one wavefront per token reads x[t] once (16-byte loads) and
 //           writes it to each of the token's kept rows of x_perm
 #include "common.h"
@@ -98,19 +100,88 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ ch
         offsets[E] = base + incl;
 }
 
+// The scatter, as above.  With kFused the scan is done here too: chunk_cnt
+// still holds the per-chunk counts, and every block sums them for its own
+// base ranks (the chunks before it) and the experts' totals, clips them to
+// the capacity and scans them into offsets (block 0 writes counts and
+// offsets out).  That costs each block nchunks*E reads, so it is used when
+// that product is at most kFuseScanMax, and saves the scan's launch.
+constexpr long long kFuseScanMax = 64 * 1024;
+
+template <bool kFused>
 __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __restrict__ topk_idx, int T, int E,
                                                              int k, long long C,
-                                                             const int32_t* __restrict__ chunk_base,
-                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ chunk_cnt, int nchunks,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ slot,
                                                              int32_t* __restrict__ src_token)
 {
     constexpr int kWaves = kChunk / kWave;
     __shared__ int32_t wave_cnt[kWaves][kMaxE];
+    __shared__ int32_t s_base[kMaxE];  // this chunk's base rank per expert
+    __shared__ int32_t s_off[kMaxE];   // the experts' first rows
+    __shared__ int32_t wsum[kWaves];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     for (int i = threadIdx.x; i < kWaves * E; i += kChunk)
         wave_cnt[i / E][i % E] = 0;
+    if constexpr (kFused) {
+        for (int e = threadIdx.x; e < E; e += kChunk) {
+            int b = 0, tot = 0;  // integer sums: the order does not matter
+#pragma unroll 8
+            for (int c = 0; c < nchunks; ++c) {
+                const int v = chunk_cnt[(size_t)c * E + e];
+                b += c < (int)blockIdx.x ? v : 0;
+                tot += v;
+            }
+            s_base[e] = b;
+            s_off[e] = (C >= 0 && tot > C) ? (int)C : tot;  // kept, scanned below
+            if (blockIdx.x == 0)
+                counts[e] = tot;
+        }
+        __syncthreads();
+        // exclusive scan of the kept counts: thread i holds experts 4i..4i+3
+        int v[4], loc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * (int)threadIdx.x + q;
+            v[q] = e < E ? s_off[e] : 0;
+            loc += v[q];
+        }
+        int incl = loc;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int n = __shfl_up(incl, o);
+            if (lane >= o)
+                incl += n;
+        }
+        if (lane == kWave - 1)
+            wsum[wave] = incl;
+        __syncthreads();
+        int run = incl - loc, total = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            run += w < wave ? wsum[w] : 0;
+            total += wsum[w];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * (int)threadIdx.x + q;
+            if (e < E) {
+                s_off[e] = run;
+                if (blockIdx.x == 0)
+                    offsets[e] = run;
+                run += v[q];
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            offsets[E] = total;
+    } else {
+        for (int e = threadIdx.x; e < E; e += kChunk) {
+            s_base[e] = chunk_cnt[(size_t)blockIdx.x * E + e];
+            s_off[e] = offsets[e];
+        }
+    }
     __syncthreads();
     const int t = blockIdx.x * kChunk + threadIdx.x;
     const bool live = t < T;
@@ -153,9 +224,9 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
             continue;
         for (int w = 0; w < wave; ++w)
             r += wave_cnt[w][e];
-        const long long rank = (long long)chunk_base[(size_t)blockIdx.x * E + e] + r;
+        const long long rank = (long long)s_base[e] + r;
         if (C < 0 || rank < C) {
-            const int row = offsets[e] + (int)rank;
+            const int row = s_off[e] + (int)rank;
             slot[(size_t)t * k + j] = row;
             src_token[row] = t;
         } else {
@@ -359,9 +430,14 @@ extern "C" hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, con
     } else {
         const int nchunks = (T + kChunk - 1) / kChunk;
         moe_count_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, chunk_cnt);
-        moe_scan_kernel<<<1, 1024, 0, stream>>>(chunk_cnt, nchunks, E, C, counts, offsets);
-        moe_scatter_kernel<<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, C, chunk_cnt, offsets, slot,
-                                                           src_token);
+        if ((long long)nchunks * E <= kFuseScanMax) {
+            moe_scatter_kernel<true><<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, C, chunk_cnt, nchunks,
+                                                                     offsets, counts, slot, src_token);
+        } else {
+            moe_scan_kernel<<<1, 1024, 0, stream>>>(chunk_cnt, nchunks, E, C, counts, offsets);
+            moe_scatter_kernel<false><<<nchunks, kChunk, 0, stream>>>(topk_idx, T, E, k, C, chunk_cnt, nchunks,
+                                                                      offsets, counts, slot, src_token);
+        }
     }
     if (x_perm == nullptr)
         return hipGetLastError();
