@@ -59,10 +59,25 @@ __device__ __forceinline__ void store_vec(typename ET::storage* p, const float* 
     *reinterpret_cast<uint4*>(p) = o;
 }
 
+template <typename ET>
+__device__ __forceinline__ void unpack_vec(const uint4& raw, float* f)  // 16 bytes
+{
+    if constexpr (ET::kBytes == 2) {
+        unpack8(raw, f, bf16_t{});
+    } else {
+        f[0] = __uint_as_float(raw.x);
+        f[1] = __uint_as_float(raw.y);
+        f[2] = __uint_as_float(raw.z);
+        f[3] = __uint_as_float(raw.w);
+    }
+}
+
 // One wavefront per token.  Lane l owns 16-byte vectors l, l+64, ... of the
 // row; a dot product is the lanes' partial sums (each in vector order) added
-// by a fixed shuffle tree.  Slots at or past max_rows count as dropped.
-template <typename ET>
+// by a fixed shuffle tree.  Slots at or past max_rows count as dropped.  Two
+// vectors of dy and of every kept choice's y_perm row are loaded before any
+// is used (kMaxK bounds k, so the registers follow the choice count).
+template <typename ET, int kMaxK>
 __global__ __launch_bounds__(256) void moe_combine_bwd_kernel(const typename ET::storage* __restrict__ dy,
                                                               const typename ET::storage* __restrict__ y_perm,
                                                               const int32_t* __restrict__ slot,
@@ -71,40 +86,69 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_kernel(const typename ET:
                                                               float* __restrict__ d_w)
 {
     constexpr int kPer = 16 / ET::kBytes;
+    constexpr int kU = 2;  // vectors per lane per pass
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T)
         return;
     const int nvec = d / kPer;
-    int rows[8];
-    float w[8], dot[8];
+    int rows[kMaxK];
+    float w[kMaxK], dot[kMaxK];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kMaxK; ++j) {
         rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
         if (rows[j] >= max_rows)
             rows[j] = -1;
         w[j] = (j < k) ? topk_w[(size_t)t * k + j] : 0.0f;
         dot[j] = 0.0f;
     }
-    for (int v = lane; v < nvec; v += kWave) {
-        float g[kPer];
-        load_vec<ET>(dy + (size_t)t * d + (size_t)v * kPer, g);
+    const uint4* gsrc = reinterpret_cast<const uint4*>(dy + (size_t)t * d);
+    for (int v0 = lane; v0 < nvec; v0 += kWave * kU) {
+        uint4 graw[kU], yraw[kU][kMaxK];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int u = 0; u < kU; ++u) {
+            const int v = v0 + u * kWave;
+            if (v < nvec)
+                graw[u] = gsrc[v];
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
             if (rows[j] < 0)
                 continue;
-            float yv[kPer], o[kPer];
-            load_vec<ET>(y_perm + (size_t)rows[j] * d + (size_t)v * kPer, yv);
+            const uint4* ysrc = reinterpret_cast<const uint4*>(y_perm + (size_t)rows[j] * d);
 #pragma unroll
-            for (int q = 0; q < kPer; ++q) {
-                dot[j] = fmaf(g[q], yv[q], dot[j]);
-                o[q] = w[j] * g[q];
+            for (int u = 0; u < kU; ++u) {
+                const int v = v0 + u * kWave;
+                if (v < nvec)
+                    yraw[u][j] = ysrc[v];
             }
-            store_vec<ET>(d_yp + (size_t)rows[j] * d + (size_t)v * kPer, o);
+        }
+        // keep the uses below the loads (otherwise each load is waited on alone)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int v = v0 + u * kWave;
+            if (v >= nvec)
+                break;
+            float g[kPer];
+            unpack_vec<ET>(graw[u], g);
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) {
+                if (rows[j] < 0)
+                    continue;
+                float yv[kPer], o[kPer];
+                unpack_vec<ET>(yraw[u][j], yv);
+#pragma unroll
+                for (int q = 0; q < kPer; ++q) {
+                    dot[j] = fmaf(g[q], yv[q], dot[j]);
+                    o[q] = w[j] * g[q];
+                }
+                store_vec<ET>(d_yp + (size_t)rows[j] * d + (size_t)v * kPer, o);
+            }
         }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kMaxK; ++j) {
         if (j >= k)
             break;
         const float s = wave_sum_f(dot[j]);
@@ -337,19 +381,6 @@ __global__ __launch_bounds__(256) void moe_seg_transpose_bf16_kernel(const uint1
 // they are added.
 constexpr int kUnpVec = 1;
 constexpr int kUnpTok = 2;
-
-template <typename ET>
-__device__ __forceinline__ void unpack_vec(const uint4& raw, float* f)  // 16 bytes
-{
-    if constexpr (ET::kBytes == 2) {
-        unpack8(raw, f, bf16_t{});
-    } else {
-        f[0] = __uint_as_float(raw.x);
-        f[1] = __uint_as_float(raw.y);
-        f[2] = __uint_as_float(raw.z);
-        f[3] = __uint_as_float(raw.w);
-    }
-}
 
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_unpermute_bwd_kernel(const typename ET::storage* __restrict__ dx_perm,
@@ -612,12 +643,20 @@ extern "C" hipError_t moe_launch_combine_bwd(int dtype, const void* dy, const vo
 {
     using namespace moe;
     const dim3 grid((T + 3) / 4), block(256);
-    if (dtype == 0)
-        moe_combine_bwd_kernel<f32_t><<<grid, block, 0, stream>>>((const float*)dy, (const float*)y_perm, slot, topk_w,
-                                                                  T, d, k, max_rows, (float*)d_yp, d_w);
+    if (dtype == 0 && k <= 2)
+        moe_combine_bwd_kernel<f32_t, 2><<<grid, block, 0, stream>>>((const float*)dy, (const float*)y_perm, slot,
+                                                                     topk_w, T, d, k, max_rows, (float*)d_yp, d_w);
+    else if (dtype == 0)
+        moe_combine_bwd_kernel<f32_t, 8><<<grid, block, 0, stream>>>((const float*)dy, (const float*)y_perm, slot,
+                                                                     topk_w, T, d, k, max_rows, (float*)d_yp, d_w);
+    else if (k <= 2)
+        moe_combine_bwd_kernel<bf16_t, 2><<<grid, block, 0, stream>>>((const uint16_t*)dy, (const uint16_t*)y_perm,
+                                                                      slot, topk_w, T, d, k, max_rows,
+                                                                      (uint16_t*)d_yp, d_w);
     else
-        moe_combine_bwd_kernel<bf16_t><<<grid, block, 0, stream>>>((const uint16_t*)dy, (const uint16_t*)y_perm, slot,
-                                                                   topk_w, T, d, k, max_rows, (uint16_t*)d_yp, d_w);
+        moe_combine_bwd_kernel<bf16_t, 8><<<grid, block, 0, stream>>>((const uint16_t*)dy, (const uint16_t*)y_perm,
+                                                                      slot, topk_w, T, d, k, max_rows,
+                                                                      (uint16_t*)d_yp, d_w);
     return hipGetLastError();
 }
 
