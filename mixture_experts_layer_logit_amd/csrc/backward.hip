@@ -72,6 +72,16 @@ __device__ __forceinline__ void unpack_vec(const uint4& raw, float* f)  // 16 by
     }
 }
 
+// 16 bytes of a stream read once (non-temporal: no allocation that would
+// displace reused or dirty lines).
+template <typename T>
+__device__ __forceinline__ uint4 nt_load16(const T* p)
+{
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v q = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(q.x, q.y, q.z, q.w);
+}
+
 // One wavefront per token.  Lane l owns 16-byte vectors l, l+64, ... of the
 // row; a dot product is the lanes' partial sums (each in vector order) added
 // by a fixed shuffle tree.  Slots at or past max_rows count as dropped.  Two
@@ -109,7 +119,7 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_kernel(const typename ET:
         for (int u = 0; u < kU; ++u) {
             const int v = v0 + u * kWave;
             if (v < nvec)
-                graw[u] = gsrc[v];
+                graw[u] = nt_load16(gsrc + v);
         }
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(256) void moe_combine_bwd_kernel(const typename ET:
             for (int u = 0; u < kU; ++u) {
                 const int v = v0 + u * kWave;
                 if (v < nvec)
-                    yraw[u][j] = ysrc[v];
+                    yraw[u][j] = nt_load16(ysrc + v);
             }
         }
         // keep the uses below the loads (otherwise each load is waited on alone)
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(256) void moe_seg_transpose_bf16_kernel(const uint1
         const int r = __shfl(row, 8 * pg + i);
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (r >= 0)
-            v = *reinterpret_cast<const uint4*>(src + (size_t)r * C + c0 + 8 * cg);
+            v = nt_load16(src + (size_t)r * C + c0 + 8 * cg);
         w[i][0] = v.x;
         w[i][1] = v.y;
         w[i][2] = v.z;
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(256) void moe_unpermute_bwd_kernel(const typename E
                 for (int u = 0; u < kUnpVec; ++u) {
                     const int v = v0 + u * kWave + lane;
                     if (v < nvec)
-                        raw[i][h][u] = src[v];
+                        raw[i][h][u] = nt_load16(src + v);
                 }
             }
 #pragma unroll
