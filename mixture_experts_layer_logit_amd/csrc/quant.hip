@@ -77,6 +77,8 @@ __global__ __launch_bounds__(256) void moe_quantize_fp8_kernel(const typename ET
 // row: the row is read once into registers (V 16-byte vectors per thread),
 // the block finds max|v| (wavefront shuffles, then the 4 wavefronts through
 // LDS) and writes the codes from the registers, so the row crosses HBM once.
+// The loads are non-temporal (the row is not read again) and unconditional
+// (index clamped; vectors past the row are zeroed after the load).
 template <int V>
 __global__ __launch_bounds__(256) void moe_quantize_fp8_bf16_kernel(const uint16_t* __restrict__ src, int K,
                                                                     uint8_t* __restrict__ codes,
@@ -90,7 +92,9 @@ __global__ __launch_bounds__(256) void moe_quantize_fp8_bf16_kernel(const uint16
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int c = threadIdx.x + 256 * i;
-        buf[i] = c < nvec ? row[c] : make_uint4(0u, 0u, 0u, 0u);
+        typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+        const u32x4v q = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(row + min(c, nvec - 1)));
+        buf[i] = c < nvec ? make_uint4(q.x, q.y, q.z, q.w) : make_uint4(0u, 0u, 0u, 0u);
     }
     float amax = 0.0f;
 #pragma unroll
