@@ -19,7 +19,7 @@
 // Slots at or past the row count (T*k) are treated as dropped.  With y_add
 // (the shared expert's output, industry overview page, "MoE未來重點研究方向"
 // item 4: DeepSeekMoE's shared experts) the sum starts from y_add[t]: every
-// token gets it with weight one.
+// token gets it with weight one (its row is read once too, non-temporally).
 #include "common.h"
 
 namespace moe {
@@ -55,18 +55,27 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const typename ET::sto
             acc[u][q] = 0.0f;
     if (y_add) {
         const uint4* src = reinterpret_cast<const uint4*>(y_add + (size_t)t * d);
+        uint4 ra[kVec];
 #pragma unroll
         for (int u = 0; u < kVec; ++u) {
             const int v = v0 + u * kWave + lane;
             if (v < nvec) {
-                const uint4 raw = src[v];
+                typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+                const u32x4v q = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(src + v));
+                ra[u] = make_uint4(q.x, q.y, q.z, q.w);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < nvec) {
                 if constexpr (ET::kBytes == 2) {
-                    unpack8(raw, acc[u], bf16_t{});
+                    unpack8(ra[u], acc[u], bf16_t{});
                 } else {
-                    acc[u][0] = __uint_as_float(raw.x);
-                    acc[u][1] = __uint_as_float(raw.y);
-                    acc[u][2] = __uint_as_float(raw.z);
-                    acc[u][3] = __uint_as_float(raw.w);
+                    acc[u][0] = __uint_as_float(ra[u].x);
+                    acc[u][1] = __uint_as_float(ra[u].y);
+                    acc[u][2] = __uint_as_float(ra[u].z);
+                    acc[u][3] = __uint_as_float(ra[u].w);
                 }
             }
         }
