@@ -184,7 +184,7 @@ def test_permute(name):
 
 
 @pytest.mark.parametrize("kind", ["heavy_drop", "one_expert", "empty_experts", "max_experts", "k8_capacity",
-                                  "ragged_T"])
+                                  "ragged_T", "scan_in_scatter_limit", "scan_launched"])
 def test_permute_edges(kind):
     print(f"[permute-edge] {kind}", flush=True)
     base = moe_inputs.get("mixtral_s")
@@ -206,6 +206,12 @@ def test_permute_edges(kind):
         case = base.with_(E=40, k=8, cf=1.0, T=777)
         idx = oracle.route(RNG.standard_normal((case.T, case.E)).astype(np.float32) * np.linspace(
             1, 3, 40, dtype=np.float32), case.k)[0]
+    elif kind in ("scan_in_scatter_limit", "scan_launched"):
+        # 256-token chunks x 1024 experts: 64 chunks is the most for which the
+        # scatter kernel scans the chunk counts itself; 65 launches the scan
+        case = base.with_(E=1024, k=2, cf=1.0, T=16384 if kind == "scan_in_scatter_limit" else 16385)
+        idx = oracle.route(RNG.standard_normal((case.T, case.E)).astype(np.float32) * np.linspace(
+            1, 2, case.E, dtype=np.float32), case.k)[0]
     else:
         case = base.with_(T=257)
         idx = oracle.route(RNG.standard_normal((case.T, case.E)).astype(np.float32), case.k)[0]
