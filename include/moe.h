@@ -94,7 +94,7 @@ typedef struct {
     int32_t dtype;            /* MOE_F32 | MOE_BF16 */
     int32_t normalize;        /* 0: softmax(z); 1: softmax(lambda * standardise(z)) */
     float lambda;             /* finite and > 0 when normalize == 1 */
-    float capacity_factor;    /* <= 0: dropless; > 0: capacity C = ceil(cf*T*k/E) */
+    float capacity_factor;    /* <= 0: dropless; > 0: capacity C = ceil(cf*T*k/E), see moe_capacity */
 } moe_problem;
 
 /* Optional outputs of moe_forward; each field may be NULL (the library then
@@ -114,10 +114,16 @@ const char* moe_status_string(moe_status s);
 /* Message of the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);
 
-/* Expert capacity of a problem: C = ceil(cf * T * k / E) evaluated in double
- * (cf > 0), or -1 when dropless (cf <= 0).  Tokens beyond C on one expert are
- * dropped and contribute zero; the caller's residual connection carries them
- * (Megatron-Core page, "MoE负载均衡的挑战与应对" and its Q&A).  Host only. */
+/* Expert capacity of a problem: C = ceil(cf * T * k / E) (cf > 0), or -1
+ * when dropless (cf <= 0).  cf is the fp32 value held in the problem, and C
+ * is the exact ceiling for that value (the product and quotient are formed in
+ * double, where they are exact or cannot cross an integer): a factor that is
+ * not exact in binary rounds from its fp32 neighbour, so cf = 0.3f with
+ * T*k/E = 100 gives C = 31 (0.3f is slightly above 0.3), while dyadic factors
+ * such as 0.25 or 1.25 give the decimal result.  Tokens beyond C on one
+ * expert are dropped and contribute zero; the caller's residual connection
+ * carries them (Megatron-Core page, "MoE负载均衡的挑战与应对" and its Q&A).
+ * Host only. */
 moe_status moe_capacity(const moe_problem* p, int32_t* C);
 
 /* Bytes of workspace that suffice for every entry point of this problem
@@ -334,7 +340,9 @@ moe_status moe_fp8_workspace_size(const moe_problem* p, size_t* bytes);
 
 /* FP8 first expert layer: as moe_expert_up, with aq the codes of x
  * (src_token given, rows gathered on the fly) or of x_perm (src_token NULL)
- * and as their row scales (indexed like aq's rows). */
+ * and as their row scales (indexed like aq's rows).  The gather addresses
+ * the codes with 32-bit byte offsets: with src_token, T*d must stay below
+ * 0xF0000000 bytes, else MOE_ERR_UNSUPPORTED (pass permuted codes). */
 moe_status moe_expert_up_fp8(const moe_problem* p, const uint8_t* aq, const float* as, const int32_t* src_token,
                              const int32_t* offsets, const uint8_t* W1q, const float* w1s, void* h, void* ws,
                              size_t ws_bytes, void* stream);
@@ -347,7 +355,9 @@ moe_status moe_expert_down_fp8(const moe_problem* p, const uint8_t* hq, const fl
 
 /* The whole layer with FP8 experts: route and permute as moe_forward, then
  * quantise x per token, FP8 up-projection, quantise h per row, FP8
- * down-projection, combine.  Needs ws_bytes >= moe_fp8_workspace_size. */
+ * down-projection, combine.  Needs ws_bytes >= moe_fp8_workspace_size.  The
+ * up-projection gathers the token codes (T*d bytes) with 32-bit offsets:
+ * T*d >= 0xF0000000 returns MOE_ERR_UNSUPPORTED. */
 moe_status moe_forward_fp8(const moe_problem* p, const void* x, const void* Wg, const float* bg, const uint8_t* W1q,
                            const float* w1s, const uint8_t* W2q, const float* w2s, void* y, float* logits,
                            const moe_route_info* info, void* ws, size_t ws_bytes, void* stream);

@@ -335,6 +335,14 @@ moe_status check_fp8(const moe_problem* p)
     return MOE_OK;
 }
 
+// Whether the FP8 codes of x (one byte per value) can be read through
+// src_token: the gather addresses them with 32-bit byte offsets, like x in
+// the bf16 path.
+bool gather_ok_fp8(const moe_problem* p)
+{
+    return (unsigned long long)p->T * p->d < kGatherBytes;
+}
+
 // The bf16 layout, then the codes and scales of x and h.
 struct LayoutFp8 {
     Layout base;
@@ -765,8 +773,12 @@ moe_status moe_expert_up_fp8(const moe_problem* p, const uint8_t* aq, const floa
         return ok();
     CHECK(check_ptr(aq, src_token ? "xq" : "x_perm codes", 16));
     CHECK(check_ptr(as, "activation scales", 4));
-    if (src_token)
+    if (src_token) {
         CHECK(check_ptr(src_token, "src_token", 4));
+        if (!gather_ok_fp8(p))
+            return fail(MOE_ERR_UNSUPPORTED, "x codes of %llu bytes are too large to gather; pass permuted codes",
+                        (unsigned long long)p->T * p->d);
+    }
     CHECK(check_ptr(offsets, "offsets", 4));
     CHECK(check_ptr(W1q, "W1q", 16));
     CHECK(check_ptr(w1s, "w1s", 4));
@@ -805,6 +817,9 @@ moe_status moe_forward_fp8(const moe_problem* p, const void* x, const void* Wg, 
     CHECK(check_fp8(p));
     if (p->T == 0)
         return ok();
+    if (!gather_ok_fp8(p))
+        return fail(MOE_ERR_UNSUPPORTED, "x codes of %llu bytes are too large to gather (limit 0xF0000000 bytes)",
+                    (unsigned long long)p->T * p->d);
     CHECK(check_ptr(x, "x", 16));
     CHECK(check_ptr(W1q, "W1q", 16));
     CHECK(check_ptr(w1s, "w1s", 4));

@@ -206,8 +206,17 @@ def route(z32, k, normalize_flag=False, lam=1.0, want_p=False):
 
 
 def capacity(T, E, k, cf) -> int:
-    """Expert capacity, or -1 for no limit."""
-    return int(_load().orc_capacity(int(T), int(E), int(k), float(cf)))
+    """Expert capacity C = ceil(cf * T * k / E), or -1 for no limit (cf <= 0).
+
+    The capacity factor is a single-precision number (the layer's problem
+    statement holds it as fp32), so a Python float is first rounded to the
+    nearest fp32 value, and C is the exact ceiling for that value: fp32(0.3)
+    is slightly above 0.3, so T*k/E = 100 gives C = 31 (a dyadic factor such
+    as 0.25 or 1.25 lands on integers exactly).  The C routine evaluates the
+    product and quotient in double, which is exact here (a 24-bit factor times
+    T*k < 2^27 fits in 53 bits, and a quotient that is not an integer lies
+    further from one than a double rounding can move it)."""
+    return int(_load().orc_capacity(int(T), int(E), int(k), float(np.float32(cf))))
 
 
 def dispatch(topk_idx, E, C):

@@ -34,8 +34,13 @@ def test_status_strings():
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
 
 
+# The last rows use factors that are not exact in fp32 at shapes where the
+# decimal factor times T*k/E is an integer: both sides take the fp32 value.
 @pytest.mark.parametrize("T,E,k,cf", [(4096, 16, 2, 1.25), (10, 3, 1, 1.0), (8, 4, 2, 1e-30), (4096, 8, 2, 0.0),
-                                      (4096, 8, 2, -1.0), (16384, 512, 2, 0.25), (1, 1, 1, 3.0)])
+                                      (4096, 8, 2, -1.0), (16384, 512, 2, 0.25), (1, 1, 1, 3.0),
+                                      (100, 1, 1, 0.1), (100, 1, 1, 0.3), (100, 1, 1, 0.7), (100, 1, 1, 1.1),
+                                      (1000, 10, 1, 0.3), (10, 1, 1, 0.3), (1000, 4, 2, 0.3), (600, 8, 2, 0.7),
+                                      (1 << 24, 1024, 8, 0.1)])
 def test_capacity_matches_oracle(T, E, k, cf):
     p = moe.problem(T, 64, E, k, 64, cf=cf)
     assert moe.moe_capacity(p) == oracle.capacity(T, E, k, cf)
@@ -220,6 +225,29 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert lib.moe_expert_down_fp8(pp, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_fp8_gather_limited_to_32_bit_offsets():
+    # 2^20 tokens x 4096 codes = 4 GiB: the token codes cannot be gathered
+    # through src_token (32-bit byte offsets); the limit is T*d < 0xF0000000
+    lib = moe.load()
+    big = moe.problem(1 << 20, 4096, 8, 2, 256)
+    pb = ctypes.byref(big)
+    assert lib.moe_expert_up_fp8(pb, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert b"gather" in lib.moe_last_error()
+    ws = moe.moe_fp8_workspace_size(big)
+    assert lib.moe_forward_fp8(pb, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws,
+                               None) == moe.MOE_ERR_UNSUPPORTED
+    # without src_token the codes are permuted rows, addressed per tile: accepted past validation
+    # (the workspace check is the next one to fail here)
+    assert lib.moe_expert_up_fp8(pb, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == \
+        moe.MOE_ERR_WORKSPACE
+    # just below the limit the gather is accepted
+    ok = moe.problem(983040 - 1, 4096, 8, 2, 256)   # (983040 - 1) * 4096 < 0xF0000000
+    po = ctypes.byref(ok)
+    assert lib.moe_expert_up_fp8(po, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == \
+        moe.MOE_ERR_WORKSPACE
+
+
 def backward_formula(T, d, E, k, F, act, b):
     r = lambda n: (n + 255) // 256 * 256
     n1 = 2 * F if act == "swiglu" else F
@@ -298,3 +326,4 @@ def test_backward_entry_points_reject_bad_arguments():
         moe.MOE_OK
     assert lib.moe_backward(p0p, None, None, None, None, None, None, None, None, None, None, None, None, None, None,
                             None, 0, None) == moe.MOE_ERR_INVALID_ARG
+

@@ -10,8 +10,11 @@ Bars:
     bf16 h while the oracle quantises the exact h; where the two straddle an
     E4M3 rounding boundary (the bf16 store moves h by <= 2^-9 relative, about
     1/32 of an E4M3 step) a code differs by one step (<= 2^-3 relative) and
-    moves each output by that step times one weight.  A few such flips per
-    row stay below 3e-2 of max|y|; routing (bf16 gate) is bit-exact.
+    moves each output by that step times one weight.  Each output element is
+    held to the bf16 bar (2e-2 of max|y|) plus the largest change such flips
+    can make to it, computed from the oracle's exact h (tests/_fp8_bound.py);
+    where no code of h can straddle, that is the plain bf16 bar.  Routing
+    (bf16 gate) is bit-exact.
 Inputs come from the seeded generator and the oracle (including every code
 and scale fed to the GPU GEMMs), never from the GPU.
 """
@@ -22,14 +25,15 @@ import torch
 import mixture_experts_layer_logit_amd as moe
 import moe_inputs
 import oracle
-from _gpu import dev, host, maxrel, problem_of
+from _gpu import TOL, dev, host, maxrel, problem_of, to_f64
+from _fp8_bound import fp8_code_allowance
+import _tiles
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 RNG = np.random.default_rng(31337)
 TOL_GEMM = 2e-2
-TOL_LAYER = 3e-2
 
 # Small FP8 workloads (d and F multiples of 128), ragged segments and drops.
 FP8_SMALL = {
@@ -229,9 +233,20 @@ def test_forward_fp8(name):
     act = oracle.SWIGLU if case.act == "swiglu" else oracle.RELU
     ref = oracle.forward_tokens_fp8(inp["x"], inp["W1q"], inp["w1s"], inp["W2q"], inp["w2s"], idx, w,
                                     disp["slot"], act, case.F)
-    assert maxrel(y, ref) <= TOL_LAYER
+    check_fp8_layer(case, inp, w, disp, y, ref)
     gone = np.all(disp["slot"] < 0, axis=1)
     assert not y[gone].any()
+
+
+def check_fp8_layer(case, inp, w, disp, got, ref, tokens=None):
+    """Every element within the bf16 bar plus its derived allowance for E4M3
+    codes of h that the GPU's bf16 h may round the other way."""
+    allow = fp8_code_allowance(case, inp["x"], inp["W1q"], inp["w1s"], inp["W2q"], inp["w2s"], w, disp, tokens)
+    over = np.abs(to_f64(got) - ref) - (TOL["bf16"] * np.max(np.abs(ref)) + allow)
+    err = maxrel(got, ref)
+    assert np.all(over <= 0), f"max-abs-rel {err:.3e}; {float(over.max()):.3e} beyond the bound"
+    print(f"  max-abs-rel {err:.2e}, mean allowance {float(allow.mean() / max(np.max(np.abs(ref)), 1e-30)):.2e} "
+          f"of max|y|", flush=True)
 
 
 def test_forward_fp8_full_size_sampled():
@@ -242,7 +257,11 @@ def test_forward_fp8_full_size_sampled():
     idx, w, disp = routing(case, inp)
     y, gidx, gslot = run_forward_fp8(case, inp)
     assert np.array_equal(gidx, idx) and np.array_equal(gslot, disp["slot"])
-    toks = np.sort(np.random.default_rng(5).choice(case.T, 12, replace=False)).astype(np.int32)
+    # tokens whose rows reach every m-tile of every expert and every row of
+    # the smallest tile that the last round of each GEMM splits along K
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    toks = _tiles.covering_tokens(disp["offsets"], disp["src_token"], [(case.F + 127) // 128, (case.d + 255) // 256],
+                                  G, extra=np.random.default_rng(5).choice(case.T, 12, replace=False))
     ref = oracle.forward_tokens_fp8(inp["x"], inp["W1q"], inp["w1s"], inp["W2q"], inp["w2s"], idx, w,
                                     disp["slot"], oracle.SWIGLU, case.F, tokens=toks)
-    assert maxrel(y[toks], ref) <= TOL_LAYER
+    check_fp8_layer(case, inp, w, disp, y[toks], ref, tokens=toks)

@@ -15,6 +15,7 @@ import moe_inputs
 import oracle
 from _gpu import TOL, TOPK_W_ATOL, dev, host, maxrel, problem_of, run_forward, to_f64, torch_dtype
 from _margins import exact_sum_certified, logit_eps, unstable_keys
+import _tiles
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -184,10 +185,21 @@ def test_permute(name):
 
 
 @pytest.mark.parametrize("kind", ["heavy_drop", "one_expert", "empty_experts", "max_experts", "k8_capacity",
-                                  "ragged_T", "scan_in_scatter_limit", "scan_launched"])
+                                  "ragged_T", "scan_in_scatter_limit", "scan_launched", "cf_not_dyadic"])
 def test_permute_edges(kind):
     print(f"[permute-edge] {kind}", flush=True)
     base = moe_inputs.get("mixtral_s")
+    if kind == "cf_not_dyadic":
+        # fp32(0.3) * 600 * 2 / 8 = 45.0000018: the capacity is 46, one above
+        # the decimal product; skewed logits make the clip bite on most experts
+        case = base.with_(cf=0.3)
+        assert oracle.capacity(case.T, case.E, case.k, case.cf) == 46 == moe.moe_capacity(problem_of(case))
+        idx = oracle.route(RNG.standard_normal((case.T, case.E)).astype(np.float32) + np.linspace(
+            1, 0, case.E, dtype=np.float32), case.k)[0]
+        o = check_permute(case, idx, moe_inputs.f32_to_bf16_bits(
+            RNG.standard_normal((case.T, case.d)).astype(np.float32)))
+        assert int(np.sum(o["counts"] > 46)) >= 4 and o["P"] < case.T * case.k
+        return
     if kind == "heavy_drop":
         case = base.with_(cf=0.25)
         idx = oracle.route(RNG.standard_normal((case.T, case.E)).astype(np.float32) + np.linspace(2, 0, case.E,
@@ -278,6 +290,11 @@ SPLIT_CASES = {
     # name: (dtype, act, T, d, E, k, F, segment rows)
     "large_relu": ("bf16", "relu", 1024, 1024, 4, 2, 1536, [700, 300, 512, 536]),
     "large_ragged": ("bf16", "relu", 1024, 1024, 4, 2, 1024, [1, 0, 1019, 1000]),
+    # the SwiGLU epilogue on the large tile: gate and up columns paired, a
+    # partly filled last column tile (F = 320 is 2.5 tiles of 128 outputs),
+    # a ragged K (d = 640 is 20 slices of 32)
+    "large_swiglu": ("bf16", "swiglu", 1024, 512, 4, 2, 768, [700, 300, 512, 536]),
+    "large_swiglu_ragged": ("bf16", "swiglu", 1024, 640, 4, 2, 320, [1, 0, 1019, 1028]),
     "medium_swiglu": ("bf16", "swiglu", 512, 512, 4, 2, 512, [300, 0, 257, 300]),
     "small_relu": ("bf16", "relu", 512, 1024, 16, 2, 512, [64] * 14 + [1, 63]),
     "f32_relu": ("f32", "relu", 512, 512, 4, 1, 512, [130, 0, 200, 150]),
@@ -391,6 +408,10 @@ def test_forward_small(name):
 
 
 def sample_tokens(case, inp, disp, n=24):
+    """Random tokens, the first and last, hot and dropped ones; on the large
+    tile (bf16, at least 512 rows per expert on average) also tokens whose
+    rows reach every m-tile of every expert, and every row of the smallest
+    tile that the last round of each expert GEMM splits along K."""
     T = case.T
     g = np.random.default_rng(case.seed)
     picks = {0, T - 1}
@@ -399,7 +420,19 @@ def sample_tokens(case, inp, disp, n=24):
         picks.update(inp["hot_tokens"][:4].tolist())
     dropped_any = np.nonzero(np.any(disp["slot"] < 0, axis=1))[0]
     picks.update(dropped_any[:4].tolist())
+    if uses_large_tile(case):
+        G = torch.cuda.get_device_properties(0).multi_processor_count
+        ntns = [(case.F + 127) // 128 if case.act == "swiglu" else (case.F + 255) // 256, (case.d + 255) // 256]
+        picks.update(_tiles.covering_tokens(disp["offsets"], disp["src_token"], ntns, G).tolist())
     return np.array(sorted(picks), np.int32)
+
+
+def uses_large_tile(case):
+    rows = case.T * case.k // case.E
+    C = oracle.capacity(case.T, case.E, case.k, case.cf)
+    if C >= 0:
+        rows = min(rows, C)
+    return case.dtype == "bf16" and rows >= 512
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -439,7 +472,7 @@ def test_forward_deterministic_and_workspace_independent():
 
 
 @pytest.mark.parametrize("kind", ["T1", "E_equals_k", "k1", "single_expert", "heavy_drop", "all_to_one",
-                                  "fp32_swiglu_norm"])
+                                  "fp32_swiglu_norm", "cf_not_dyadic"])
 def test_forward_edges(kind):
     print(f"[forward-edge] {kind}", flush=True)
     base = moe_inputs.get("mixtral_s").with_(bias="none")
@@ -456,9 +489,16 @@ def test_forward_edges(kind):
         case = base.with_(name="edge_drop", cf=0.25, normalize=True)
     elif kind == "all_to_one":
         case = base.with_(name="edge_one", cf=0.5)
+    elif kind == "cf_not_dyadic":
+        # capacity from fp32(0.7): 0.7 * 600 * 2 / 8 = 105 in decimal, C = 105
+        # from fp32(0.7) = 0.69999999; the Zipf bias of mixtral_s makes it bite
+        case = moe_inputs.get("mixtral_s").with_(name="edge_cf07", cf=0.7)
+        assert oracle.capacity(case.T, case.E, case.k, case.cf) == moe.moe_capacity(problem_of(case)) == 105
     else:
         case = base.with_(name="edge_f32", dtype="f32", x_std=0.5, normalize=True, lam=2.0, cf=1.0, T=300)
-    inp = moe_inputs.make(case)
+    # the Zipf-biased variant reuses mixtral_s's calibrated gate bias
+    inp = moe_inputs.make(case, bias_override=moe_inputs.zipf_bias(moe_inputs.get("mixtral_s"))
+                          if case.bias == "zipf" else None)
     if kind == "all_to_one":
         # every token's logits favour experts 5 then 2 (zero gate weight, fixed bias)
         inp["Wg"] = np.zeros_like(inp["Wg"])

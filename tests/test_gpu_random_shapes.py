@@ -36,6 +36,7 @@ import moe_inputs
 import oracle
 from _gpu import TOL, TOPK_W_ATOL, dev, host, maxrel, problem_of, run_train, to_f64, torch_dtype, within
 from _margins import logit_eps, relu_unpinned
+from _fp8_bound import fp8_code_allowance
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -175,54 +176,6 @@ def random_fp8_case(i):
         x_std=1.0, w_std=0.05, wg_std=0.05)
 
 
-def fp8_code_allowance(case, inp, W1q, w1s, W2q, w2s, w, disp):
-    """Per-token allowance [T, d] for the FP8 layer: the GPU quantises its
-    bf16 h, within 2^-9 (one bf16 rounding) plus 2^-16 (fp32 arithmetic, far
-    below it) relative of the exact h, while the oracle quantises the exact
-    h.  A code can differ only where [|v|(1 - rel), |v|(1 + rel)] (v = h /
-    2^e in the row's scale) holds a rounding midpoint of the E4M3 grid; it
-    then moves by at most the gap between the two neighbours, times the row
-    scale.  A row whose scale exponent itself is ambiguous gets twice the
-    coarser gap on every element.  The change reaches y[t] through w_j |W2|
-    (dequantised)."""
-    xq, xs = oracle.quant_rows_fp8(inp["x"])
-    src = disp["src_token"]
-    P, F, d = disp["P"], case.F, case.d
-    out = np.zeros((case.T, d))
-    if P == 0:
-        return out
-    _, h = oracle.ffn_rows_fp8(xq[src], xs[src], disp["offsets"], W1q, w1s, W2q, w2s, act_code(case), F,
-                               want_h=True)
-    grid = np.abs(oracle.e4m3_decode(np.arange(128, dtype=np.uint8)))
-    mags = np.unique(grid[np.isfinite(grid)])  # the grid, 0 .. 448 (the NaN code left out)
-    mids = (mags[1:] + mags[:-1]) / 2
-    gaps = mags[1:] - mags[:-1]
-    rel = 2.0 ** -9 + 2.0 ** -16
-    amax = np.max(np.abs(h), axis=1)
-    e = np.array([oracle.fp8_scale_exp(a) for a in amax])
-    ambiguous = np.array([oracle.fp8_scale_exp(a * (1 - rel)) != oracle.fp8_scale_exp(a * (1 + rel)) for a in amax])
-    s = 2.0 ** e
-    a = np.abs(h) / s[:, None]
-    lo = np.searchsorted(mids, a * (1 - rel), side="left")
-    hi = np.searchsorted(mids, a * (1 + rel), side="right")
-    coef = np.where(hi > lo, gaps[np.minimum(lo, gaps.size - 1)], 0.0) * s[:, None]
-    coarse = gaps[np.minimum(np.searchsorted(mids, a), gaps.size - 1)] * s[:, None] * 2
-    coef[ambiguous] = 2 * coarse[ambiguous]
-    per_row = np.zeros((P, d))
-    offs = disp["offsets"]
-    for e in range(case.E):
-        r0, r1 = offs[e], offs[e + 1]
-        if r1 > r0:
-            W2d = np.abs(oracle.e4m3_decode(W2q[e]) * np.asarray(w2s[e], np.float64)[:, None])  # [d, F]
-            per_row[r0:r1] = coef[r0:r1] @ W2d.T
-    for t in range(case.T):
-        for j in range(case.k):
-            r = disp["slot"][t, j]
-            if r >= 0:
-                out[t] += w[t, j] * per_row[r]
-    return out
-
-
 @pytest.mark.parametrize("i", range(N_FP8_CASES))
 def test_random_shape_fp8(i):
     case = random_fp8_case(i)
@@ -254,7 +207,7 @@ def test_random_shape_fp8(i):
     err = maxrel(got, ref)
     # the bf16 layer bar, plus the allowance for E4M3 codes of h that the
     # GPU's bf16 h may round the other way
-    allow = fp8_code_allowance(case, inp, W1q, w1s, W2q, w2s, w, disp)
+    allow = fp8_code_allowance(case, inp["x"], W1q, w1s, W2q, w2s, w, disp)
     over = np.abs(to_f64(got) - ref) - (TOL["bf16"] * np.max(np.abs(ref)) + allow)
     assert np.all(over <= 0), f"max-abs-rel {err:.3e}; {float(over.max()):.3e} beyond the bound"
     gone = np.all(disp["slot"] < 0, axis=1)

@@ -193,6 +193,21 @@ def test_capacity_formula():
     assert oracle.capacity(4096, 8, 2, 0.25) == 256
 
 
+# The capacity factor is a single-precision number; C is the exact ceiling of
+# fp32(cf) * T * k / E, checked here with rational arithmetic (no floating
+# point).  Factors that are not dyadic (0.1, 0.3, 0.7, 1.1, 1/3) land just
+# above or below an integer, where a product or quotient rounded the wrong
+# way would move C by one.
+@pytest.mark.parametrize("T,E,k,cf", [(100, 1, 1, 0.3), (1000, 10, 1, 0.3), (10, 1, 1, 0.3), (100, 1, 1, 0.1),
+                                      (100, 1, 1, 0.7), (100, 1, 1, 1.1), (1000, 4, 2, 0.3), (300, 3, 2, 1 / 3),
+                                      (4096, 16, 2, 1.25), (16384, 512, 2, 0.25), (1 << 24, 1024, 8, 0.7),
+                                      (777, 40, 8, 1.0), (5, 7, 3, 2.2)])
+def test_capacity_is_exact_ceiling_of_fp32_factor(T, E, k, cf):
+    from fractions import Fraction
+    exact = Fraction(float(np.float32(cf))) * T * k / E
+    assert oracle.capacity(T, E, k, cf) == math.ceil(exact)
+
+
 def brute_dispatch(idx, E, C):
     T, k = idx.shape
     slot = np.full((T, k), -1, np.int64)
