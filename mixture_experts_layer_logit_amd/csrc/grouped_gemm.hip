@@ -50,6 +50,8 @@
 //  * SwiGLU: a wave's N range holds its gate columns then the matching up
 //    columns, so gate and up values of one output meet in the same lane.
 //  * Rows past a segment's end are computed on zeros and not stored.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -1004,9 +1006,17 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         // MFMA operand fragments of one k-step, double-buffered in registers
         // so that a k-step's LDS reads can be issued before the previous
         // k-step's MFMAs.
+        // LC (a std::integral_constant) is the number of this wave's row
+        // fragments that hold rows of the segment: all kFM except in an
+        // expert's last, partly filled m-tile, where fragments wholly past
+        // the segment's end are neither read nor multiplied (their rows are
+        // never stored).  Each count has its own copy of the K loop below, so
+        // the full-tile loop keeps its schedule.
         Frag<S> fr0, fr1;
-        auto read_frags = [&](const uint8_t* buf, int kk, Frag<S>& f) {
+        auto read_frags = [&](const uint8_t* buf, int kk, Frag<S>& f, auto LC) {
+            constexpr int L = decltype(LC)::value;
             auto rd = [&](uint32_t off) { return *reinterpret_cast<const i32x4*>(buf + off); };
+            if constexpr (L > 0) {
 #pragma unroll
             for (int j = 0; j < S::kFN; ++j) {
                 if constexpr (WT) {
@@ -1021,8 +1031,9 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                     f.a[j] = rd(rdB[kk][0] + j * 32 * S::RB);
                 }
             }
+            }
 #pragma unroll
-            for (int i = 0; i < S::kFM; ++i) {
+            for (int i = 0; i < L; ++i) {
                 if constexpr (S::kChunks == 2) {
                     f.b[i].lo = rd(rdA[kk][0] + i * 32 * S::RB);
                     f.b[i].hi = rd(rdA[kk][1] + i * 32 * S::RB);
@@ -1031,9 +1042,10 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 }
             }
         };
-        auto mfmas = [&](const Frag<S>& f) {
+        auto mfmas = [&](const Frag<S>& f, auto LC) {
+            constexpr int L = decltype(LC)::value;
 #pragma unroll
-            for (int i = 0; i < S::kFM; ++i)
+            for (int i = 0; i < L; ++i)
 #pragma unroll
                 for (int j = 0; j < S::kFN; ++j) {
                     if constexpr (ET::kBytes == 1) {
@@ -1064,7 +1076,8 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         // the last k-step's MFMAs.  Buffers are distinct LDS arrays known at
         // compile time.
         static_assert(S::kKSteps == 2 || S::kKSteps == 4, "2 or 4 k-steps per slice");
-        auto slice = [&](int kt, const uint8_t* cur, int cur_stage, const uint8_t* nxt) {
+        auto slice = [&](int kt, const uint8_t* cur, int cur_stage, const uint8_t* nxt, auto LC) {
+            constexpr int L = decltype(LC)::value;
             if constexpr (S::kChunks == 2) {
                 // FP8: a k-step's fragments are 32 bytes per operand block,
                 // too wide to double-buffer beside 128 accumulators; they are
@@ -1073,9 +1086,9 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 // k-steps' reads above the MFMAs, which would need a second
                 // register set for the fragments)
                 static_assert(S::kKSteps == 2, "FP8 slices are 128 bytes: 2 k-steps");
-                mfmas(fr0);
+                mfmas(fr0, LC);
                 __builtin_amdgcn_sched_barrier(0);
-                read_frags(cur, 1, fr0);
+                read_frags(cur, 1, fr0, LC);
                 __builtin_amdgcn_sched_barrier(0);
                 const bool more = kt + 1 < k1;
                 if (more) {
@@ -1084,9 +1097,9 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                     if (kt + S::S < k1)
                         issue(kt + S::S, cur_stage);
                 }
-                mfmas(fr0);  // one call site: the accumulators keep one register set
+                mfmas(fr0, LC);  // one call site: the accumulators keep one register set
                 __builtin_amdgcn_sched_barrier(0);
-                read_frags(nxt, 0, fr0);  // unconditional: see below
+                read_frags(nxt, 0, fr0, LC);  // unconditional: see below
                 __builtin_amdgcn_sched_barrier(0);
                 return;
             }
@@ -1096,8 +1109,8 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             // results the next MFMAs wait for (3-4% on these tiles; the
             // smaller tiles of the short-K shapes are faster as scheduled).
             constexpr bool kInterleave = S::kFM == 4 && S::kFN == 2;
-            constexpr int kMfmas = S::kFM * S::kFN;
-            constexpr int kReads = (WT ? 2 * S::kFN : S::kFN) + S::kFM;
+            constexpr int kMfmas = L * S::kFN;
+            constexpr int kReads = (L > 0 ? (WT ? 2 * S::kFN : S::kFN) : 0) + L;
             auto interleave = [&]() {
                 if constexpr (kInterleave) {
 #pragma unroll
@@ -1111,15 +1124,15 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                         __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfmas, 0);
                 }
             };
-            read_frags(cur, 1, fr1);
-            mfmas(fr0);
+            read_frags(cur, 1, fr1, LC);
+            mfmas(fr0, LC);
             interleave();
             if constexpr (S::kKSteps == 4) {
-                read_frags(cur, 2, fr0);
-                mfmas(fr1);
+                read_frags(cur, 2, fr0, LC);
+                mfmas(fr1, LC);
                 interleave();
-                read_frags(cur, 3, fr1);
-                mfmas(fr0);
+                read_frags(cur, 3, fr1, LC);
+                mfmas(fr0, LC);
                 interleave();
             }
             if (kt + 1 < k1) {
@@ -1133,12 +1146,13 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             // before any DMA reuses the buffer).  Reading unconditionally
             // keeps the fragment registers free of a merge of old and new
             // values, which would cost register copies.
-            read_frags(nxt, 0, fr0);
-            mfmas(fr1);
+            read_frags(nxt, 0, fr0, LC);
+            mfmas(fr1, LC);
             interleave();
         };
         static_assert(S::kKSteps % 2 == 0, "k-steps per slice must be even");
 
+        auto kloop = [&](auto LC) {
         wait_vmcnt<0>();  // the previous tile's stores are out of the vmcnt count
         __syncthreads();  // every wave is done with the previous tile's buffers
         // fill the ring: slices k0 .. k0+S-1, then wait for the first
@@ -1149,7 +1163,7 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
         }
         wait_slices(min(S::S - 1, k1 - 1 - k0));
         lds_barrier();
-        read_frags(lds0, 0, fr0);
+        read_frags(lds0, 0, fr0, LC);
         // slice k0 + n uses buffer n mod S
         int kt = k0;
         if constexpr (S::kChunks == 2) {
@@ -1159,40 +1173,59 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             static_assert(S::S == 2, "FP8 tiles use 2 LDS stages");
             for (; kt < k1; ++kt) {
                 const bool odd = (kt - k0) & 1;
-                slice(kt, odd ? lds1 : lds0, odd ? 1 : 0, odd ? lds0 : lds1);
+                slice(kt, odd ? lds1 : lds0, odd ? 1 : 0, odd ? lds0 : lds1, LC);
             }
         } else if constexpr (S::S == 2) {
             for (; kt + 2 <= k1; kt += 2) {
-                slice(kt, lds0, 0, lds1);
-                slice(kt + 1, lds1, 1, lds0);
+                slice(kt, lds0, 0, lds1, LC);
+                slice(kt + 1, lds1, 1, lds0, LC);
             }
             if (kt < k1)
-                slice(kt, lds0, 0, lds1);
+                slice(kt, lds0, 0, lds1, LC);
         } else if constexpr (S::S == 3) {
             for (; kt + 3 <= k1; kt += 3) {
-                slice(kt, lds0, 0, lds1);
-                slice(kt + 1, lds1, 1, lds2);
-                slice(kt + 2, lds2, 2, lds0);
+                slice(kt, lds0, 0, lds1, LC);
+                slice(kt + 1, lds1, 1, lds2, LC);
+                slice(kt + 2, lds2, 2, lds0, LC);
             }
             if (kt < k1)
-                slice(kt, lds0, 0, lds1);
+                slice(kt, lds0, 0, lds1, LC);
             if (kt + 1 < k1)
-                slice(kt + 1, lds1, 1, lds2);
+                slice(kt + 1, lds1, 1, lds2, LC);
         } else {
             for (; kt + 4 <= k1; kt += 4) {
-                slice(kt, lds0, 0, lds1);
-                slice(kt + 1, lds1, 1, lds2);
-                slice(kt + 2, lds2, 2, lds3);
-                slice(kt + 3, lds3, 3, lds0);
+                slice(kt, lds0, 0, lds1, LC);
+                slice(kt + 1, lds1, 1, lds2, LC);
+                slice(kt + 2, lds2, 2, lds3, LC);
+                slice(kt + 3, lds3, 3, lds0, LC);
             }
             if (kt < k1)
-                slice(kt, lds0, 0, lds1);
+                slice(kt, lds0, 0, lds1, LC);
             if (kt + 1 < k1)
-                slice(kt + 1, lds1, 1, lds2);
+                slice(kt + 1, lds1, 1, lds2, LC);
             if (kt + 2 < k1)
-                slice(kt + 2, lds2, 2, lds3);
+                slice(kt + 2, lds2, 2, lds3, LC);
         }
 
+        };
+        // live row fragments of this wave (see read_frags); the 256-row
+        // tiles, whose expert segments end in partly filled m-tiles, take a
+        // loop per count
+        if constexpr (S::kFM == 4 && !KG) {
+            const int live = min(max((t.rows - wm * S::kWaveM + 31) / 32, 0), S::kFM);
+            if (live >= 4)
+                kloop(std::integral_constant<int, 4>{});
+            else if (live == 3)
+                kloop(std::integral_constant<int, 3>{});
+            else if (live == 2)
+                kloop(std::integral_constant<int, 2>{});
+            else if (live == 1)
+                kloop(std::integral_constant<int, 1>{});
+            else
+                kloop(std::integral_constant<int, 0>{});
+        } else {
+            kloop(std::integral_constant<int, S::kFM>{});
+        }
         if (slot < 0) {
             if constexpr (EPI == EPI_NONE && ET::kBytes != 1)  // unscaled plain output
                 store_tile_lds<OT, S, KG>(acc, Cb, t, Nout, ncols, wave, lds0, lds1);
