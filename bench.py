@@ -1,32 +1,38 @@
 #!/usr/bin/env python3
 """MoE-layer forward benchmark on one MI355X.
 
-One step = one pass of the whole hot path over one batch of seeded synthetic
-tokens, through the C ABI: gate GEMM + routing (moe_route), counting-sort
-permutation (moe_permute), expert up and down layers (moe_expert_up,
-moe_expert_down) and the weighted combine (moe_combine).  The default
-workload is the Mixtral-8x7B-shaped layer (T=4096 tokens, d=4096, 8 experts,
-top-2, SwiGLU 4096->14336->4096, bf16, Zipf(1.2)-skewed gate bias); every input
-is resident in HBM before the timed region starts.
+One step = one moe_forward call (the whole hot path: gate GEMM, routing,
+counting-sort permutation, expert up and down layers, weighted combine) over
+one batch of seeded synthetic tokens, through the C ABI, with every input
+resident in HBM before the timed region starts.  The default workload is the
+Mixtral-8x7B-shaped layer (T=4096 tokens, d=4096, 8 experts, top-2, SwiGLU
+4096->14336->4096, bf16, Zipf(1.2)-skewed gate bias).
 
-Prints ONE JSON line: tokens/s of the whole job (value), the roofline of the
-dominant kernel (the expert up-projection grouped GEMM, with its split-K
-reduction) from HIP events on the stream it runs on, and the CPU oracle timed
-on a bounded sample of the same workload on this host's cores.  The same line
-also carries the router statistics, a shared expert (width F), the layer with
-FP8 expert weights and the training step (forward keeping its intermediates,
-then the backward) timed on the same workload ("next_rows"), and the step
-timing of the other workloads
-("other_configs": routing inputs from the seeded generator, expert weights
-drawn on the device with the same distribution, since their values do not
-change the work).
+`value` is T divided by the median of the per-step HIP-event times of
+moe_forward (W warm-up calls, then K timed calls, K >= 50 by default); the
+timed calls are also bracketed by device synchronisations and their wall
+clock reported.  A separate pass times the five entry points one by one
+(moe_route, moe_permute, moe_expert_up, moe_expert_down, moe_combine) for the
+per-stage breakdown and the roofline of the dominant kernel (the expert
+up-projection grouped GEMM with its split-K reduction).  The CPU oracle is
+timed on this host's cores: a bounded sample of the Mixtral layer for the
+headline line, and per workload below.
+
+Also on the line: a device-to-device copy's bandwidth (the HBM reference),
+the standalone permutation with its row copy (moe_permute writing x_perm),
+the router statistics, a shared expert, the layer with FP8 expert weights and
+the training step ("next_rows"), and every other workload ("other_configs":
+moe_forward median, stage breakdown, roofline against the bound that applies,
+and a CPU-oracle baseline; routing inputs from the seeded generator, expert
+weights drawn on the device with the same distribution, since their values
+do not change the work).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                   [--no-cpu-baseline] [--no-other-configs] [--no-next-rows]
                   [--mode copy|train]
 
 --mode train times only the training step and prints its own JSON line (for
-profiling the backward); --mode copy times a plain device copy (the HBM
+profiling the backward); --mode copy runs plain device copies (the HBM
 counter calibration).
 """
 from __future__ import annotations
@@ -116,16 +122,66 @@ def cpu_baseline(case, inp, budget_s: float):
             break
         n = len(toks) * 2
     per_token = t_route / case.T + t_ffn / done
+    flops = case.ffn_flops_dropless * (disp["P"] / (case.T * case.k)) + (
+        2.0 * case.T * case.d * case.E if case.logits == "gate" else 0.0)
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "gflops": flops / case.T / per_token / 1e9,
             "sample": f"{done} of {case.T} tokens of the {case.name} layer (expert FFN + combine of the sample; "
                       f"gate, routing and permutation of all {case.T} tokens charged per token)",
             "seconds": round(t_route + t_ffn, 2)}
 
 
+def cpu_baseline_full(case, inp, reps: int = 3):
+    """Oracle tokens/s of whole forwards (gate, routing, permutation, expert
+    FFN and combine of every token), best of `reps`."""
+    import oracle
+    act = oracle.SWIGLU if case.act == "swiglu" else oracle.RELU
+    best = None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        if case.logits == "gate":
+            _ze, z32 = oracle.gate_logits(inp["x"], inp["Wg"], inp["bg"])
+        else:
+            z32 = inp["logits"]
+        idx, w = oracle.route(z32, case.k, case.normalize, case.lam)
+        disp = oracle.dispatch(idx, case.E, oracle.capacity(case.T, case.E, case.k, case.cf))
+        oracle.forward_tokens(inp["x"], inp["W1"], inp["W2"], idx, w, disp["slot"], act, case.F)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    flops = case.ffn_flops_dropless * (disp["P"] / (case.T * case.k)) + (
+        2.0 * case.T * case.d * case.E if case.logits == "gate" else 0.0)
+    return {"value": case.T / best, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "gflops": flops / best / 1e9,
+            "sample": f"whole forward of all {case.T} tokens of the {case.name} layer, best of {reps}",
+            "seconds": round(best, 3)}
+
+
+def copy_bandwidth(stream, n=1 << 30, reps=10):
+    """Achieved bandwidth of a plain device-to-device copy of n bytes (read n,
+    write n), HIP events on the stream; the reference for the HBM fractions."""
+    import numpy as np
+    import torch
+    with torch.cuda.stream(stream):
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            b.copy_(a)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            b.copy_(a)
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+    del a, b
+    return {"gbps": 2.0 * n / (ms * 1e-3) / 1e9, "bytes_moved": 2 * n, "ms": ms,
+            "frac_of_8TBps": 2.0 * n / (ms * 1e-3) / 1e9 / HBM_GBPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -167,17 +223,19 @@ def main():
         r.update(workload=workload_name(case), steps=args.steps)
         print(json.dumps(r), flush=True)
         return
-    log(f"[bench] warmup {args.warmup}")
-    res = lay.time(args.steps, args.warmup)
+    log(f"[bench] moe_forward: {args.warmup} warm-up + {args.steps} timed steps")
+    fwd = lay.time_forward(args.steps, args.warmup)
+    log("[bench] stage pass")
+    res = lay.time(args.steps, 2)
     T, d, E, k, F = case.T, case.d, case.E, case.k, case.F
-    stage_ms, elapsed, P = res["stage_ms"], res["elapsed"], res["P"]
-    ms_per_step = elapsed * 1e3 / args.steps
+    stage_ms, P = res["stage_ms"], res["P"]
+    ms_per_step = fwd["median_ms"]
     peak = PEAK_TFLOPS[case.dtype]
     up_tflops = lay.up_flops(P) / (stage_ms["expert_up"] * 1e-3) / 1e12
 
     result = {
         "metric": METRIC,
-        "value": T * args.steps / elapsed,
+        "value": T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -190,18 +248,26 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(case), "T": T, "d": d, "E": E, "k": k, "F": F,
                    "parallelism": "single GPU"},
+        "timing": {"entry_point": "moe_forward", "stat": f"median of {args.steps} HIP-event step times after "
+                   f"{args.warmup} warm-ups", "mean_ms": fwd["mean_ms"], "min_ms": fwd["min_ms"],
+                   "wall_ms_per_step": fwd["wall_ms"],
+                   "stage_sum_ms": sum(stage_ms.values()),
+                   "stage_sum_vs_forward": sum(stage_ms.values()) / ms_per_step},
         "roofline": {"bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": up_tflops / peak, "traffic": stored_traffic(case.name),
                      "kernel": "moe_expert_up: moe_grouped_gemm_kernel (up-projection + activation) and its K-split reduction"},
     }
     result.update(lay.summary(res, ms_per_step))
+    log("[bench] copy bandwidth, standalone permutation with its row copy")
+    result["copy_bandwidth"] = copy_bandwidth(stream)
+    result["permute_row_copy"] = lay.time_permute_copy(args.steps)
     if not args.no_graph:
         result["graph_replay"] = lay.time_graph(args.steps)
 
     # rows beyond the layer step: router statistics, shared expert
     if not args.no_next_rows:
         log("[bench] router statistics and shared expert")
-        result["next_rows"] = lay.time_next_rows(args.steps, res)
+        result["next_rows"] = lay.time_next_rows(min(args.steps, 20), res)
 
     if not args.no_other_configs:
         others = {}
@@ -219,13 +285,25 @@ def main():
                 w = {"W1": (torch.randn(c.E, n1, c.d, generator=gen, device="cuda") * c.w_std).to(dt),
                      "W2": (torch.randn(c.E, c.d, c.F, generator=gen, device="cuda") * c.w_std).to(dt)}
             lo = Layer(moe, c, ri, w, stream)
-            steps = max(args.steps // 2, 3)
-            r = lo.time(steps, max(args.warmup // 2, 2))
-            msps = r["elapsed"] * 1e3 / steps
-            o = {"workload": workload_name(c), "tokens_per_s": c.T * steps / r["elapsed"], "ms_per_step": msps}
+            f = lo.time_forward(args.steps, args.warmup)
+            r = lo.time(max(args.steps // 2, 10), 2)
+            msps = f["median_ms"]
+            o = {"workload": workload_name(c), "tokens_per_s": c.T / (msps * 1e-3), "ms_per_step": msps,
+                 "mean_ms": f["mean_ms"], "stage_sum_ms": sum(r["stage_ms"].values())}
             o.update(lo.summary(r, msps))
+            o["roofline"] = lo.roofline(r)
             if not args.no_graph:
-                o["graph_replay"] = lo.time_graph(steps)
+                o["graph_replay"] = lo.time_graph(max(args.steps // 2, 10))
+            if not args.no_cpu_baseline:
+                # the oracle's arithmetic does not depend on the weights'
+                # values: it runs on host copies of the device weights
+                torch.cuda.synchronize()
+                ri["W1"], ri["W2"] = to_host(w["W1"]), to_host(w["W2"])
+                log(f"[bench] {name}: timing the CPU oracle")
+                if name in ("skywork_m", "skywork_m_zipf"):
+                    o["cpu_baseline"] = cpu_baseline(c, ri, args.cpu_seconds / 2)
+                else:
+                    o["cpu_baseline"] = cpu_baseline_full(c, ri, 3)
             others[name] = o
             del lo, w, ri
             torch.cuda.empty_cache()
@@ -235,6 +313,14 @@ def main():
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(case, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def to_host(t):
+    import numpy as np
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
 
 
 def to_dev(a):
@@ -255,10 +341,11 @@ def workload_name(case):
 
 
 class Layer:
-    """Device buffers and the timed step of one workload.  One step = gate +
-    routing, permutation (indices only: the up projection gathers the token
-    rows itself), expert up and down layers, weighted combine, all on one
-    stream with an event between the stages."""
+    """Device buffers and the timed step of one workload.  One step = one
+    moe_forward call: gate + routing, permutation (indices only: the up
+    projection gathers the token rows itself), expert up and down layers,
+    weighted combine, all on one stream.  The stage pass calls the five entry
+    points of the same step one by one with an event between them."""
 
     NAMES = ["route", "permute", "expert_up", "expert_down", "combine"]
 
@@ -306,7 +393,89 @@ class Layer:
         moe.moe_combine(p, self.y_perm, self.slot, self.w, self.y, stream=s)
         rec(5)
 
+    def forward(self):
+        """One moe_forward call (the step), with the routing outputs kept in
+        the step's buffers."""
+        moe, p, s = self.moe, self.p, self.stream.cuda_stream
+        info = {"topk_idx": self.idx, "topk_w": self.w, "counts": self.counts, "offsets": self.offsets,
+                "slot": self.slot, "src_token": self.src}
+        moe.moe_forward(p, self.x, self.Wg, self.bg, self.W1, self.W2, self.y, logits=self.logits, info=info,
+                        ws=self.ws, stream=s)
+
+    def time_forward(self, steps, warmup):
+        """moe_forward: warm-ups, then `steps` calls with a HIP event after
+        each on the layer's stream, the whole timed region bracketed by device
+        synchronisations."""
+        import numpy as np
+        import torch
+        for _ in range(warmup):
+            self.forward()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(self.stream)
+        for i in range(steps):
+            self.forward()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+        return {"median_ms": float(np.median(ms)), "mean_ms": float(ms.mean()), "min_ms": float(ms.min()),
+                "wall_ms": wall * 1e3 / steps}
+
+    def time_permute_copy(self, steps):
+        """moe_permute with its row copy (x_perm written, the path moe_forward
+        takes when x is beyond the fused gather's 32-bit offsets), on the
+        step's routing.  Algorithmic bytes: x read once, P rows written, plus
+        the index traffic (12 T k)."""
+        import numpy as np
+        import torch
+        moe, p, c, s = self.moe, self.p, self.case, self.stream.cuda_stream
+        with torch.cuda.stream(self.stream):
+            xp = torch.empty(c.T * c.k, c.d, dtype=self.dt, device="cuda")
+        call = lambda: moe.moe_permute(p, self.idx, self.x, self.counts, self.offsets, self.slot, self.src, xp,  # noqa
+                                       self.ws, stream=s)
+        for _ in range(3):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(self.stream)
+        for i in range(steps):
+            call()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+        P = int(self.offsets[-1].item())
+        b = 4 if c.dtype == "f32" else 2
+        byts = (c.T + P) * c.d * b + 12.0 * c.T * c.k
+        del xp
+        return {"ms": ms, "bytes": byts, "gbps": byts / (ms * 1e-3) / 1e9,
+                "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_GBPS,
+                "note": "count + scan + scatter + row gather kernels of one moe_permute call with x_perm"}
+
+    def roofline(self, res):
+        """Roofline of the grouped GEMM (up + down) and of the step:
+        frac = max(t_flops, t_bytes) / t, with t_flops at the dtype's MFMA peak
+        and t_bytes the algorithmic HBM bytes (expert weights, the activation
+        rows read, h written and read back, y_perm written) at 8 TB/s; bound
+        names the larger of the two."""
+        c = self.case
+        stage_ms, P = res["stage_ms"], res["P"]
+        b = 4 if c.dtype == "f32" else 2
+        flops = self.up_flops(P) + 2.0 * P * c.F * c.d
+        wbytes = c.E * (self.n1 * c.d + c.d * c.F) * b
+        byts = wbytes + P * c.d * b + 2.0 * P * c.F * b + P * c.d * b
+        t = (stage_ms["expert_up"] + stage_ms["expert_down"]) * 1e-3
+        t_f = flops / (PEAK_TFLOPS[c.dtype] * 1e12)
+        t_b = byts / (HBM_GBPS * 1e9)
+        return {"kernel": "grouped GEMM, up + down (with their K-split reductions)",
+                "bound": "mfma" if t_f >= t_b else "hbm", "frac": max(t_f, t_b) / t,
+                "t_flops_us": t_f * 1e6, "t_bytes_us": t_b * 1e6, "measured_us": t * 1e6,
+                "flops": flops, "bytes": byts, "mfma_frac": t_f / t, "hbm_frac": t_b / t}
+
     def time(self, steps, warmup):
+        """The stage pass: the five entry points of the step called one by
+        one with an event between them; per-stage medians."""
         import numpy as np
         import torch
         for _ in range(warmup):
@@ -319,21 +488,21 @@ class Layer:
             self.step(events[i])
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
+        stage_ms = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in events]))
                     for i, n in enumerate(self.NAMES)}
         return {"stage_ms": stage_ms, "elapsed": elapsed, "P": int(self.offsets[-1].item())}
 
     def time_graph(self, steps):
-        """The same step captured once in a HIP graph (every entry point only
-        launches kernels on the given stream) and replayed: the step without
-        the host's per-launch cost."""
+        """The same step (moe_forward) captured once in a HIP graph (every
+        entry point only launches kernels on the given stream) and replayed:
+        the step without the host's per-launch cost."""
         import numpy as np
         import torch
-        self.step()
+        self.forward()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=self.stream):
-            self.step()
+            self.forward()
         torch.cuda.synchronize()
         for _ in range(2):
             g.replay()
@@ -345,7 +514,7 @@ class Layer:
                 g.replay()
                 ev[i + 1].record(self.stream)
         torch.cuda.synchronize()
-        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+        ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
         del g
         return {"ms_per_step": ms, "tokens_per_s": self.case.T / (ms * 1e-3)}
 
