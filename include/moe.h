@@ -207,6 +207,25 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, cons
                        const void* W2, void* y, float* logits, const moe_route_info* info, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same steps and kernels, with the workspace in the library's own device
+ * scratch, a fixed 32 MiB array per GPU (held from the library's load until
+ * the process ends; its address is looked up once per device on that
+ * device's first call).  The caller passes inputs and outputs as in
+ * moe_forward and no workspace; nothing is allocated or freed.  The grouped
+ * GEMMs run without the K split of their last round (the split needs room for
+ * partial tiles), so y may differ from moe_forward's in the last bits (fp32
+ * summation order); routing and permutation are identical.  Problems whose
+ * workspace without those partial tiles exceeds 32 MiB (about 450 tokens at
+ * the Mixtral shape) return MOE_ERR_WORKSPACE.  Every call on a GPU uses that
+ * GPU's one scratch: calls that overlap on one GPU (other streams, other
+ * threads) race and give undefined results; no step relies on the scratch's
+ * previous contents. */
+moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* Wg, const float* bg,
+                               const void* W1, const void* W2, void* y, float* logits,
+                               const moe_route_info* info, void* stream);
+
 /* Router by-products (Megatron-Core page, "MoE负载均衡的挑战与应对": an
  * auxiliary loss pushes experts towards equal token counts, "关键特性":
  * Z-Loss; Skywork-MoE news item, "技术创新 2. 自适应的Aux Loss", and slides,

@@ -10,7 +10,7 @@ moe_route, moe_permute, moe_expert_up, moe_expert_down, moe_grouped_ffn,
 moe_combine, moe_forward, moe_router_stats, moe_shared_workspace_size,
 moe_shared_expert, moe_combine_shared, moe_quantize_fp8, moe_fp8_workspace_size,
 moe_expert_up_fp8, moe_expert_down_fp8, moe_forward_fp8, moe_forward_train,
-moe_backward_workspace_size, moe_backward.
+moe_backward_workspace_size, moe_backward, moe_forward_noalloc.
 """
 from __future__ import annotations
 
@@ -29,7 +29,8 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_capacity", "moe_workspace
            "moe_permute", "moe_expert_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_forward",
            "moe_router_stats", "moe_shared_workspace_size", "moe_shared_expert", "moe_combine_shared",
            "moe_quantize_fp8", "moe_fp8_workspace_size", "moe_expert_up_fp8", "moe_expert_down_fp8",
-           "moe_forward_fp8", "moe_forward_train", "moe_backward_workspace_size", "moe_backward")
+           "moe_forward_fp8", "moe_forward_train", "moe_backward_workspace_size", "moe_backward",
+           "moe_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -84,6 +85,7 @@ def load() -> ctypes.CDLL:
     lib.moe_grouped_ffn.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_combine.argtypes = [PP, P, P, P, P, P]
     lib.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), P, ctypes.c_size_t, P]
+    lib.moe_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, ctypes.POINTER(RouteInfo), P]
     lib.moe_router_stats.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_shared_workspace_size.argtypes = [PP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_shared_expert.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, ctypes.c_size_t, P]
@@ -201,6 +203,16 @@ def moe_forward(p, x, Wg, bg, W1, W2, y, logits=None, info=None, ws=None, stream
     _check(load().moe_forward(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(y),
                               _ptr(logits), ctypes.byref(ri) if ri is not None else None, _ptr(ws), _nbytes(ws),
                               _stream(stream)))
+
+
+def moe_forward_noalloc(p, x, Wg, bg, W1, W2, y, logits=None, info=None, stream=None):
+    """moe_forward with the library's own device scratch as workspace (no
+    allocation; problems up to 32 MiB of workspace)."""
+    ri = None
+    if info:
+        ri = RouteInfo(*[_ptr(info.get(f)) for f, _ in RouteInfo._fields_])
+    _check(load().moe_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(W2), _ptr(y),
+                                      _ptr(logits), ctypes.byref(ri) if ri is not None else None, _stream(stream)))
 
 
 def moe_router_stats(p, logits, counts, offsets, frac, mean_prob, scalars, ws, stream=None):

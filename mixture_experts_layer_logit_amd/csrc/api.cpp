@@ -170,7 +170,9 @@ int mean_rows_of(const moe_problem* p);
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-Layout layout_of(const moe_problem* p)
+// with_partial: room for the K-split partial tiles of the grouped GEMM's last
+// round (without it the GEMMs run unsplit).
+Layout layout_of(const moe_problem* p, bool with_partial = true)
 {
     Layout L;
     const size_t T = (size_t)p->T, k = (size_t)p->k, E = (size_t)p->E, d = (size_t)p->d, F = (size_t)p->F;
@@ -191,7 +193,7 @@ Layout layout_of(const moe_problem* p)
     L.chunk_cnt = take(std::max<size_t>(nchunks, 1) * E * 4);
     L.logits = take(T * E * 4);
     L.stats = take(moe_router_stats_partial_bytes(p->T, p->E));
-    L.partial = take(moe_grouped_gemm_partial_bytes(p->dtype, mean_rows_of(p)));
+    L.partial = take(with_partial ? moe_grouped_gemm_partial_bytes(p->dtype, mean_rows_of(p)) : 0);
     L.h = take(T * k * F * b);
     L.y_perm = take(T * k * d * b);
     L.x_perm = take(gather_ok(p) ? 0 : T * k * d * b);
@@ -226,6 +228,38 @@ moe_status hip_status(hipError_t e, const char* what)
 {
     if (e != hipSuccess)
         return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+// ---- the allocation-free forward's scratch
+// One file-scope device array per GPU (each device holds its own copy, at its
+// own address, from the library's load until the process ends).  Host code
+// never uses the array's name as an address: it takes the device address
+// once per device with hipGetSymbolAddress and passes that to the kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's scratch (looked up on the device's first
+// call, with the device current).
+moe_status scratch_address(void** out)
+{
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the 64 the scratch table holds", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
     return MOE_OK;
 }
 
@@ -601,13 +635,14 @@ moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* 
     return ok();
 }
 
-moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
-                       const void* W2, void* y, float* logits, const moe_route_info* info, void* ws, size_t ws_bytes,
-                       void* stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks of moe_forward other than the workspace.
+moe_status check_forward(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                         const void* W2, const void* y, const float* logits)
 {
-    CHECK(check_problem(p));
-    if (p->T == 0)
-        return ok();
     CHECK(check_ptr(x, "x", 16));
     CHECK(check_ptr(W1, "W1", 16));
     CHECK(check_ptr(W2, "W2", 16));
@@ -623,8 +658,15 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, cons
             return fail(MOE_ERR_INVALID_ARG, "logits must be given when Wg is NULL");
         CHECK(check_ptr(logits, "logits", 4));
     }
-    CHECK(check_ws(p, ws, ws_bytes));
-    const Layout L = layout_of(p);
+    return MOE_OK;
+}
+
+// The forward's launch sequence on a validated workspace of layout L (with
+// or without the K-split partial tiles).
+moe_status forward_steps(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                         const void* W2, void* y, float* logits, const moe_route_info* info, void* ws,
+                         const Layout& L, bool split, hipStream_t s)
+{
     moe_route_info r = {};
     if (info)
         r = *info;
@@ -640,10 +682,9 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, cons
     for (const void* q : ptrs)
         CHECK(check_ptr(q, "route info field", 4));
     float* z = logits ? logits : at<float>(ws, L.logits);
-    float* partial = at<float>(ws, L.partial);
+    float* partial = split ? at<float>(ws, L.partial) : nullptr;
     void* h = at<char>(ws, L.h);
     void* y_perm = at<char>(ws, L.y_perm);
-    hipStream_t s = (hipStream_t)stream;
     CHECK(do_route(p, Wg ? x : nullptr, Wg, bg, z, topk_idx, topk_w, s));
     // the up projection reads the token rows of x through src_token, so the
     // permutation writes no x_perm copy (unless x is beyond 32-bit offsets)
@@ -657,6 +698,40 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, cons
     }
     CHECK(do_down(p, h, offsets, W2, y_perm, partial, s));
     CHECK(do_combine(p, y_perm, slot, topk_w, nullptr, y, s));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                       const void* W2, void* y, float* logits, const moe_route_info* info, void* ws, size_t ws_bytes,
+                       void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_forward(p, x, Wg, bg, W1, W2, y, logits));
+    CHECK(check_ws(p, ws, ws_bytes));
+    CHECK(forward_steps(p, x, Wg, bg, W1, W2, y, logits, info, ws, layout_of(p), true, (hipStream_t)stream));
+    return ok();
+}
+
+moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* Wg, const float* bg, const void* W1,
+                               const void* W2, void* y, float* logits, const moe_route_info* info, void* stream)
+{
+    CHECK(check_problem(p));
+    if (p->T == 0)
+        return ok();
+    CHECK(check_forward(p, x, Wg, bg, W1, W2, y, logits));
+    const Layout L = layout_of(p, false);
+    if (L.total > kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE, "the problem needs %zu bytes of scratch; the allocation-free forward has %zu",
+                    L.total, kScratchBytes);
+    void* ws = nullptr;
+    CHECK(scratch_address(&ws));
+    CHECK(forward_steps(p, x, Wg, bg, W1, W2, y, logits, info, ws, L, false, (hipStream_t)stream));
     return ok();
 }
 

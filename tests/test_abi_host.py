@@ -327,3 +327,23 @@ def test_backward_entry_points_reject_bad_arguments():
     assert lib.moe_backward(p0p, None, None, None, None, None, None, None, None, None, None, None, None, None, None,
                             None, 0, None) == moe.MOE_ERR_INVALID_ARG
 
+
+def test_noalloc_forward_rejects_before_any_device_call():
+    lib = moe.load()
+    # the Mixtral-shaped layer needs ~235 MB of workspace: beyond the 32 MiB scratch
+    big = moe.problem(4096, 4096, 8, 2, 14336, act="swiglu")
+    pb = ctypes.byref(big)
+    assert lib.moe_forward_noalloc(pb, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert b"scratch" in lib.moe_last_error()
+    small = moe.problem(64, 64, 8, 2, 64)
+    ps = ctypes.byref(small)
+    # bad pointers and missing logits are rejected as in moe_forward
+    assert lib.moe_forward_noalloc(ps, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_noalloc(ps, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # T == 0 is a no-op
+    p0 = moe.problem(0, 64, 8, 2, 64)
+    assert lib.moe_forward_noalloc(ctypes.byref(p0), None, None, None, None, None, None, None, None, None) == \
+        moe.MOE_OK
