@@ -374,14 +374,18 @@ __global__ __launch_bounds__(kSmallThreads) void moe_permute_small_kernel(const 
     }
 }
 
-// One wavefront per token; the row is read once and written to each kept slot.
+// One wavefront per token; the row is read once and written to each kept
+// slot.  The token and its slots are wave-uniform (scalar loads, no
+// divergent branches); x is read and x_perm written with non-temporal
+// accesses (each byte is touched once here).
 template <typename ET>
 __global__ __launch_bounds__(256) void moe_gather_kernel(const typename ET::storage* __restrict__ x,
                                                          const int32_t* __restrict__ slot, int T, int d, int k,
                                                          typename ET::storage* __restrict__ x_perm)
 {
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
     const int lane = lane_id();
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / kWave);
     if (t >= T)
         return;
     constexpr int kPer = 16 / ET::kBytes;           // elements per 16-byte vector
@@ -390,25 +394,25 @@ __global__ __launch_bounds__(256) void moe_gather_kernel(const typename ET::stor
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         rows[j] = (j < k) ? slot[(size_t)t * k + j] : -1;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * d);
+    const u32x4v* src = reinterpret_cast<const u32x4v*>(x + (size_t)t * d);
     for (int v0 = 0; v0 < nvec; v0 += kWave * 8) {
-        uint4 buf[8];
+        u32x4v buf[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int v = v0 + u * kWave + lane;
             if (v < nvec)
-                buf[u] = src[v];
+                buf[u] = __builtin_nontemporal_load(src + v);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if (rows[j] < 0)
                 continue;
-            uint4* dst = reinterpret_cast<uint4*>(x_perm + (size_t)rows[j] * d);
+            u32x4v* dst = reinterpret_cast<u32x4v*>(x_perm + (size_t)rows[j] * d);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int v = v0 + u * kWave + lane;
                 if (v < nvec)
-                    dst[v] = buf[u];
+                    __builtin_nontemporal_store(buf[u], dst + v);
             }
         }
     }
