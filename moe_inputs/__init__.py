@@ -103,6 +103,12 @@ SMALL = {
     "skywork_m_s": FULL["skywork_m"].with_(name="skywork_m_s", T=512, d=320, F=384, seed=2004),
     "skywork_m_zipf_s": FULL["skywork_m_zipf"].with_(name="skywork_m_zipf_s", T=512, d=320, F=384, seed=2014),
     "many_small_s": FULL["many_small"].with_(name="many_small_s", T=2048, d=256, F=128, seed=2005),
+    # Mixtral-family layers with about 680 rows per expert, so that the
+    # expert GEMMs take their largest (256 x 256) tile and the whole layer is
+    # still checked output by output: Zipf(1.2) loads, dropless and with a
+    # capacity factor of 1 that clips the two hottest experts.
+    "mixtral_m": FULL["mixtral"].with_(name="mixtral_m", T=2048, d=512, E=6, F=768, seed=2006),
+    "mixtral_m_cap": FULL["mixtral"].with_(name="mixtral_m_cap", T=2048, d=512, E=6, F=768, seed=2007, cf=1.0),
 }
 
 # Large token counts at small widths: index arithmetic, grids and chunk loops

@@ -1,6 +1,7 @@
 """Calibrate the per-expert gate bias of the Zipf-skewed synthetic cases.
 
-Run from the repository root:  python oracle/calibrate_zipf_bias.py
+Run from the repository root:  python oracle/calibrate_zipf_bias.py [case ...]
+(no names: every case; entries of cases not named are kept as stored)
 
 For each case whose gate bias is "zipf", the bias b [E] is chosen so that the
 share of top-k assignments that land on expert e follows q_e ~ (e+1)^-s.
@@ -61,8 +62,9 @@ def main():
     if os.path.exists(moe_inputs.ZIPF_BIAS_FILE):
         with open(moe_inputs.ZIPF_BIAS_FILE) as f:
             table = json.load(f)
+    names = sys.argv[1:]
     for name, case in moe_inputs.CASES.items():
-        if case.bias != "zipf":
+        if case.bias != "zipf" or (names and name not in names):
             continue
         bias, loads, q = calibrate(case)
         key = moe_inputs.case_key(case)

@@ -43,6 +43,9 @@ FP8_SMALL = {
     "skywork_fp8_s": ("skywork_m_s", dict(d=384, F=384)),
     "skywork_zipf_fp8_s": ("skywork_m_zipf_s", dict(d=384, F=384)),
     "many_small_fp8_s": ("many_small_s", dict(F=128)),
+    # the 256 x 256 FP8 tile, every output checked
+    "mixtral_fp8_m": ("mixtral_m", dict()),
+    "mixtral_fp8_m_cap": ("mixtral_m_cap", dict()),
 }
 
 
