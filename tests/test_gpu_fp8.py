@@ -167,9 +167,9 @@ def test_expert_up_and_down_fp8(name):
 # Segment layouts that make the last tile round split along K (one per tile
 # configuration), FP8 weights.
 FP8_SPLIT = {
-    "large": ("swiglu", 1024, 1024, 4, 2, 1536, [700, 300, 512, 536]),
-    "medium": ("relu", 512, 1024, 4, 2, 1024, [300, 0, 257, 300]),
-    "small": ("relu", 512, 1024, 16, 2, 512, [64] * 14 + [1, 63]),
+    "large": ("swiglu", 1024, 2048, 4, 2, 1536, [700, 300, 512, 536]),
+    "medium": ("relu", 512, 2048, 4, 2, 1024, [300, 0, 257, 300]),
+    "small": ("relu", 512, 2048, 16, 2, 512, [64] * 14 + [1, 63]),
 }
 
 

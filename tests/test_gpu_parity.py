@@ -287,17 +287,18 @@ def test_expert_up_and_down(name):
 # filled, so that, given a workspace, the grouped GEMM splits those tiles
 # along K (one per tile configuration: large, medium, small and fp32).
 SPLIT_CASES = {
-    # name: (dtype, act, T, d, E, k, F, segment rows)
-    "large_relu": ("bf16", "relu", 1024, 1024, 4, 2, 1536, [700, 300, 512, 536]),
-    "large_ragged": ("bf16", "relu", 1024, 1024, 4, 2, 1024, [1, 0, 1019, 1000]),
+    # name: (dtype, act, T, d, E, k, F, segment rows); the split runs only
+    # where K >= 2048, so d (the up-projection's K) is at least that
+    "large_relu": ("bf16", "relu", 1024, 2048, 4, 2, 2048, [700, 300, 512, 536]),
+    "large_ragged": ("bf16", "relu", 1024, 2048, 4, 2, 2048, [1, 0, 1019, 1000]),
     # the SwiGLU epilogue on the large tile: gate and up columns paired, a
     # partly filled last column tile (F = 320 is 2.5 tiles of 128 outputs),
-    # a ragged K (d = 640 is 20 slices of 32)
-    "large_swiglu": ("bf16", "swiglu", 1024, 512, 4, 2, 768, [700, 300, 512, 536]),
-    "large_swiglu_ragged": ("bf16", "swiglu", 1024, 640, 4, 2, 320, [1, 0, 1019, 1028]),
-    "medium_swiglu": ("bf16", "swiglu", 512, 512, 4, 2, 512, [300, 0, 257, 300]),
-    "small_relu": ("bf16", "relu", 512, 1024, 16, 2, 512, [64] * 14 + [1, 63]),
-    "f32_relu": ("f32", "relu", 512, 512, 4, 1, 512, [130, 0, 200, 150]),
+    # an odd slice count (d = 2112 is 33 slices of 64)
+    "large_swiglu": ("bf16", "swiglu", 1024, 2048, 4, 2, 768, [700, 300, 512, 536]),
+    "large_swiglu_ragged": ("bf16", "swiglu", 1024, 2112, 4, 2, 320, [1, 0, 1019, 1028]),
+    "medium_swiglu": ("bf16", "swiglu", 512, 2048, 4, 2, 512, [300, 0, 257, 300]),
+    "small_relu": ("bf16", "relu", 512, 2048, 16, 2, 512, [64] * 14 + [1, 63]),
+    "f32_relu": ("f32", "relu", 512, 2048, 4, 1, 512, [130, 0, 200, 150]),
 }
 
 
