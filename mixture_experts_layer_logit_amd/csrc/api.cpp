@@ -15,6 +15,9 @@
 extern "C" {
 hipError_t moe_launch_gate(int dtype, const void* x, const void* Wg, const float* bg, float* logits, int T, int d,
                            int E, hipStream_t stream);
+hipError_t moe_launch_gate_route(int dtype, const void* x, const void* Wg, const float* bg, float* logits, int T,
+                                 int d, int E, int k, int normalize, float lambda, int32_t* topk_idx, float* topk_w,
+                                 hipStream_t stream);
 hipError_t moe_launch_router(const float* logits, int T, int E, int k, int normalize, float lambda,
                              int32_t* topk_idx, float* topk_w, hipStream_t stream);
 hipError_t moe_launch_permute(int dtype, const int32_t* topk_idx, const void* x, int T, int d, int E, int k,
@@ -275,6 +278,11 @@ moe_status check_ws(const moe_problem* p, const void* ws, size_t ws_bytes)
 moe_status do_route(const moe_problem* p, const void* x, const void* Wg, const float* bg, float* logits,
                     int32_t* topk_idx, float* topk_w, hipStream_t s)
 {
+    // up to 64 experts one kernel computes the logits and routes them
+    if (Wg && p->E <= 64)
+        return hip_status(moe_launch_gate_route(p->dtype, x, Wg, bg, logits, p->T, p->d, p->E, p->k, p->normalize,
+                                                p->lambda, topk_idx, topk_w, s),
+                          "gate and router launch");
     if (Wg) {
         CHECK(hip_status(moe_launch_gate(p->dtype, x, Wg, bg, logits, p->T, p->d, p->E, s), "gate launch"));
     }

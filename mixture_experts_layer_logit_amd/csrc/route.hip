@@ -1,4 +1,5 @@
-// Gate GEMM and wavefront-per-token router (gfx950).
+// Gate GEMM and wavefront-per-token router (gfx950); for up to 64 experts
+// both in one kernel, routing each token with a group of lanes.
 //
 // Gate: one fully connected layer scores every token against every expert
 // (FastMoE announcement page, "特色二").  Router: optional Skywork gating-logit
@@ -6,6 +7,8 @@
 // softmax over all experts, top-k on the fp32 logit (Megatron-Core page,
 // "关键特性"; FastMoE page, Fig. 4: the top-2 gate takes the two best scores).
 #include "common.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -144,35 +147,42 @@ __device__ __forceinline__ uint32_t ordered_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ double wave_sum(double v)
+// Reductions over aligned groups of G lanes (G = 64: the wavefront).
+template <int G>
+__device__ __forceinline__ double group_sum(double v)
 {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
+    for (int o = G / 2; o >= 1; o >>= 1)
         v += __shfl_xor(v, o);
     return v;
 }
-__device__ __forceinline__ double wave_max(double v)
+template <int G>
+__device__ __forceinline__ double group_max(double v)
 {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
+    for (int o = G / 2; o >= 1; o >>= 1)
         v = fmax(v, __shfl_xor(v, o));
     return v;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+template <int G>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v)
 {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
+    for (int o = G / 2; o >= 1; o >>= 1) {
         const uint64_t w = __shfl_xor(v, o);
         v = w > v ? w : v;
     }
     return v;
 }
+__device__ __forceinline__ double wave_sum(double v) { return group_sum<kWave>(v); }
+__device__ __forceinline__ double wave_max(double v) { return group_max<kWave>(v); }
 
-// Gate probabilities of one token held by a wavefront: z[i] is the logit of
-// expert lane + 64 i (0 past E).  Scores s in fp64 are the logit, or
+// Gate probabilities of one token held by a group of G lanes (by default
+// the wavefront): z[i] is the logit of expert lane + G i, lane being the
+// index within the group (0 past E).  Scores s in fp64 are the logit, or
 // lambda * (z - mu) / sigma (population sigma over the E experts; sigma == 0
 // gives s = 0); p_e = ex[i] / denom with ex = exp(s - max s).
-template <int VPL>
+template <int VPL, int G = kWave>
 __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int E, int normalize, float lambda,
                                             double (&ex)[VPL], double& denom)
 {
@@ -181,15 +191,15 @@ __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int
         double part = 0.0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
-            part += (lane + kWave * i < E) ? (double)z[i] : 0.0;
-        const double mu = wave_sum(part) / E;
+            part += (lane + G * i < E) ? (double)z[i] : 0.0;
+        const double mu = group_sum<G>(part) / E;
         part = 0.0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const double c = (double)z[i] - mu;
-            part += (lane + kWave * i < E) ? c * c : 0.0;
+            part += (lane + G * i < E) ? c * c : 0.0;
         }
-        const double sigma = sqrt(wave_sum(part) / E);
+        const double sigma = sqrt(group_sum<G>(part) / E);
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
             s[i] = sigma == 0.0 ? 0.0 : (double)lambda * ((double)z[i] - mu) / sigma;
@@ -201,16 +211,49 @@ __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int
     double m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-        if (lane + kWave * i < E)
+        if (lane + G * i < E)
             m = fmax(m, s[i]);
-    m = wave_max(m);
+    m = group_max<G>(m);
     double part = 0.0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        ex[i] = (lane + kWave * i < E) ? exp(s[i] - m) : 0.0;
+        ex[i] = (lane + G * i < E) ? exp(s[i] - m) : 0.0;
         part += ex[i];
     }
-    denom = wave_sum(part);
+    denom = group_sum<G>(part);
+}
+
+// The k selections of one token held by a group of G lanes: k rounds of a
+// group-wide maximum of the keys; the owner of the winning expert hands its
+// exp term to the group and clears the key.  Lane 0 of the group stores.
+template <int VPL, int G = kWave>
+__device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], const double (&ex)[VPL], double denom, int lane,
+                                            int t, int k, int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w)
+{
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            best = key[i] > best ? key[i] : best;
+        best = group_max_u64<G>(best);
+        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+        const int owner = e % G;
+        const int reg = e / G;
+        double mine = 0.0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            if (i == reg && lane == owner) {
+                mine = ex[i];
+                key[i] = 0;  // taken
+            }
+        }
+        const double pe = __shfl(mine, owner, G) / denom;
+        if (lane == 0) {
+            topk_idx[(size_t)t * k + j] = e;
+            topk_w[(size_t)t * k + j] = (float)pe;
+        }
+    }
 }
 
 template <int VPL>
@@ -234,30 +277,119 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
     }
     double ex[VPL], denom;
     token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
+    select_topk<VPL>(key, ex, denom, lane, t, k, topk_idx, topk_w);
+}
 
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
+// ---------------------------------------------------------------- gate + router
+// For E <= 64 one block computes all E logits of its 16 tokens and routes
+// them, which saves the router's launch and its re-read of the logits.
+// The gate part is the gate kernel above with NT 16-expert column tiles
+// that share each x chunk: every logit is still the fp64 sum of exact
+// products, each wavefront adding its own k blocks, the wavefronts'
+// partials added in wavefront order with the bias, rounded once to fp32.
+// The logits go to memory and to LDS; then each token is routed by a group
+// of G = threads / 16 lanes, expert e in group lane e % G, register e / G,
+// with the router kernel's arithmetic (selection on the fp32 logit, fp64
+// probabilities).
+template <typename ET, int NT, int SPLIT>
+__global__ __launch_bounds__(SPLIT * kWave) void moe_gate_route_kernel(
+    const typename ET::storage* __restrict__ x, const typename ET::storage* __restrict__ Wg,
+    const float* __restrict__ bg, float* __restrict__ logits, int T, int d, int E, int k, int normalize,
+    float lambda, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w)
+{
+    typedef double f64x4 __attribute__((ext_vector_type(4)));
+    constexpr int kCols = kGateTile * NT;             // experts covered
+    constexpr int G = SPLIT * kWave / kGateTile;      // routing lanes per token
+    constexpr int VPL = (kCols + G - 1) / G;
+    static_assert(G <= kWave && kWave % G == 0, "routing groups lie inside a wavefront");
+    __shared__ double s_part[SPLIT][kGateTile * kCols];
+    __shared__ float s_z[kGateTile][kCols];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int t0 = blockIdx.x * kGateTile;
+    const int i = lane % kGateTile, g = lane / kGateTile;
+    const typename ET::storage* xr = x + (size_t)min(t0 + i, T - 1) * d + 8 * g;
+    const typename ET::storage* wr[NT];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
-        const int owner = e % kWave;
-        const int reg = e / kWave;
-        double mine = 0.0;
+    for (int n = 0; n < NT; ++n)
+        wr[n] = Wg + (size_t)min(kGateTile * n + i, E - 1) * d + 8 * g;
+    f64x4 acc[NT];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            if (i == reg && lane == owner) {
-                mine = ex[i];
-                key[i] = 0;  // taken
+    for (int n = 0; n < NT; ++n)
+        acc[n] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const int nb = (d / 32 - wave + SPLIT - 1) / SPLIT;
+    typedef GateChunk<ET> Chunk;
+    Chunk xq[kGateDepth], wq[kGateDepth][NT];
+#pragma unroll
+    for (int q = 0; q < kGateDepth; ++q)
+        if (q < nb) {
+            const size_t off = (size_t)(wave + q * SPLIT) * 32;
+            xq[q].load(xr + off);
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                wq[q][n].load(wr[n] + off);
+        }
+    for (int it = 0; it < nb; it += kGateDepth) {
+#pragma unroll
+        for (int q = 0; q < kGateDepth; ++q) {
+            if (it + q < nb) {
+                float xf[8], wf[NT][8];
+                xq[q].unpack(xf);
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    wq[q][n].unpack(wf[n]);
+                if (it + q + kGateDepth < nb) {
+                    const size_t off = (size_t)(wave + (it + q + kGateDepth) * SPLIT) * 32;
+                    xq[q].load(xr + off);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        wq[q][n].load(wr[n] + off);
+                }
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const double xd = (double)xf[s];
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd, (double)wf[n][s], acc[n], 0, 0, 0);
+                }
             }
         }
-        const double pe = __shfl(mine, owner) / denom;
-        if (lane == 0) {
-            topk_idx[(size_t)t * k + j] = e;
-            topk_w[(size_t)t * k + j] = (float)pe;
-        }
     }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            s_part[wave][(4 * r + g) * kCols + kGateTile * n + i] = acc[n][r];
+    __syncthreads();
+    for (int q = threadIdx.x; q < kGateTile * kCols; q += SPLIT * kWave) {
+        const int tok = q / kCols, e = q % kCols;
+        double sum = s_part[0][q];
+#pragma unroll
+        for (int w = 1; w < SPLIT; ++w)
+            sum += s_part[w][q];
+        if (bg && e < E)
+            sum += (double)bg[e];
+        const float z = (float)sum;
+        s_z[tok][e] = z;
+        if (t0 + tok < T && e < E)
+            logits[(size_t)(t0 + tok) * E + e] = z;
+    }
+    __syncthreads();
+    const int tok = threadIdx.x / G, li = threadIdx.x % G;
+    const int t = t0 + tok;
+    if (t >= T)
+        return;  // whole groups leave together
+    float z[VPL];
+    uint64_t key[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = li + G * v;
+        z[v] = e < E ? s_z[tok][e] : 0.0f;
+        key[v] = e < E ? ((uint64_t)ordered_key(z[v]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
+    }
+    double ex[VPL], denom;
+    token_probs<VPL, G>(z, li, E, normalize, lambda, ex, denom);
+    select_topk<VPL, G>(key, ex, denom, li, t, k, topk_idx, topk_w);
 }
 
 // ---------------------------------------------------------------- router backward
@@ -530,6 +662,42 @@ extern "C" hipError_t moe_launch_gate(int dtype, const void* x, const void* Wg, 
     else
         moe_gate_logits_kernel<bf16_t>
             <<<grid, block, 0, stream>>>((const uint16_t*)x, (const uint16_t*)Wg, bg, logits, T, d, E);
+    return hipGetLastError();
+}
+
+// Gate and router in one launch; E <= 64 (hipErrorInvalidValue otherwise).
+extern "C" hipError_t moe_launch_gate_route(int dtype, const void* x, const void* Wg, const float* bg, float* logits,
+                                            int T, int d, int E, int k, int normalize, float lambda,
+                                            int32_t* topk_idx, float* topk_w, hipStream_t stream)
+{
+    using namespace moe;
+    const int nt = (E + kGateTile - 1) / kGateTile;
+    if (nt < 1 || nt > 4)
+        return hipErrorInvalidValue;
+    const dim3 grid((T + kGateTile - 1) / kGateTile);
+    // up to 32 experts: 8 wavefronts split the model dimension (as in the
+    // gate kernel); beyond, 4 wavefronts keep the partial tiles at 32 KB
+    auto go = [&](auto et, auto ntc, auto splitc) {
+        typedef decltype(et) ET;
+        constexpr int NT = decltype(ntc)::value, SPLIT = decltype(splitc)::value;
+        moe_gate_route_kernel<ET, NT, SPLIT><<<grid, SPLIT * kWave, 0, stream>>>(
+            (const typename ET::storage*)x, (const typename ET::storage*)Wg, bg, logits, T, d, E, k, normalize,
+            lambda, topk_idx, topk_w);
+    };
+    auto by_nt = [&](auto et) {
+        if (nt == 1)
+            go(et, std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{});
+        else if (nt == 2)
+            go(et, std::integral_constant<int, 2>{}, std::integral_constant<int, 8>{});
+        else if (nt == 3)
+            go(et, std::integral_constant<int, 3>{}, std::integral_constant<int, 4>{});
+        else
+            go(et, std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
+    };
+    if (dtype == 0)
+        by_nt(f32_t{});
+    else
+        by_nt(bf16_t{});
     return hipGetLastError();
 }
 
