@@ -19,8 +19,9 @@ timed on this host's cores: a bounded sample of the Mixtral layer for the
 headline line, and per workload below.
 
 Also on the line: a device-to-device copy's bandwidth (the HBM reference),
-the standalone permutation with its row copy (moe_permute writing x_perm),
-the router statistics, a shared expert, the layer with FP8 expert weights and
+the standalone permutation with its row copy (moe_permute writing x_perm)
+and the combine alone (both per launch, from batches of launches between
+two events, so the events' own cost is spread), the router statistics, a shared expert, the layer with FP8 expert weights and
 the training step ("next_rows"), and every other workload ("other_configs":
 moe_forward median, stage breakdown, roofline against the bound that applies,
 and a CPU-oracle baseline; routing inputs from the seeded generator, expert
@@ -261,6 +262,7 @@ def main():
     log("[bench] copy bandwidth, standalone permutation with its row copy")
     result["copy_bandwidth"] = copy_bandwidth(stream)
     result["permute_row_copy"] = lay.time_permute_copy(args.steps)
+    result["combine_alone"] = lay.time_combine_alone()
     if not args.no_graph:
         result["graph_replay"] = lay.time_graph(args.steps)
 
@@ -424,6 +426,36 @@ class Layer:
         return {"median_ms": float(np.median(ms)), "mean_ms": float(ms.mean()), "min_ms": float(ms.min()),
                 "wall_ms": wall * 1e3 / steps}
 
+    def time_batched(self, call, reps=5, batch=10):
+        """Per-launch time of a short call: events around `batch` calls in a
+        row (so the events' own cost is spread over them), median of `reps`."""
+        import numpy as np
+        import torch
+        for _ in range(3):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(self.stream)
+        for i in range(reps):
+            for _ in range(batch):
+                call()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) / batch
+
+    def time_combine_alone(self):
+        """moe_combine on the step's y_perm and routing, launched back to back.
+        Algorithmic bytes: the kept rows of y_perm read, y written, 8 T k of
+        slot and weight."""
+        c, s = self.case, self.stream.cuda_stream
+        ms = self.time_batched(lambda: self.moe.moe_combine(self.p, self.y_perm, self.slot, self.w, self.y,
+                                                            stream=s))
+        P = int(self.offsets[-1].item())
+        b = 4 if c.dtype == "f32" else 2
+        byts = (c.T + P) * c.d * b + 8.0 * c.T * c.k
+        return {"us": ms * 1e3, "bytes": byts, "gbps": byts / (ms * 1e-3) / 1e9,
+                "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_GBPS,
+                "note": "per launch, 10 launches between two HIP events, median of 5"}
+
     def time_permute_copy(self, steps):
         """moe_permute with its row copy (x_perm written, the path moe_forward
         takes when x is beyond the fused gather's 32-bit offsets), on the
@@ -436,22 +468,15 @@ class Layer:
             xp = torch.empty(c.T * c.k, c.d, dtype=self.dt, device="cuda")
         call = lambda: moe.moe_permute(p, self.idx, self.x, self.counts, self.offsets, self.slot, self.src, xp,  # noqa
                                        self.ws, stream=s)
-        for _ in range(3):
-            call()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record(self.stream)
-        for i in range(steps):
-            call()
-            ev[i + 1].record(self.stream)
-        torch.cuda.synchronize()
-        ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+        ms = self.time_batched(call, reps=max(steps // 10, 5))
         P = int(self.offsets[-1].item())
         b = 4 if c.dtype == "f32" else 2
         byts = (c.T + P) * c.d * b + 12.0 * c.T * c.k
         del xp
         return {"ms": ms, "bytes": byts, "gbps": byts / (ms * 1e-3) / 1e9,
                 "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_GBPS,
-                "note": "count + scan + scatter + row gather kernels of one moe_permute call with x_perm"}
+                "note": "count + scan + scatter + row gather kernels of one moe_permute call with x_perm; "
+                        "per call, 10 calls between two HIP events, median"}
 
     def roofline(self, res):
         """Roofline of the grouped GEMM (up + down) and of the step:
