@@ -227,7 +227,7 @@ def main():
     log(f"[bench] moe_forward: {args.warmup} warm-up + {args.steps} timed steps")
     fwd = lay.time_forward(args.steps, args.warmup)
     log("[bench] stage pass")
-    res = lay.time(args.steps, 2)
+    res = lay.time(args.steps, args.warmup)
     T, d, E, k, F = case.T, case.d, case.E, case.k, case.F
     stage_ms, P = res["stage_ms"], res["P"]
     ms_per_step = fwd["median_ms"]
