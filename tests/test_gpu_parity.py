@@ -81,6 +81,39 @@ def test_gate_logits(name):
     assert np.max(np.abs(host(w) - ow)) <= TOPK_W_ATOL
 
 
+# Gate and router: every column-tile count (E up to 16, 32, 48, 64) and the
+# separate kernels beyond 64 experts; T = 37 leaves a partial 16-token block
+# and d = 192 gives some wavefronts no 32-element block of the model dimension.
+@pytest.mark.parametrize("E", [1, 2, 15, 16, 17, 32, 33, 48, 49, 64, 65])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gate_route_expert_counts(E, dtype):
+    T, d = 37, 192
+    print(f"[gate-route] E={E} {dtype}", flush=True)
+    rng = np.random.default_rng(9000 + 10 * E + (dtype == "f32"))
+    x = moe_inputs._cast(rng.standard_normal((T, d)).astype(np.float32), dtype)
+    Wg = moe_inputs._cast((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32), dtype)
+    bg = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    z_exact, z32 = oracle.gate_logits(x, Wg, bg)
+    x64, w64 = oracle.to_f64(x), oracle.to_f64(Wg)
+    free = unstable_keys(z_exact, logit_eps(x64, w64, bg)) & ~exact_sum_certified(
+        x64, w64, bg, 7 if dtype == "bf16" else 23)
+    for k, normalize, lam in [(min(2, E), False, 1.0), (min(E, 8), True, 2.0), (1, True, 0.5)]:
+        p = moe.problem(T, d, E, k, 64, normalize=normalize, lam=lam, dtype=dtype)
+        logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+        idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        moe.moe_route(p, dev(x), dev(Wg), dev(bg), logits, idx, w)
+        torch.cuda.synchronize()
+        got = host(logits)
+        assert np.array_equal(got[~free], z32[~free])
+        if free.any():
+            assert np.all(np.abs(got[free].astype(np.float64) - z_exact[free]) <= np.spacing(np.abs(z32[free])))
+        # routing decided on the GPU's own logits, as the oracle decides it
+        oi, ow = oracle.route(got, k, normalize, lam)
+        assert np.array_equal(host(idx), oi), (k, normalize)
+        assert np.max(np.abs(host(w).astype(np.float64) - ow)) <= TOPK_W_ATOL
+
+
 # ------------------------------------------------------------------ router on given logits
 def route_gpu(z32, k, normalize=False, lam=1.0):
     T, E = z32.shape
