@@ -1413,8 +1413,9 @@ hipError_t launch_wt(int epi, const GemmArgs& g)
 // Tile configurations (BM, BN, WM, WN, slice bytes, stages, blocks per CU,
 // m-tile group), picked from the mean rows per expert, which the host knows
 // without reading the device-side offsets:
-//   large   >= 512 rows per expert: 256 x 256 tiles, 8 waves (2 per SIMD, 128 x
-//           64 each), the densest tile that fits the register file; 2 x 64 KB
+//   large   >= 512 rows per expert (bf16 forward: >= 256 rows where K >=
+//           kLargeTileMinK): 256 x 256 tiles, 8 waves (2 per SIMD, 128 x 64
+//           each), the densest tile that fits the register file; 2 x 64 KB
 //           of LDS stages
 //   medium  128..511 rows: 128 x 128 tiles, 4 waves, 2 blocks per CU
 //   small   < 128 rows: 64 x 256 tiles, 4 waves (short segments, so tall
@@ -1436,15 +1437,21 @@ hipError_t launch_wt(int epi, const GemmArgs& g)
 #define MOE_SMALL_TILE_FP8 64, 256, 1, 4, 128, 2, 1, 4
 #define MOE_F32_TILE 128, 128, 2, 2, 128, 2, 1, 4
 
+// The bf16 forward takes the large tile from 256 mean rows on where K is at
+// least this long: the 64-expert 512/1024 layer's down-projection (K = 1024,
+// 256 rows per expert) ran 38.9 us on 256 x 256 tiles against 43.5 us on
+// 128 x 128, while its up-projection (K = 512) ran 52.8 against 44.9 us.
+constexpr int kLargeTileMinK = 1024;
+
 // Workspace bytes the tail split needs for a problem with this mean rows per
-// expert (the partial tiles of the configuration the launcher picks).
-// dtype: 0 fp32, 1 bf16, 2 FP8.
+// expert (the partial tiles of the largest configuration the launcher may
+// pick for it).  dtype: 0 fp32, 1 bf16, 2 FP8.
 extern "C" size_t moe_grouped_gemm_partial_bytes(int dtype, int mean_rows)
 {
     size_t tile_floats;
     if (dtype == 0)
         tile_floats = GemmShape<f32_t, MOE_F32_TILE>::kTileFloats;
-    else if (mean_rows >= 512)
+    else if (mean_rows >= 256)
         tile_floats = GemmShape<bf16_t, MOE_LARGE_TILE>::kTileFloats;
     else if (mean_rows >= 128)
         tile_floats = GemmShape<bf16_t, MOE_MEDIUM_TILE>::kTileFloats;
@@ -1471,7 +1478,7 @@ extern "C" hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A,
                         EpiArgs{nullptr, nullptr, aux_in, aux_out, aux_ld}, stream};
     if (dtype == 0)
         return launch_epi<f32_t, f32_t, GemmShape<f32_t, MOE_F32_TILE>>(epi, g);
-    if (mean_rows >= 512)
+    if (mean_rows >= 512 || (mean_rows >= 256 && K >= kLargeTileMinK))
         return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_LARGE_TILE>>(epi, g);
     if (mean_rows >= 128)
         return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, g);

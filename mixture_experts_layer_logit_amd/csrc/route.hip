@@ -137,8 +137,9 @@ __global__ __launch_bounds__(kGateSplit * kWave) void moe_gate_logits_kernel(
 // same as selecting on the probability, without depending on how either side
 // rounds exp or the reductions.
 //
-// Probabilities are formed in fp64 (mean, population variance, softmax) and
-// only the k selected ones are stored, rounded to fp32.
+// Probabilities are formed in fp64 (mean, population variance, softmax: the
+// denominator's terms from the fp32 exp, see token_probs) and only the k
+// selected ones are stored, rounded to fp32.
 __device__ __forceinline__ uint32_t ordered_key(float f)
 {
     uint32_t u = __float_as_uint(f);
@@ -181,12 +182,21 @@ __device__ __forceinline__ double wave_max(double v) { return group_max<kWave>(v
 // the wavefront): z[i] is the logit of expert lane + G i, lane being the
 // index within the group (0 past E).  Scores s in fp64 are the logit, or
 // lambda * (z - mu) / sigma (population sigma over the E experts; sigma == 0
-// gives s = 0); p_e = ex[i] / denom with ex = exp(s - max s).
-template <int VPL, int G = kWave>
+// gives s = 0); p_e = ex[i] / denom with ex = exp(s - max s), s and m = max s
+// returned as well.
+// FAST (the forward router, which stores only the k selected weights): the
+// terms of the denominator are exp(s - m) of the fp32-rounded argument in
+// fp32 (one hardware exp each instead of a software fp64 exp), summed in
+// fp64.  Every term lies in (0, 1] with a relative error of a few fp32 units
+// (the argument's rounding adds at most |s - m| 2^-24, which matters only
+// where the term itself is tiny), so the sum is within about 2^-21 relative
+// of the fp64 one; the selected numerators are recomputed in fp64
+// (select_topk), so a weight differs from the all-fp64 value by at most a
+// few fp32 units.
+template <int VPL, int G = kWave, bool FAST = false>
 __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int E, int normalize, float lambda,
-                                            double (&ex)[VPL], double& denom)
+                                            double (&ex)[VPL], double& denom, double (&s)[VPL], double& m)
 {
-    double s[VPL];
     if (normalize) {
         double part = 0.0;
 #pragma unroll
@@ -208,7 +218,7 @@ __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int
         for (int i = 0; i < VPL; ++i)
             s[i] = (double)z[i];
     }
-    double m = -INFINITY;
+    m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         if (lane + G * i < E)
@@ -217,18 +227,29 @@ __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int
     double part = 0.0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        ex[i] = (lane + G * i < E) ? exp(s[i] - m) : 0.0;
+        if constexpr (FAST)
+            ex[i] = (lane + G * i < E) ? (double)__expf((float)(s[i] - m)) : 0.0;
+        else
+            ex[i] = (lane + G * i < E) ? exp(s[i] - m) : 0.0;
         part += ex[i];
     }
     denom = group_sum<G>(part);
 }
+template <int VPL, int G = kWave>
+__device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int E, int normalize, float lambda,
+                                            double (&ex)[VPL], double& denom)
+{
+    double s[VPL], m;
+    token_probs<VPL, G, false>(z, lane, E, normalize, lambda, ex, denom, s, m);
+}
 
 // The k selections of one token held by a group of G lanes: k rounds of a
 // group-wide maximum of the keys; the owner of the winning expert hands its
-// exp term to the group and clears the key.  Lane 0 of the group stores.
+// exp term, exp(s - m) in fp64, to the group and clears the key.  Lane 0 of
+// the group stores.
 template <int VPL, int G = kWave>
-__device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], const double (&ex)[VPL], double denom, int lane,
-                                            int t, int k, int32_t* __restrict__ topk_idx,
+__device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], const double (&s)[VPL], double m, double denom,
+                                            int lane, int t, int k, int32_t* __restrict__ topk_idx,
                                             float* __restrict__ topk_w)
 {
     for (int j = 0; j < k; ++j) {
@@ -240,14 +261,15 @@ __device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], const double (
         const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
         const int owner = e % G;
         const int reg = e / G;
-        double mine = 0.0;
+        double sel = 0.0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             if (i == reg && lane == owner) {
-                mine = ex[i];
+                sel = s[i];
                 key[i] = 0;  // taken
             }
         }
+        const double mine = lane == owner ? exp(sel - m) : 0.0;
         const double pe = __shfl(mine, owner, G) / denom;
         if (lane == 0) {
             topk_idx[(size_t)t * k + j] = e;
@@ -275,9 +297,9 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
         z[i] = e < E ? zt[e] : 0.0f;
         key[i] = e < E ? ((uint64_t)ordered_key(z[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
     }
-    double ex[VPL], denom;
-    token_probs<VPL>(z, lane, E, normalize, lambda, ex, denom);
-    select_topk<VPL>(key, ex, denom, lane, t, k, topk_idx, topk_w);
+    double ex[VPL], denom, sc[VPL], m;
+    token_probs<VPL, kWave, true>(z, lane, E, normalize, lambda, ex, denom, sc, m);
+    select_topk<VPL>(key, sc, m, denom, lane, t, k, topk_idx, topk_w);
 }
 
 // ---------------------------------------------------------------- gate + router
@@ -387,9 +409,9 @@ __global__ __launch_bounds__(SPLIT * kWave) void moe_gate_route_kernel(
         z[v] = e < E ? s_z[tok][e] : 0.0f;
         key[v] = e < E ? ((uint64_t)ordered_key(z[v]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
     }
-    double ex[VPL], denom;
-    token_probs<VPL, G>(z, li, E, normalize, lambda, ex, denom);
-    select_topk<VPL, G>(key, ex, denom, li, t, k, topk_idx, topk_w);
+    double ex[VPL], denom, sc[VPL], m;
+    token_probs<VPL, G, true>(z, li, E, normalize, lambda, ex, denom, sc, m);
+    select_topk<VPL, G>(key, sc, m, denom, li, t, k, topk_idx, topk_w);
 }
 
 // ---------------------------------------------------------------- router backward

@@ -109,6 +109,10 @@ SMALL = {
     # capacity factor of 1 that clips the two hottest experts.
     "mixtral_m": FULL["mixtral"].with_(name="mixtral_m", T=2048, d=512, E=6, F=768, seed=2006),
     "mixtral_m_cap": FULL["mixtral"].with_(name="mixtral_m_cap", T=2048, d=512, E=6, F=768, seed=2007, cf=1.0),
+    # A FastMoE-family layer with 256 rows per expert and a 1024-wide hidden
+    # layer: its down-projection (K = 1024) takes the 256 x 256 tile, its
+    # up-projection (K = 256) the 128 x 128 one.
+    "fastmoe_m": FULL["fastmoe_txl"].with_(name="fastmoe_m", T=2048, d=256, E=16, seed=2008),
 }
 
 # Large token counts at small widths: index arithmetic, grids and chunk loops
