@@ -18,7 +18,8 @@ up-projection grouped GEMM with its split-K reduction).  The CPU oracle is
 timed on this host's cores: a bounded sample of the Mixtral layer for the
 headline line, and per workload below.
 
-Also on the line: a device-to-device copy's bandwidth (the HBM reference),
+Also on the line: the same expert GEMMs through the vendor library (one
+hipBLASLt product per expert, for reference), a device-to-device copy's bandwidth (the HBM reference),
 the standalone permutation with its row copy (moe_permute writing x_perm)
 and the combine alone (both per launch, from batches of launches between
 two events, so the events' own cost is spread), the router statistics, a shared expert, the layer with FP8 expert weights and
@@ -263,6 +264,12 @@ def main():
     result["copy_bandwidth"] = copy_bandwidth(stream)
     result["permute_row_copy"] = lay.time_permute_copy(args.steps)
     result["combine_alone"] = lay.time_combine_alone()
+    if case.dtype == "bf16":
+        log("[bench] the expert GEMMs through the vendor library, for reference")
+        ref = lay.time_library_reference()
+        ref["ours_vs_library_up"] = ref["up"]["ms"] / stage_ms["expert_up"]
+        ref["ours_vs_library_down"] = ref["down"]["ms"] / stage_ms["expert_down"]
+        result["library_reference"] = ref
     if not args.no_graph:
         result["graph_replay"] = lay.time_graph(args.steps)
 
@@ -565,6 +572,55 @@ class Layer:
             "expert_loads": self.counts.cpu().tolist() if c.E <= 64 else
             {"min": int(self.counts.min()), "max": int(self.counts.max())},
         }
+
+    def time_library_reference(self, reps=10):
+        """The same expert GEMMs through the vendor library, for reference:
+        one torch F.linear (hipBLASLt, bf16 in, fp32 accumulate) per expert
+        over that expert's permuted rows, no activation, with the step's
+        routing; the up-projection's 8 products then the down-projection's,
+        HIP events around each sequence on the layer's stream.  It reads a
+        permuted copy of x (made before the timed region) where the library
+        path cannot gather, and it writes u and the outputs without the
+        activation, so it does slightly less work than moe_expert_up."""
+        import numpy as np
+        import torch
+        import torch.nn.functional as Fn
+        c = self.case
+        off = [int(v) for v in self.offsets.cpu()]
+        with torch.cuda.stream(self.stream):
+            xp = self.x.index_select(0, self.src[:off[-1]].long())
+            u = torch.empty(off[-1], self.n1, dtype=self.dt, device="cuda")
+            hh = torch.empty(off[-1], c.F, dtype=self.dt, device="cuda")
+            yp = torch.empty(off[-1], c.d, dtype=self.dt, device="cuda")
+
+        def up():
+            for e in range(c.E):
+                if off[e + 1] > off[e]:
+                    torch.matmul(xp[off[e]:off[e + 1]], self.W1[e].t(), out=u[off[e]:off[e + 1]])
+
+        def down():
+            for e in range(c.E):
+                if off[e + 1] > off[e]:
+                    torch.matmul(hh[off[e]:off[e + 1]], self.W2[e].t(), out=yp[off[e]:off[e + 1]])
+        out = {}
+        P = off[-1]
+        for name, fn, flops in (("up", up, 2.0 * P * c.d * self.n1), ("down", down, 2.0 * P * c.F * c.d)):
+            with torch.cuda.stream(self.stream):
+                for _ in range(3):
+                    fn()
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+                ev[0].record(self.stream)
+                for i in range(reps):
+                    fn()
+                    ev[i + 1].record(self.stream)
+            torch.cuda.synchronize()
+            ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+            out[name] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                         "frac_of_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[c.dtype]}
+        del xp, u, hh, yp
+        out["note"] = ("hipBLASLt through torch.matmul, one product per expert over its permuted rows "
+                       "(A contiguous, W[e] read as stored, no activation); median of %d sequences" % reps)
+        return out
 
     def time_next_rows(self, steps, res):
         """Router statistics on the step's routing; a shared expert of width F
