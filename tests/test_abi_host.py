@@ -55,7 +55,9 @@ def partial_floats(T, E, k, b, cf):
         rows = min(rows, C)
     if b == 4:
         return 128 * 128
-    return 256 * 256 if rows >= 512 else 128 * 128 if rows >= 128 else 64 * 256
+    # from 256 rows on the bf16 forward may take the 256 x 256 tile (where K
+    # is long enough), so the workspace holds partial tiles of that size
+    return 256 * 256 if rows >= 256 else 128 * 128 if rows >= 128 else 64 * 256
 
 
 def workspace_formula(T, d, E, k, F, b, cf=0.0):
@@ -72,6 +74,7 @@ def workspace_formula(T, d, E, k, F, b, cf=0.0):
 @pytest.mark.parametrize("T,d,E,k,F,dt,cf", [(256, 64, 4, 2, 128, "f32", 0.0),
                                              (4096, 4096, 8, 2, 14336, "bf16", 0.0),
                                              (1, 64, 1, 1, 64, "bf16", 0.0),
+                                             (8192, 512, 64, 2, 1024, "bf16", 0.0),
                                              (16384, 1024, 512, 2, 512, "bf16", 0.0),
                                              (8192, 2048, 16, 2, 1408, "bf16", 1.25),
                                              (8192, 2048, 64, 2, 1408, "bf16", 0.25),
