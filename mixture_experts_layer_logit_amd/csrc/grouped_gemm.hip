@@ -969,17 +969,22 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             }
         }
 
-        auto issue = [&](int kt, int stage) {
+        // part: 0 the activation rows of the slice, 1 the weight rows, 2 both
+        auto issue = [&](int kt, int stage, int part = 2) {
             const uint32_t soff = (uint32_t)kt * S::RB;
             // WT: the slice is kBK rows further down W[e]
             const uint32_t soffB = WT ? (uint32_t)kt * S::kBK * (uint32_t)Nw * 2u : soff;
             const uint32_t dst = stage_addr[stage] + wave * 1024;
+            if (part != 1) {
 #pragma unroll
-            for (int i = 0; i < S::kBlkA; ++i)
-                dma16(rsA, dst + kWaves * i * 1024, voffA[i], soff);
+                for (int i = 0; i < S::kBlkA; ++i)
+                    dma16(rsA, dst + kWaves * i * 1024, voffA[i], soff);
+            }
+            if (part != 0) {
 #pragma unroll
-            for (int i = 0; i < S::kBlkB; ++i)
-                dma16(rsW, dst + S::kLdsA + kWaves * i * 1024, voffB[i], soffB);
+                for (int i = 0; i < S::kBlkB; ++i)
+                    dma16(rsW, dst + S::kLdsA + kWaves * i * 1024, voffB[i], soffB);
+            }
         };
 
         Acc<S> acc;
@@ -1135,11 +1140,20 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 mfmas(fr0, LC);
                 interleave();
             }
+            // Two-stage rings request the slice's activation rows at the
+            // barrier and its weight rows after this k-step's MFMAs: issued
+            // together, the 8 waves' DMA filled the address unit's queues
+            // right after every barrier (SQ_VMEM_TA_*_FIFO_FULL) and held up
+            // the MFMAs behind them.  Split, on one box each: the Mixtral
+            // up-projection 1.70-1.72 -> 1.68-1.70 ms, its training forward
+            // 2.72 -> 2.66 ms and backward 6.50 -> 6.39 ms.  The next
+            // barrier's wait covers both parts.
+            constexpr bool kSplit = S::S == 2;
             if (kt + 1 < k1) {
                 wait_slices(min(S::S - 2, k1 - 2 - kt));
                 lds_barrier();
                 if (kt + S::S < k1)
-                    issue(kt + S::S, cur_stage);
+                    issue(kt + S::S, cur_stage, kSplit ? 0 : 2);
             }
             // After the last slice this reads stale data nobody uses (an
             // in-bounds LDS read; the next tile's __syncthreads waits for it
@@ -1149,6 +1163,10 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
             read_frags(nxt, 0, fr0, LC);
             mfmas(fr1, LC);
             interleave();
+            if constexpr (kSplit) {
+                if (kt + S::S < k1)
+                    issue(kt + S::S, cur_stage, 1);
+            }
         };
         static_assert(S::kKSteps % 2 == 0, "k-steps per slice must be even");
 
