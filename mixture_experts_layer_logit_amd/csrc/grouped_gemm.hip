@@ -1091,10 +1091,43 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                 // k-steps' reads above the MFMAs, which would need a second
                 // register set for the fragments)
                 static_assert(S::kKSteps == 2, "FP8 slices are 128 bytes: 2 k-steps");
-                mfmas(fr0, LC);
-                __builtin_amdgcn_sched_barrier(0);
-                read_frags(cur, 1, fr0, LC);
-                __builtin_amdgcn_sched_barrier(0);
+                static_assert(S::kFN == 2, "FP8 k-step order assumes two weight blocks");
+                // One k-step: MFMAs in (weight block j, row fragment i) order;
+                // each operand is refilled with the next k-step's data as soon
+                // as its last MFMA of this k-step is issued (a[0] after the
+                // j = 0 group, b[i] after MFMA (i, 1), a[1] at the end), so
+                // every refill has at least three MFMAs to land before the
+                // next k-step uses it.
+                auto kstep = [&](const uint8_t* src, int kk) {
+                    auto rd = [&](uint32_t off) { return *reinterpret_cast<const i32x4*>(src + off); };
+                    auto mf = [&](int i, int j) {
+                        acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr0.a[j], fr0.b[i], acc.v[i][j],
+                                                                                      0, 0, 0, 127, 0, 127);
+                    };
+#pragma unroll
+                    for (int i = 0; i < L; ++i)
+                        mf(i, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (L > 0) {
+                        fr0.a[0].lo = rd(rdB[kk][0]);
+                        fr0.a[0].hi = rd(rdB[kk][1]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < L; ++i) {
+                        mf(i, 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        fr0.b[i].lo = rd(rdA[kk][0] + i * 32 * S::RB);
+                        fr0.b[i].hi = rd(rdA[kk][1] + i * 32 * S::RB);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if constexpr (L > 0) {
+                        fr0.a[1].lo = rd(rdB[kk][0] + 32 * S::RB);
+                        fr0.a[1].hi = rd(rdB[kk][1] + 32 * S::RB);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                kstep(cur, 1);
                 const bool more = kt + 1 < k1;
                 if (more) {
                     wait_slices(min(S::S - 2, k1 - 2 - kt));
@@ -1102,10 +1135,7 @@ void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const i
                     if (kt + S::S < k1)
                         issue(kt + S::S, cur_stage);
                 }
-                mfmas(fr0, LC);  // one call site: the accumulators keep one register set
-                __builtin_amdgcn_sched_barrier(0);
-                read_frags(nxt, 0, fr0, LC);  // unconditional: see below
-                __builtin_amdgcn_sched_barrier(0);
+                kstep(nxt, 0);  // after the last slice this reads stale, in-bounds data nobody uses
                 return;
             }
             // 256x256 tiles: each k-step's 8 MFMAs alternate with the next
