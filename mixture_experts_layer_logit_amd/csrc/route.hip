@@ -148,32 +148,69 @@ __device__ __forceinline__ uint32_t ordered_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Reductions over aligned groups of G lanes (G = 64: the wavefront).
+// Reductions over aligned groups of G lanes (G = 16, 32 or 64: the
+// wavefront).  Within each row of 16 lanes four DPP steps pair lane i with
+// i ^ 1, i ^ 2, 7 - i (within 8) and 15 - i: every step combines two partial
+// results that are bitwise equal on both lanes of a pair (the operations are
+// commutative), so after them every lane of a row holds the same row result,
+// with no trip through the LDS crossbar.  Rows are then combined by one
+// shuffle (G = 32) or, for the whole wavefront, by reading the four row
+// results as wave-uniform values and combining them in one fixed order.
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+template <int G, typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, Op op)
+{
+    static_assert(sizeof(T) == 8, "64-bit values");
+    static_assert(G == 16 || G == 32 || G == 64, "groups of whole rows");
+    auto step = [&](auto ctrl) {
+        constexpr int C = decltype(ctrl)::value;
+        v = op(v, __builtin_bit_cast(T, dpp_u64<C>(__builtin_bit_cast(uint64_t, v))));
+    };
+    step(std::integral_constant<int, kDppXor1>{});
+    step(std::integral_constant<int, kDppXor2>{});
+    step(std::integral_constant<int, kDppHalfMirror>{});
+    step(std::integral_constant<int, kDppMirror>{});
+    if constexpr (G == 32) {
+        v = op(v, __shfl_xor(v, 16));
+    } else if constexpr (G == 64) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const T r0 = __builtin_bit_cast(T, readlane_u64(u, 0)), r1 = __builtin_bit_cast(T, readlane_u64(u, 16));
+        const T r2 = __builtin_bit_cast(T, readlane_u64(u, 32)), r3 = __builtin_bit_cast(T, readlane_u64(u, 48));
+        v = op(op(r0, r1), op(r2, r3));
+    }
+    return v;
+}
 template <int G>
 __device__ __forceinline__ double group_sum(double v)
 {
-#pragma unroll
-    for (int o = G / 2; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    return group_reduce<G>(v, [](double a, double b) { return a + b; });
 }
 template <int G>
 __device__ __forceinline__ double group_max(double v)
 {
-#pragma unroll
-    for (int o = G / 2; o >= 1; o >>= 1)
-        v = fmax(v, __shfl_xor(v, o));
-    return v;
+    return group_reduce<G>(v, [](double a, double b) { return fmax(a, b); });
 }
 template <int G>
 __device__ __forceinline__ uint64_t group_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int o = G / 2; o >= 1; o >>= 1) {
-        const uint64_t w = __shfl_xor(v, o);
-        v = w > v ? w : v;
-    }
-    return v;
+    return group_reduce<G>(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ double wave_sum(double v) { return group_sum<kWave>(v); }
 __device__ __forceinline__ double wave_max(double v) { return group_max<kWave>(v); }
@@ -612,8 +649,9 @@ __global__ __launch_bounds__(256) void moe_router_stats_kernel(const float* __re
 
 // Pass 2, one wavefront per item e in [0, E] (E is the Z-loss sum): lanes
 // add partial[b][e] for b = lane, lane + 64, ... in order, then a fixed
-// shuffle tree adds the lanes.  Writes mean_prob[e] = sum / T and
-// frac[e] = counts[e] / (T k) and keeps terms[e] = frac[e] * mean_prob[e]
+// reduction tree (group_reduce) adds the lanes.  Writes mean_prob[e] =
+// sum / T and frac[e] = counts[e] / (T k) and keeps terms[e] = frac[e] *
+// mean_prob[e]
 // (terms[E] = Z-loss sum) for pass 3.
 __global__ __launch_bounds__(256) void moe_router_stats_reduce_kernel(const double* __restrict__ partial,
                                                                        int nblocks, int T, int E, int k,
@@ -645,7 +683,7 @@ __global__ __launch_bounds__(256) void moe_router_stats_reduce_kernel(const doub
 
 // Pass 3, one block of 1024 threads (thread e owns expert e):
 //   scalars = {E * sum_e terms[e], terms[E] / T, (T k - offsets[E]) / (T k)}
-// with the sum over experts a fixed tree (wavefront shuffles, then the 16
+// with the sum over experts a fixed tree (the wavefront reduction, then the 16
 // wavefronts in order).
 __global__ __launch_bounds__(1024) void moe_router_stats_final_kernel(const double* __restrict__ terms, int T,
                                                                       int E, int k,
