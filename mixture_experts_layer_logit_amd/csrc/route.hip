@@ -125,11 +125,12 @@ __global__ __launch_bounds__(kGateSplit * kWave) void moe_gate_logits_kernel(
 }
 
 // ---------------------------------------------------------------- router
-// One wavefront per token.  Expert e lives in lane e % 64, register e / 64.
+// One group of G = 16, 32 or 64 lanes per token.  Expert e lives in group
+// lane e % G, register e / G.
 //
 // Selection key: the raw fp32 logit mapped to an order-preserving 32-bit
 // integer (-0 folded onto +0), in the high half of a 64-bit key whose low
-// half is (0xffffffff - e); the wavefront-wide maximum is then the largest
+// half is (0xffffffff - e); the group-wide maximum is then the largest
 // logit with ties going to the lowest expert index.  k rounds of max-reduce
 // give the k experts in descending order.  The standardise-and-scale
 // normalisation and the softmax are strictly increasing maps for lambda > 0
@@ -230,31 +231,39 @@ __device__ __forceinline__ double wave_max(double v) { return group_max<kWave>(v
 // of the fp64 one; the selected numerators are recomputed in fp64
 // (select_topk), so a weight differs from the all-fp64 value by at most a
 // few fp32 units.
+// Score of one logit: z itself, or lambda * (z - mu) / sigma when
+// normalised (sigma == 0 gives 0).
+__device__ __forceinline__ double logit_score(float z, int normalize, float lambda, double mu, double sigma)
+{
+    if (!normalize)
+        return (double)z;
+    return sigma == 0.0 ? 0.0 : (double)lambda * ((double)z - mu) / sigma;
+}
+
 template <int VPL, int G = kWave, bool FAST = false>
 __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int E, int normalize, float lambda,
-                                            double (&ex)[VPL], double& denom, double (&s)[VPL], double& m)
+                                            double (&ex)[VPL], double& denom, double& m, double& mu, double& sigma)
 {
+    mu = 0.0;
+    sigma = 0.0;
     if (normalize) {
         double part = 0.0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
             part += (lane + G * i < E) ? (double)z[i] : 0.0;
-        const double mu = group_sum<G>(part) / E;
+        mu = group_sum<G>(part) / E;
         part = 0.0;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const double c = (double)z[i] - mu;
             part += (lane + G * i < E) ? c * c : 0.0;
         }
-        const double sigma = sqrt(group_sum<G>(part) / E);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            s[i] = sigma == 0.0 ? 0.0 : (double)lambda * ((double)z[i] - mu) / sigma;
-    } else {
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            s[i] = (double)z[i];
+        sigma = sqrt(group_sum<G>(part) / E);
     }
+    double s[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        s[i] = logit_score(z[i], normalize, lambda, mu, sigma);
     m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
@@ -276,18 +285,35 @@ template <int VPL, int G = kWave>
 __device__ __forceinline__ void token_probs(const float (&z)[VPL], int lane, int E, int normalize, float lambda,
                                             double (&ex)[VPL], double& denom)
 {
-    double s[VPL], m;
-    token_probs<VPL, G, false>(z, lane, E, normalize, lambda, ex, denom, s, m);
+    double m, mu, sigma;
+    token_probs<VPL, G, false>(z, lane, E, normalize, lambda, ex, denom, m, mu, sigma);
+}
+
+// Selection key of expert e with logit z: the order-preserving 32-bit image
+// of the fp32 logit above (0xffffffff - e), so that the largest key is the
+// largest logit with ties going to the lowest expert index.  Real keys are
+// never 0, which marks an empty or taken slot.
+__device__ __forceinline__ uint64_t select_key(float z, int e)
+{
+    return ((uint64_t)ordered_key(z) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+// The logit a key was made from (-0 comes back as +0, which scores alike).
+__device__ __forceinline__ float key_logit(uint64_t key)
+{
+    const uint32_t o = (uint32_t)(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
 // The k selections of one token held by a group of G lanes: k rounds of a
-// group-wide maximum of the keys; the owner of the winning expert hands its
-// exp term, exp(s - m) in fp64, to the group and clears the key.  Lane 0 of
-// the group stores.
+// group-wide maximum of the keys; every lane clears the winning key where
+// it holds it and forms the winner's weight exp(s - m) / denom in fp64 from
+// the logit inside the key (the same score as in the denominator), so the
+// weight is group-uniform and needs no exchange.  Lane 0 of the group
+// stores.
 template <int VPL, int G = kWave>
-__device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], const double (&s)[VPL], double m, double denom,
-                                            int lane, int t, int k, int32_t* __restrict__ topk_idx,
-                                            float* __restrict__ topk_w)
+__device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], int normalize, float lambda, double mu,
+                                            double sigma, double m, double denom, int lane, int t, int k,
+                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w)
 {
     for (int j = 0; j < k; ++j) {
         uint64_t best = 0;
@@ -295,19 +321,11 @@ __device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], const double (
         for (int i = 0; i < VPL; ++i)
             best = key[i] > best ? key[i] : best;
         best = group_max_u64<G>(best);
-        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
-        const int owner = e % G;
-        const int reg = e / G;
-        double sel = 0.0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            if (i == reg && lane == owner) {
-                sel = s[i];
-                key[i] = 0;  // taken
-            }
-        }
-        const double mine = lane == owner ? exp(sel - m) : 0.0;
-        const double pe = __shfl(mine, owner, G) / denom;
+        for (int i = 0; i < VPL; ++i)
+            key[i] = key[i] == best ? 0 : key[i];
+        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+        const double pe = exp(logit_score(key_logit(best), normalize, lambda, mu, sigma) - m) / denom;
         if (lane == 0) {
             topk_idx[(size_t)t * k + j] = e;
             topk_w[(size_t)t * k + j] = (float)pe;
@@ -315,28 +333,30 @@ __device__ __forceinline__ void select_topk(uint64_t (&key)[VPL], const double (
     }
 }
 
-template <int VPL>
+// One group of G lanes per token (256 / G tokens per block): expert e in
+// group lane e % G, register e / G.
+template <int VPL, int G>
 __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int normalize, float lambda,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w)
 {
-    const int lane = lane_id();
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int li = threadIdx.x % G;
+    const int t = blockIdx.x * (256 / G) + threadIdx.x / G;
     if (t >= T)
-        return;
+        return;  // whole groups leave together
     const float* zt = logits + (size_t)t * E;
     float z[VPL];
     uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
+        const int e = li + G * i;
         z[i] = e < E ? zt[e] : 0.0f;
-        key[i] = e < E ? ((uint64_t)ordered_key(z[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
+        key[i] = e < E ? select_key(z[i], e) : 0;
     }
-    double ex[VPL], denom, sc[VPL], m;
-    token_probs<VPL, kWave, true>(z, lane, E, normalize, lambda, ex, denom, sc, m);
-    select_topk<VPL>(key, sc, m, denom, lane, t, k, topk_idx, topk_w);
+    double ex[VPL], denom, m, mu, sigma;
+    token_probs<VPL, G, true>(z, li, E, normalize, lambda, ex, denom, m, mu, sigma);
+    select_topk<VPL, G>(key, normalize, lambda, mu, sigma, m, denom, li, t, k, topk_idx, topk_w);
 }
 
 // ---------------------------------------------------------------- gate + router
@@ -444,11 +464,11 @@ __global__ __launch_bounds__(SPLIT * kWave) void moe_gate_route_kernel(
     for (int v = 0; v < VPL; ++v) {
         const int e = li + G * v;
         z[v] = e < E ? s_z[tok][e] : 0.0f;
-        key[v] = e < E ? ((uint64_t)ordered_key(z[v]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0;
+        key[v] = e < E ? select_key(z[v], e) : 0;
     }
-    double ex[VPL], denom, sc[VPL], m;
-    token_probs<VPL, G, true>(z, li, E, normalize, lambda, ex, denom, sc, m);
-    select_topk<VPL, G>(key, sc, m, denom, li, t, k, topk_idx, topk_w);
+    double ex[VPL], denom, m, mu, sigma;
+    token_probs<VPL, G, true>(z, li, E, normalize, lambda, ex, denom, m, mu, sigma);
+    select_topk<VPL, G>(key, normalize, lambda, mu, sigma, m, denom, li, t, k, topk_idx, topk_w);
 }
 
 // ---------------------------------------------------------------- router backward
@@ -765,18 +785,28 @@ extern "C" hipError_t moe_launch_router(const float* logits, int T, int E, int k
                                         int32_t* topk_idx, float* topk_w, hipStream_t stream)
 {
     using namespace moe;
-    const dim3 grid((T + 3) / 4), block(256);
-    const int vpl = (E + kWave - 1) / kWave;
-    if (vpl <= 1)
-        moe_router_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
-    else if (vpl <= 2)
-        moe_router_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
-    else if (vpl <= 4)
-        moe_router_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
-    else if (vpl <= 8)
-        moe_router_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    // groups of 16 lanes up to 256 experts, then 32 and 64 lanes: at most 16
+    // experts per lane (32 per lane at 512 experts took 238 registers and
+    // ran slower at two wavefronts per SIMD)
+    auto go = [&](auto vplc, auto gc) {
+        constexpr int VPL = decltype(vplc)::value, G = decltype(gc)::value;
+        const dim3 grid((T + 256 / G - 1) / (256 / G)), block(256);
+        moe_router_kernel<VPL, G><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+    };
+    if (E <= 16)
+        go(std::integral_constant<int, 1>{}, std::integral_constant<int, 16>{});
+    else if (E <= 32)
+        go(std::integral_constant<int, 2>{}, std::integral_constant<int, 16>{});
+    else if (E <= 64)
+        go(std::integral_constant<int, 4>{}, std::integral_constant<int, 16>{});
+    else if (E <= 128)
+        go(std::integral_constant<int, 8>{}, std::integral_constant<int, 16>{});
+    else if (E <= 256)
+        go(std::integral_constant<int, 16>{}, std::integral_constant<int, 16>{});
+    else if (E <= 512)
+        go(std::integral_constant<int, 16>{}, std::integral_constant<int, 32>{});
     else
-        moe_router_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, k, normalize, lambda, topk_idx, topk_w);
+        go(std::integral_constant<int, 16>{}, std::integral_constant<int, 64>{});
     return hipGetLastError();
 }
 
