@@ -107,6 +107,7 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ ch
 // offsets out).  That costs each block nchunks*E reads, so it is used when
 // that product is at most kFuseScanMax, and saves the scan's launch.
 constexpr long long kFuseScanMax = 64 * 1024;
+constexpr int kScanBatch = 32;
 
 template <bool kFused>
 __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __restrict__ topk_idx, int T, int E,
@@ -129,11 +130,19 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
     if constexpr (kFused) {
         for (int e = threadIdx.x; e < E; e += kChunk) {
             int b = 0, tot = 0;  // integer sums: the order does not matter
-#pragma unroll 8
-            for (int c = 0; c < nchunks; ++c) {
-                const int v = chunk_cnt[(size_t)c * E + e];
-                b += c < (int)blockIdx.x ? v : 0;
-                tot += v;
+            // 32 chunk counts in flight at a time: the sums are bound by
+            // the latency of these loads, not by their bytes
+            for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+                int v[kScanBatch];
+#pragma unroll
+                for (int q = 0; q < kScanBatch; ++q)
+                    v[q] = chunk_cnt[(size_t)min(c0 + q, nchunks - 1) * E + e];
+#pragma unroll
+                for (int q = 0; q < kScanBatch; ++q) {
+                    const int c = c0 + q;
+                    b += c < (int)blockIdx.x ? v[q] : 0;
+                    tot += c < nchunks ? v[q] : 0;
+                }
             }
             s_base[e] = b;
             s_off[e] = (C >= 0 && tot > C) ? (int)C : tot;  // kept, scanned below

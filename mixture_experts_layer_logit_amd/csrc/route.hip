@@ -348,10 +348,15 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const float* __restrict
     const float* zt = logits + (size_t)t * E;
     float z[VPL];
     uint64_t key[VPL];
+    // every load from a clamped index, the padding zeroed afterwards: a load
+    // under the index test is waited on before the next one is issued
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        z[i] = zt[min(li + G * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = li + G * i;
-        z[i] = e < E ? zt[e] : 0.0f;
+        z[i] = e < E ? z[i] : 0.0f;
         key[i] = e < E ? select_key(z[i], e) : 0;
     }
     double ex[VPL], denom, m, mu, sigma;
@@ -461,9 +466,12 @@ __global__ __launch_bounds__(SPLIT * kWave) void moe_gate_route_kernel(
     float z[VPL];
     uint64_t key[VPL];
 #pragma unroll
+    for (int v = 0; v < VPL; ++v)
+        z[v] = s_z[tok][min(li + G * v, kCols - 1)];
+#pragma unroll
     for (int v = 0; v < VPL; ++v) {
         const int e = li + G * v;
-        z[v] = e < E ? s_z[tok][e] : 0.0f;
+        z[v] = e < E ? z[v] : 0.0f;
         key[v] = e < E ? select_key(z[v], e) : 0;
     }
     double ex[VPL], denom, m, mu, sigma;
