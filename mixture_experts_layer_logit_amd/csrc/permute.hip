@@ -35,11 +35,15 @@ __global__ __launch_bounds__(kChunk) void moe_count_kernel(const int32_t* __rest
     __syncthreads();
     const int t = blockIdx.x * kChunk + threadIdx.x;
     if (t < T) {
-        for (int j = 0; j < k; ++j) {
-            const int e = topk_idx[(size_t)t * k + j];
-            if (e >= 0 && e < E)
-                atomicAdd(&hist[e], 1);
-        }
+        // the token's k choices loaded together, then counted
+        int ch[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            ch[j] = j < k ? topk_idx[(size_t)t * k + j] : -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (ch[j] >= 0 && ch[j] < E)
+                atomicAdd(&hist[ch[j]], 1);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kChunk)
@@ -196,12 +200,11 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(const int32_t* __re
     const bool live = t < T;
     int my[8];
 #pragma unroll
+    for (int j = 0; j < 8; ++j)
+        my[j] = (j < k && live) ? topk_idx[(size_t)t * k + j] : -1;
+#pragma unroll
     for (int j = 0; j < 8; ++j) {
-        my[j] = -1;
-        if (j < k && live) {
-            const int e = topk_idx[(size_t)t * k + j];
-            my[j] = (e >= 0 && e < E) ? e : -1;
-        }
+        my[j] = (my[j] >= 0 && my[j] < E) ? my[j] : -1;
         if (my[j] >= 0)
             atomicAdd(&wave_cnt[wave][my[j]], 1);
     }
