@@ -78,6 +78,9 @@ struct GemmShape {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RB = RB_, S = S_, OCC = OCC_, GM = GM_;
     static constexpr int kThreads = WM * WN * kWave;
     static constexpr int kWaves = WM * WN;
+    // waves each SIMD holds with OCC blocks resident (the compiler's
+    // register budget): 4 SIMDs per CU
+    static constexpr int kWavesPerSimd = OCC * kWaves / 4;
     static constexpr int kBK = RB / ET::kBytes;           // K elements per slice
     static constexpr int kNch = RB / 16;                  // 16-byte chunks per row
     static constexpr int kRowsPerBlk = 1024 / RB;         // rows per 1 KB DMA block
@@ -105,6 +108,7 @@ struct GemmShape {
     static_assert(S >= 2 && S <= 4, "2 to 4 stages");
     static_assert((S - 1) * kLoads <= 63, "vmcnt range");
     static_assert(kWaves % 2 == 0, "block parity must be fixed per wave");
+    static_assert(kWavesPerSimd >= 1 && (OCC * kWaves) % 4 == 0, "whole waves per SIMD");
 };
 
 // LDS byte offset of 16-byte chunk `c` of tile row `row` for RB-byte rows.
@@ -808,7 +812,7 @@ __device__ __forceinline__ size_t partial_index(int wave, int i, int j, int g, i
 // row stride K, C [E][max_rows][Nout] (Nout == Nw).  No row segments, no
 // gather, no split.
 template <typename ET, typename OT, typename S, int EPI, bool KG = false, bool WT = false>
-__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
+__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWavesPerSimd, S::kWavesPerSimd)))
 void moe_grouped_gemm_kernel(const typename ET::storage* __restrict__ A, const int32_t* __restrict__ gather,
                              int gather_rows, const typename ET::storage* __restrict__ W,
                              typename OT::storage* __restrict__ C, const int32_t* __restrict__ offsets, int E,
@@ -1465,20 +1469,26 @@ hipError_t launch_wt(int epi, const GemmArgs& g)
 //           kLargeTileMinK): 256 x 256 tiles, 8 waves (2 per SIMD, 128 x 64
 //           each), the densest tile that fits the register file; 2 x 64 KB
 //           of LDS stages
-//   medium  128..511 rows: 128 x 128 tiles, 4 waves, 2 blocks per CU
+//   medium  128..511 rows: 128 x 128 tiles, 8 waves (64 x 32 each), 2 blocks
+//           per CU, so 4 waves share each SIMD (against 4 waves of 64 x 64,
+//           same box, per layer: the 64-expert 512/1024 layer 0.1213-0.1216 ->
+//           0.1192-0.1194 ms, the 2048-token Mixtral-family case 0.0402-0.0405
+//           -> 0.0382-0.0383 ms; outputs bit-identical)
 //   small   < 128 rows: 64 x 256 tiles, 4 waves (short segments, so tall
 //           tiles would mostly compute padding); 3 LDS stages of 40 KB, which
 //           keep two slices in flight per CU on these weight-streaming
 //           shapes (512 experts of 1024 x 512: up 138 -> 129 us, down 156 ->
 //           147 us against 2 stages)
 // The same shapes serve bf16 and FP8 (a 128-byte slice is 64 bf16 or 128 FP8
-// values of K); the FP8 small tile keeps 2 stages, which its K loop needs.
+// values of K); the FP8 small tile keeps 2 stages and the FP8 medium tile 4
+// waves of 64 x 64, which its K loop needs (two weight blocks per wave).
 #ifndef MOE_LARGE_TILE
 #define MOE_LARGE_TILE 256, 256, 2, 4, 128, 2, 1, 8
 #endif
 #ifndef MOE_MEDIUM_TILE
-#define MOE_MEDIUM_TILE 128, 128, 2, 2, 128, 2, 2, 4
+#define MOE_MEDIUM_TILE 128, 128, 2, 4, 128, 2, 2, 4
 #endif
+#define MOE_MEDIUM_TILE_FP8 128, 128, 2, 2, 128, 2, 2, 4
 #ifndef MOE_SMALL_TILE
 #define MOE_SMALL_TILE 64, 256, 1, 4, 128, 3, 1, 4
 #endif
@@ -1566,7 +1576,7 @@ extern "C" hipError_t moe_launch_grouped_gemm_fp8(int epi, const void* A, const 
     if (mean_rows >= 512)
         return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_LARGE_TILE>>(epi, g);
     if (mean_rows >= 128)
-        return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_MEDIUM_TILE>>(epi, g);
+        return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_MEDIUM_TILE_FP8>>(epi, g);
     return launch_epi<fp8_t, bf16_t, GemmShape<fp8_t, MOE_SMALL_TILE_FP8>>(epi, g);
 }
 
