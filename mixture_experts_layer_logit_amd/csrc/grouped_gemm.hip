@@ -415,7 +415,15 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
         if (ep.a)
             as = ep.a[gather ? gather[t.row0 + m] : t.row0 + m];
         const float* wsc = ep.w ? ep.w + (size_t)t.e * Nw : nullptr;
-        constexpr int kJ = (EPI == EPI_SWIGLU) ? S::kFN / 2 : S::kFN;
+        // SwiGLU: the wave's kWaveN columns are its gate columns, then the
+        // matching up columns.  With two or more 32-column blocks per wave
+        // the up value of gate block j sits in block j + kFN / 2 at the same
+        // place; with one block (kWaveN = 32) gate and up share the block,
+        // the up value 16 columns (two 8-column groups) further on.
+        constexpr bool kOneBlock = S::kFN == 1;
+        constexpr int kJ = (EPI == EPI_SWIGLU) ? (kOneBlock ? 1 : S::kFN / 2) : S::kFN;
+        constexpr int kG4 = (EPI == EPI_SWIGLU && kOneBlock) ? 2 : 4;  // gate groups of a block
+        constexpr int kUpJ = kOneBlock ? 0 : S::kFN / 2, kUpG4 = kOneBlock ? 2 : 0;
         // Backward epilogues: this row fragment's saved u, all loaded before
         // any of its stores.  Stores and loads retire in issue order, so a
         // load issued after a store would wait for that store as well.
@@ -440,7 +448,7 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
 #pragma unroll
         for (int j = 0; j < kJ; ++j) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
+            for (int g4 = 0; g4 < kG4; ++g4) {
                 const int nl = j * 32 + 8 * g4 + 4 * (lane >> 5);
                 const int n = t.n0 + ((EPI == EPI_SWIGLU) ? wn * (S::kWaveN / 2) : wn * S::kWaveN) + nl;
                 if (n >= ncols)
@@ -453,7 +461,7 @@ __device__ __forceinline__ void store_tile(const Acc<S>& acc, typename OT::stora
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float u = acc.v[i][j][4 * g4 + q];
-                    float up = (EPI == EPI_SWIGLU) ? acc.v[i][j + S::kFN / 2][4 * g4 + q] : 0.0f;
+                    float up = (EPI == EPI_SWIGLU) ? acc.v[i][j + kUpJ][4 * (g4 + kUpG4) + q] : 0.0f;
                     if (wsc) {
                         u *= as * wsc[n + q];
                         if (EPI == EPI_SWIGLU)
@@ -1474,11 +1482,14 @@ hipError_t launch_wt(int epi, const GemmArgs& g)
 //           same box, per layer: the 64-expert 512/1024 layer 0.1213-0.1216 ->
 //           0.1192-0.1194 ms, the 2048-token Mixtral-family case 0.0402-0.0405
 //           -> 0.0382-0.0383 ms; outputs bit-identical)
-//   small   < 128 rows: 64 x 256 tiles, 4 waves (short segments, so tall
-//           tiles would mostly compute padding); 3 LDS stages of 40 KB, which
-//           keep two slices in flight per CU on these weight-streaming
-//           shapes (512 experts of 1024 x 512: up 138 -> 129 us, down 156 ->
-//           147 us against 2 stages)
+//   small   < 128 rows: 64 x 256 tiles, 8 waves (64 x 32 each, 2 per SIMD;
+//           short segments, so tall tiles would mostly compute padding); 3 LDS
+//           stages of 40 KB, which keep two slices in flight per CU on these
+//           weight-streaming shapes (512 experts of 1024 x 512: up 138 -> 129
+//           us, down 156 -> 147 us against 2 stages).  Against 4 waves of 64 x
+//           64, same box, per layer: the 2048-token 512-expert case 0.0663-
+//           0.0681 -> 0.0600-0.0619 ms, the 512-expert 16384-token layer
+//           0.3401-0.3463 -> 0.3336-0.3387 ms; outputs bit-identical
 // The same shapes serve bf16 and FP8 (a 128-byte slice is 64 bf16 or 128 FP8
 // values of K); the FP8 small tile keeps 2 stages and the FP8 medium tile 4
 // waves of 64 x 64, which its K loop needs (two weight blocks per wave).
@@ -1490,7 +1501,7 @@ hipError_t launch_wt(int epi, const GemmArgs& g)
 #endif
 #define MOE_MEDIUM_TILE_FP8 128, 128, 2, 2, 128, 2, 2, 4
 #ifndef MOE_SMALL_TILE
-#define MOE_SMALL_TILE 64, 256, 1, 4, 128, 3, 1, 4
+#define MOE_SMALL_TILE 64, 256, 1, 8, 128, 3, 1, 4
 #endif
 #define MOE_SMALL_TILE_FP8 64, 256, 1, 4, 128, 2, 1, 4
 #define MOE_F32_TILE 128, 128, 2, 2, 128, 2, 1, 4

@@ -329,7 +329,13 @@ SPLIT_CASES = {
     # an odd slice count (d = 2112 is 33 slices of 64)
     "large_swiglu": ("bf16", "swiglu", 1024, 2048, 4, 2, 768, [700, 300, 512, 536]),
     "large_swiglu_ragged": ("bf16", "swiglu", 1024, 2112, 4, 2, 320, [1, 0, 1019, 1028]),
+    # 256 mean rows with K >= 1024: the bf16 forward takes the large tile here
     "medium_swiglu": ("bf16", "swiglu", 512, 2048, 4, 2, 512, [300, 0, 257, 300]),
+    # 128 mean rows per expert: the medium tile, whose waves hold one
+    # 32-column block (16 gate and 16 up columns), with its SwiGLU tail store
+    "medium_tile_swiglu": ("bf16", "swiglu", 512, 2048, 8, 2, 320, [200, 0, 130, 170, 128, 140, 120, 110]),
+    # 64 mean rows per expert: the small tile, likewise one block per wave
+    "small_swiglu": ("bf16", "swiglu", 512, 2048, 16, 2, 320, [64] * 14 + [1, 63]),
     "small_relu": ("bf16", "relu", 512, 2048, 16, 2, 512, [64] * 14 + [1, 63]),
     "f32_relu": ("f32", "relu", 512, 2048, 4, 1, 512, [130, 0, 200, 150]),
 }
