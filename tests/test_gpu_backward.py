@@ -103,6 +103,23 @@ def test_backward_small(name):
     print("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
 
 
+@pytest.mark.parametrize("E", [8, 16])
+def test_backward_split_tail_tiles(E):
+    """The training step on the 128 x 128 (E = 8: 128 rows per expert) and
+    64 x 256 (E = 16: 64 rows) tiles, whose waves hold one 32-column block,
+    with the K-split tail in every GEMM whose K reaches 2048: the
+    up-projection (K = d), the activation-backward GEMM (K = d) and the
+    input-gradient GEMM (K = 2F).  Capacity factor 1 keeps each expert within
+    one m-tile, so few enough tiles remain for their last round to split."""
+    case = moe_inputs.get("mixtral_s").with_(name=f"bsplit_E{E}", T=512, d=2048, F=1024, E=E, cf=1.0, bias="none")
+    print(f"[backward split tail] {case.name}", flush=True)
+    inp = moe_inputs.make(case)
+    dy = moe_inputs.make_dy(case)
+    out = run_train(case, inp, dy)
+    errs = check_backward(case, inp, out, dy)
+    print("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+
+
 def sample(case, inp, n):
     g = np.random.default_rng(case.seed + 77)
     picks = {0, case.T - 1}
