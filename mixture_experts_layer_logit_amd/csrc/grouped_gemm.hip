@@ -50,6 +50,7 @@
 //  * SwiGLU: a wave's N range holds its gate columns then the matching up
 //    columns, so gate and up values of one output meet in the same lane.
 //  * Rows past a segment's end are computed on zeros and not stored.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -1512,6 +1513,20 @@ hipError_t launch_wt(int epi, const GemmArgs& g)
 // 128 x 128, while its up-projection (K = 512) ran 52.8 against 44.9 us.
 constexpr int kLargeTileMinK = 1024;
 
+// ... and only where that gives at least a quarter of the CUs a tile
+// (estimated from the mean rows per expert): the 16-expert 256/1024 layer of
+// 2048 tokens has about 16 tiles of 256 x 256 for its down-projection and ran
+// 0.0526-0.0553 ms per layer on the 8-wave 128 x 128 tile against 0.0642-
+// 0.0661 ms, while the 8192-token 64-expert layer (about 128 estimated, 194
+// actual) keeps the large tile (0.1168-0.1200 against 0.1198-0.1239 ms).
+static bool large_tile_fills(const GemmArgs& g, int epi, int mean_rows)
+{
+    const int ncols = epi == EPI_SWIGLU ? g.F : g.Nout;
+    const int tile_cols = epi == EPI_SWIGLU ? 128 : 256;
+    const long long est = (long long)g.E * std::max(1, mean_rows / 256) * ((ncols + tile_cols - 1) / tile_cols);
+    return 4 * est >= g.ncu;
+}
+
 // Workspace bytes the tail split needs for a problem with this mean rows per
 // expert (the partial tiles of the largest configuration the launcher may
 // pick for it).  dtype: 0 fp32, 1 bf16, 2 FP8.
@@ -1547,7 +1562,7 @@ extern "C" hipError_t moe_launch_grouped_gemm(int dtype, int epi, const void* A,
                         EpiArgs{nullptr, nullptr, aux_in, aux_out, aux_ld}, stream};
     if (dtype == 0)
         return launch_epi<f32_t, f32_t, GemmShape<f32_t, MOE_F32_TILE>>(epi, g);
-    if (mean_rows >= 512 || (mean_rows >= 256 && K >= kLargeTileMinK))
+    if (mean_rows >= 512 || (mean_rows >= 256 && K >= kLargeTileMinK && large_tile_fills(g, epi, mean_rows)))
         return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_LARGE_TILE>>(epi, g);
     if (mean_rows >= 128)
         return launch_epi<bf16_t, bf16_t, GemmShape<bf16_t, MOE_MEDIUM_TILE>>(epi, g);
